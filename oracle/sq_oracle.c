@@ -1,0 +1,259 @@
+/*
+ * sq_oracle.c -- plain, slow CPU oracle for the SmoothQuant-smoothed W8A8
+ * linear layer Y = (X S^-1)(S W).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library includes, links
+ * or calls this file; only the tests, the smoke check and the CPU-baseline
+ * leg of the benchmark load it.  It shares no header, helper, table or
+ * constant with the HIP path.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -shared -fPIC.
+ * No intrinsics, no vectorisation hints, rounding mode round-to-nearest-even.
+ * On x86-64 every float operation below is a single IEEE-754 binary32
+ * operation (SSE, no excess precision), so the op order written here is the
+ * op order that is computed.
+ *
+ * Conventions (all row-major):
+ *   X     fp16 bits [M][ldx]   tokens x input channels
+ *   W     fp16 bits [K][ldw]   input channels x output channels
+ *   Wq    int8      [N][K]     folded, quantized weights, K contiguous
+ *   Xq    int8      [M][K]     quantized activations
+ *   acc   int32     [M][N]
+ *
+ * Sources (pages the method is taken from):
+ *   [P1] "Move activation scale without changing the real linear map"
+ *        (study.greatitself.com, activation outliers and smoothing)
+ *   [P2] SmoothQuant glossary entry (dataterminology.com)
+ *   [P4] Pith review of arXiv 2506.01967 "Smooth Rotation"
+ *   [P5] "Quantization" chapter (learn-kernels.com)
+ *
+ * Readings where the pages are silent (each is listed with its reason in the
+ * design notes):
+ *   - s_j = max|X_j|^alpha / max|W_j|^(1-alpha), evaluated in double and
+ *     rounded once to float; alpha = 1/2 is [P4]'s key-machinery formula.
+ *   - X is divided by s (multiplied by 1/s in float), row j of W (input
+ *     channel j) is multiplied by s [P1 para. 1].
+ *   - a zero statistic would make s zero or infinite, which [P1 para. 1]
+ *     forbids; such a channel takes s = 1.
+ *   - quantization is symmetric to [-127, 127] with round-half-even, per token
+ *     for activations and per output channel for weights; scales are
+ *     absmax/127 in float.
+ *   - the int32 accumulator is exact for K < 133144.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ---- fp16 decoding ------------------------------------------------------ */
+
+/* Exact value of an IEEE-754 binary16 bit pattern, as a float.  Every binary16
+ * value is representable in binary32, so this conversion is exact. */
+static float half_to_float(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int m = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);              /* zero and subnormals */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m + 1024), e - 25);  /* 1.m * 2^(e-15) */
+    return (float)(sign ? -v : v);
+}
+
+float oracle_half_to_float(uint16_t h) { return half_to_float(h); }
+
+/* ---- A1: calibration statistics ---------------------------------------- */
+
+/* ax[j] = max over the T calibration tokens of |X[t][j]|, the per-input-channel
+ * activation maximum that the smoothing factor divides by ([P4] key machinery:
+ * max|X_j|; [P2]: statistics from a small calibration set).  With accumulate,
+ * the previous ax[j] takes part in the maximum, so batches can be streamed.
+ * A NaN anywhere in a column (or in the previous ax[j]) makes ax[j] NaN. */
+void oracle_calibrate_absmax(const uint16_t *x, int64_t T, int64_t K, int64_t ldx,
+                             float *ax, int accumulate)
+{
+    for (int64_t j = 0; j < K; ++j) {
+        float best = 0.0f;
+        int nan = 0;
+        if (accumulate) {
+            if (isnan(ax[j])) nan = 1;
+            else best = ax[j];
+        }
+        for (int64_t t = 0; t < T; ++t) {
+            float v = half_to_float(x[t * ldx + j]);
+            if (isnan(v)) { nan = 1; continue; }
+            if (fabsf(v) > best) best = fabsf(v);
+        }
+        ax[j] = nan ? NAN : best;
+    }
+}
+
+/* ---- A2: weight statistics and smoothing factors ----------------------- */
+
+/* aw[j] = max over output channels n of |W[j][n]|: the maximum of weight row j,
+ * i.e. of input channel j ([P4] key machinery: max|W_j|; W is in x out per
+ * [P1 para. 1]).  NaN anywhere in the row gives NaN. */
+void oracle_row_absmax(const uint16_t *w, int64_t K, int64_t N, int64_t ldw, float *aw)
+{
+    for (int64_t j = 0; j < K; ++j) {
+        float best = 0.0f;
+        int nan = 0;
+        for (int64_t n = 0; n < N; ++n) {
+            float v = half_to_float(w[j * ldw + n]);
+            if (isnan(v)) { nan = 1; continue; }
+            if (fabsf(v) > best) best = fabsf(v);
+        }
+        aw[j] = nan ? NAN : best;
+    }
+}
+
+/* Smoothing factors.  [P4] key machinery gives s_j = sqrt(max|X_j| / max|W_j|)
+ * (the paper's Eq. 4, strength 1/2); the general strength alpha weighs the two
+ * statistics as max|X_j|^alpha / max|W_j|^(1-alpha), which is the same formula
+ * at alpha = 1/2.  Evaluated in double, rounded once to float; inv_s is the
+ * float reciprocal.  Returns 0 on success, 1 when a statistic is not finite
+ * or negative, 2 when s or 1/s is not a finite normal float ([P1 para. 1]:
+ * factors must be finite, nonzero and representable). */
+int oracle_smoothing_factors(const float *ax, const float *aw, int64_t K, float alpha,
+                             float *s, float *inv_s)
+{
+    const double a = (double)alpha;
+    int status = 0;
+    for (int64_t j = 0; j < K; ++j) {
+        if (!isfinite(ax[j]) || !isfinite(aw[j]) || ax[j] < 0.0f || aw[j] < 0.0f) {
+            s[j] = NAN;
+            inv_s[j] = NAN;
+            status = 1;
+            continue;
+        }
+        float sj;
+        if (ax[j] == 0.0f || aw[j] == 0.0f)
+            sj = 1.0f;   /* dead channel or zero row: any positive s keeps Y; take 1 */
+        else
+            sj = (float)(pow((double)ax[j], a) / pow((double)aw[j], 1.0 - a));
+        float ij = 1.0f / sj;
+        s[j] = sj;
+        inv_s[j] = ij;
+        if (status == 0 && (!isnormal(sj) || !isnormal(ij)))
+            status = 2;
+    }
+    return status;
+}
+
+/* ---- A3: fold S into W and quantize per output channel ------------------ */
+
+/* Wt[j][n] = float(W[j][n]) * s[j]: row j of W takes the factor of input
+ * channel j, which compensates X[:, j] / s[j] exactly in real arithmetic
+ * ([P1 para. 1]; done offline before serving, [P5 para. 2]).
+ * Per output channel n: amax = max_j |Wt[j][n]|, w_scale[n] = amax / 127,
+ * r = 127 / amax, Wq[n][j] = clamp(rint(Wt[j][n] * r), -127, 127).
+ * amax == 0 gives scale 0 and codes 0. */
+void oracle_fold_quant_weights(const uint16_t *w, int64_t K, int64_t N, int64_t ldw,
+                               const float *s, int8_t *wq, float *w_scale)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        float amax = 0.0f;
+        for (int64_t j = 0; j < K; ++j) {
+            float wt = half_to_float(w[j * ldw + n]) * s[j];
+            if (fabsf(wt) > amax) amax = fabsf(wt);
+        }
+        if (amax == 0.0f) {
+            w_scale[n] = 0.0f;
+            for (int64_t j = 0; j < K; ++j) wq[n * K + j] = 0;
+            continue;
+        }
+        float r = 127.0f / amax;
+        w_scale[n] = amax / 127.0f;
+        for (int64_t j = 0; j < K; ++j) {
+            float wt = half_to_float(w[j * ldw + n]) * s[j];
+            float q = rintf(wt * r);
+            if (q > 127.0f) q = 127.0f;
+            if (q < -127.0f) q = -127.0f;
+            wq[n * K + j] = (int8_t)q;
+        }
+    }
+}
+
+/* ---- A4: per-token dynamic activation quantization ---------------------- */
+
+/* xt[m][j] = float(X[m][j]) * inv_s[j] -- the division by s applied where the
+ * activation is quantized instead of in a separate scaling kernel ([P1 para.
+ * 3]); xt stays in float.  Per token m: a = max_j |xt|, x_scale[m] = a / 127,
+ * r = 127 / a, Xq[m][j] = clamp(rint(xt * r), -127, 127).  a == 0 gives scale
+ * 0 and codes 0; a row holding a non-finite xt gets scale NaN and codes 0. */
+void oracle_quant_act_per_token(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                                const float *inv_s, int8_t *xq, float *x_scale)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        float a = 0.0f;
+        int bad = 0;
+        for (int64_t j = 0; j < K; ++j) {
+            float xt = half_to_float(x[m * ldx + j]) * inv_s[j];
+            if (!isfinite(xt)) { bad = 1; continue; }
+            if (fabsf(xt) > a) a = fabsf(xt);
+        }
+        if (bad || a == 0.0f) {
+            x_scale[m] = bad ? NAN : 0.0f;
+            for (int64_t j = 0; j < K; ++j) xq[m * K + j] = 0;
+            continue;
+        }
+        float r = 127.0f / a;
+        x_scale[m] = a / 127.0f;
+        for (int64_t j = 0; j < K; ++j) {
+            float xt = half_to_float(x[m * ldx + j]) * inv_s[j];
+            float q = rintf(xt * r);
+            if (q > 127.0f) q = 127.0f;
+            if (q < -127.0f) q = -127.0f;
+            xq[m * K + j] = (int8_t)q;
+        }
+    }
+}
+
+/* ---- A5: integer matrix product ----------------------------------------- */
+
+/* acc[m][n] = sum_j Xq[m][j] * Wq[n][j]: both operands int8 ([P2]: W8A8;
+ * [P5 para. 2]: the product runs on low-precision hardware paths).  Summed in
+ * int64 and stored as int32, which is exact whenever K * 127^2 < 2^31.
+ * Returns the number of sums that did not fit int32 (0 for valid K). */
+int64_t oracle_gemm_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K,
+                        int32_t *acc)
+{
+    int64_t overflow = 0;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t t = 0;
+            for (int64_t j = 0; j < K; ++j)
+                t += (int64_t)xq[m * K + j] * (int64_t)wq[n * K + j];
+            if (t > INT32_MAX || t < INT32_MIN) ++overflow;
+            acc[m * N + n] = (int32_t)t;
+        }
+    }
+    return overflow;
+}
+
+/* ---- A6: dequantization ------------------------------------------------- */
+
+/* y[m][n] = acc[m][n] * x_scale[m] * w_scale[n], the value the two int8 codes
+ * stand for.  Evaluated in double (relative error below 2^-52); the caller
+ * rounds it once to the output precision. */
+void oracle_dequant(const int32_t *acc, const float *x_scale, const float *w_scale,
+                    int64_t M, int64_t N, double *y)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            y[m * N + n] = (double)acc[m * N + n] * (double)x_scale[m] * (double)w_scale[n];
+}
+
+/* The runtime layer (A4 + A5 + A6) on a block of tokens, for timing the
+ * oracle as a CPU baseline.  Uses the functions above unchanged. */
+void oracle_layer(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const float *inv_s,
+                  const int8_t *wq, const float *w_scale, int64_t N,
+                  int8_t *xq_tmp, float *x_scale_tmp, int32_t *acc_tmp, double *y)
+{
+    oracle_quant_act_per_token(x, M, K, ldx, inv_s, xq_tmp, x_scale_tmp);
+    oracle_gemm_i32(xq_tmp, wq, M, N, K, acc_tmp);
+    oracle_dequant(acc_tmp, x_scale_tmp, w_scale, M, N, y);
+}
