@@ -1,0 +1,176 @@
+/*
+ * sq.h -- C ABI of the MI355X (gfx950) SmoothQuant-smoothed W8A8 linear layer
+ *
+ *     Y = (X S^-1)(S W)
+ *
+ * X is tokens x input channels, W is input channels x output channels and S is
+ * a positive diagonal over the input channels, so the product equals X W in
+ * exact arithmetic ("Move activation scale without changing the real linear
+ * map", para. 1).  The factors come from calibration statistics, the weights
+ * are folded and quantized offline, and at serving time the activations are
+ * quantized per token and multiplied on int8 matrix cores (SmoothQuant
+ * glossary entry: W8A8, calibration-based; "Quantization", learn-kernels.com,
+ * para. 2: both operands int8, transform applied offline before serving).
+ *
+ * Conventions for every call:
+ *   - All array arguments are caller-owned DEVICE pointers on the current HIP
+ *     device (for instance a torch tensor's data_ptr()).  The library never
+ *     allocates, frees or keeps them.
+ *   - Matrices are row-major; "ld" arguments are row strides in elements.
+ *   - fp16 data is IEEE binary16 passed as raw bits (const void*).
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *     Work is enqueued on that stream; only sq_smooth_fold_weights waits for it.
+ *   - Every argument is checked before any HIP call or any write: a call that
+ *     returns an argument error (SQ_ERR_NULL, _SHAPE, _ALIGN, _ALPHA, _KIND)
+ *     has no side effects.
+ *   - Shape limits: sizes >= 0 (a zero token/output count is a no-op); K is a
+ *     multiple of 16 with 16 <= K <= SQ_MAX_K, so that every int32 sum of K
+ *     int8 products is exact; M, N, T < 2^31; ld >= the row length used.
+ *   - Alignment: every input pointer 16-byte aligned and fp16 input strides
+ *     multiples of 8 (whole 16-byte row chunks); the product's output y only
+ *     needs its element alignment, with any stride ldy >= N.
+ *   - Stateless and reentrant: calls on different streams may run
+ *     concurrently; calls that write the same buffers must be ordered by the
+ *     caller.
+ */
+#ifndef SQ_H
+#define SQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SQ_OK = 0,
+    SQ_ERR_NULL = 1,       /* a required pointer is NULL                          */
+    SQ_ERR_SHAPE = 2,      /* a size or stride is out of range                    */
+    SQ_ERR_ALIGN = 3,      /* a pointer or stride breaks the alignment rules      */
+    SQ_ERR_ALPHA = 4,      /* alpha is not in [0, 1] (or is NaN)                  */
+    SQ_ERR_NONFINITE = 5,  /* fold: a statistic or given factor is NaN, infinite
+                              or negative                                        */
+    SQ_ERR_RANGE = 6,      /* fold: a factor or its reciprocal is zero, infinite
+                              or subnormal in float                              */
+    SQ_ERR_HIP = 7,        /* the HIP runtime reported an error                   */
+    SQ_ERR_KIND = 8        /* unknown out_kind                                    */
+} sq_status;
+
+/* Output kinds of sq_w8a8_gemm. */
+enum {
+    SQ_OUT_F16 = 0,        /* y fp16 = round_to_nearest_even((acc * x_scale[m]) * w_scale[n]) */
+    SQ_OUT_I32 = 1         /* y int32 = acc, the raw integer sums                              */
+};
+
+/* Largest K: 131056 * 128 * 128 < 2^31, so int32 sums of any int8 codes are exact. */
+#define SQ_MAX_K 131056
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *sq_status_str(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int sq_version(void);
+
+/*
+ * Calibration statistics (offline).
+ * The per-input-channel activation maximum max|X_j| that the smoothing factor
+ * divides by (Pith review of arXiv 2506.01967, key machinery, Eq. 4), taken
+ * over calibration tokens (SmoothQuant glossary: a small representative
+ * dataset estimates the activation statistics).
+ *
+ *   x_cal       fp16 [T][ldx], T calibration tokens of K channels
+ *   act_absmax  float [K], written: act_absmax[j] = max_t |x_cal[t][j]|;
+ *               with accumulate != 0 the previous contents take part in the
+ *               maximum (stream the calibration set batch by batch; the
+ *               previous values must be >= 0 or NaN).  A NaN in a column makes
+ *               its entry NaN, an infinity makes it +inf; sq_smooth_fold_weights
+ *               rejects both.  T == 0 writes zeros (accumulate == 0) or leaves
+ *               the buffer unchanged (accumulate != 0).
+ * Asynchronous.
+ */
+sq_status sq_calibrate_absmax(const void *x_cal_f16, int64_t T, int64_t K, int64_t ldx,
+                              float *act_absmax, int accumulate, void *stream);
+
+/*
+ * Smoothing factors and the offline fold of S into W (offline, synchronous).
+ * s_j = act_absmax[j]^alpha / max_n|W[j][n]|^(1 - alpha), evaluated in double
+ * and rounded once to float (alpha = 1/2 is the Pith review's
+ * s_j = sqrt(max|X_j| / max|W_j|)); a channel whose activation or weight
+ * statistic is 0 takes s_j = 1.  Row j of W (input channel j) is multiplied
+ * by s_j, the compensation for dividing activation channel j by s_j ("Move
+ * activation scale ...", para. 1); the result is quantized symmetrically per
+ * output channel n to int8 with round-half-even:
+ *   Wt[j][n]   = float(W[j][n]) * s_j
+ *   w_scale[n] = max_j |Wt[j][n]| / 127
+ *   wq[n][j]   = clamp(rint(Wt[j][n] * (127 / max_j|Wt[j][n]|)), -127, 127)
+ * (an all-zero column gets scale 0 and codes 0).
+ *
+ *   w           fp16 [K][ldw], N output channels used per row
+ *   act_absmax  float [K] from sq_calibrate_absmax; ignored when smooth_in != NULL
+ *   alpha       migration strength in [0, 1]; ignored when smooth_in != NULL
+ *   smooth_in   NULL, or float [K] of given factors (e.g. a factor vector shared
+ *               by several consumers of one activation, "Move activation scale
+ *               ...", para. 3); used as s as is
+ *   smooth_out      float [K], written: s
+ *   inv_smooth_out  float [K], written: 1.0f / s  (the input of
+ *                   sq_quant_act_per_token)
+ *   wq          int8 [N][K], written: K-contiguous folded codes
+ *   w_scale     float [N], written
+ * Several consumers of one activation: pass their weights side by side as one
+ * K x (N1 + N2 + ...) matrix (ldw = total), so s uses the maximum over all of
+ * them and each consumer's codes and scales are contiguous slices; or fold
+ * each one with smooth_in set to the shared s.  Both give identical codes.
+ *
+ * The call waits for the stream once, to check the statistics and factors on
+ * the host.  Data errors: SQ_ERR_NONFINITE when a statistic (or a smooth_in
+ * entry) is NaN, infinite or negative; SQ_ERR_RANGE when a factor or its
+ * reciprocal is zero, infinite or subnormal.  On a data error wq is not
+ * written; smooth_out, inv_smooth_out and w_scale hold unspecified values.
+ */
+sq_status sq_smooth_fold_weights(const void *w_f16, int64_t K, int64_t N, int64_t ldw,
+                                 const float *act_absmax, float alpha, const float *smooth_in,
+                                 float *smooth_out, float *inv_smooth_out,
+                                 int8_t *wq, float *w_scale, void *stream);
+
+/*
+ * Per-token dynamic activation quantization with the 1/s scaling fused in,
+ * instead of a separate runtime scaling kernel ("Move activation scale ...",
+ * para. 3).  Per token m, in float:
+ *   xt[j]      = float(x[m][j]) * inv_smooth[j]
+ *   x_scale[m] = max_j |xt[j]| / 127
+ *   xq[m][j]   = clamp(rint(xt[j] * (127 / max_j|xt[j]|)), -127, 127)
+ * An all-zero row gets scale 0 and codes 0; a row with a non-finite xt gets
+ * scale NaN and codes 0 (so its outputs are NaN).
+ *
+ *   x           fp16 [M][ldx]
+ *   inv_smooth  float [K] (inv_smooth_out of the fold)
+ *   xq          int8 [M][K], written
+ *   x_scale     float [M], written
+ * Asynchronous.
+ */
+sq_status sq_quant_act_per_token(const void *x_f16, int64_t M, int64_t K, int64_t ldx,
+                                 const float *inv_smooth, int8_t *xq, float *x_scale,
+                                 void *stream);
+
+/*
+ * The W8A8 product on int8 matrix cores with a fused dequantizing epilogue
+ * ("Quantization", learn-kernels.com, para. 2: both operands int8, run on the
+ * low-precision hardware path):
+ *   acc[m][n] = sum_j xq[m][j] * wq[n][j]        (exact int32)
+ *   SQ_OUT_F16: y[m][n] = fp16_rne((float(acc) * x_scale[m]) * w_scale[n])
+ *   SQ_OUT_I32: y[m][n] = acc                     (x_scale, w_scale may be NULL)
+ *
+ *   xq       int8 [M][K]      (row stride K)
+ *   wq       int8 [N][K]      (row stride K)
+ *   y        fp16 or int32 [M][ldy]
+ * Asynchronous.
+ */
+sq_status sq_w8a8_gemm(const int8_t *xq, const float *x_scale, const int8_t *wq,
+                       const float *w_scale, int64_t M, int64_t N, int64_t K,
+                       void *y, int64_t ldy, int out_kind, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SQ_H */

@@ -1,0 +1,374 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every stage is fed the oracle's own inputs (so a failure names its kernel),
+then the whole chain runs on the GPU from the raw fp16 data.  Codes, scales,
+statistics, factors and int32 sums must be bit-exact; fp16 outputs within
+2^-10 relative (floor 2^-14) of the oracle's correctly rounded value.  The
+workloads run at their real sizes in the launch configuration the benchmark
+times; where the oracle's O(MNK) product would be slow, a seeded sample of
+rows (always including the first and last token) is compared.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2.0 ** -10
+FLOOR = 2.0 ** -14
+
+
+@pytest.fixture(scope="module")
+def sq():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import w8a8_post_quantization_sq_amd as m
+    m.lib()
+    return m
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    return torch.device("cuda:0")
+
+
+def T(a, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def H(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def bits_equal(a, b):
+    a = np.asarray(a)
+    b = np.asarray(b)
+    if a.dtype.kind == "f":
+        na, nb = np.isnan(a), np.isnan(b)
+        if not np.array_equal(na, nb):
+            return False
+        return np.array_equal(a[~na].view(np.uint32 if a.dtype == np.float32 else np.uint16),
+                              b[~nb].view(np.uint32 if b.dtype == np.float32 else np.uint16))
+    return np.array_equal(a, b)
+
+
+def assert_f16_close(y_gpu, y64_ref):
+    ref = np.asarray(y64_ref, np.float64).astype(np.float16).astype(np.float64)
+    g = np.asarray(y_gpu).astype(np.float64)
+    assert np.array_equal(np.isnan(g), np.isnan(ref))
+    fin = np.isfinite(ref)
+    assert np.array_equal(g[~fin & ~np.isnan(ref)], ref[~fin & ~np.isnan(ref)])
+    err = np.abs(g[fin] - ref[fin]) / np.maximum(np.abs(ref[fin]), FLOOR)
+    assert err.size == 0 or err.max() <= TOL, f"max rel err {err.max():.3g}"
+    return err
+
+
+def sample_rows(M, n, seed):
+    if M <= n:
+        return np.arange(M)
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, M - 1), n - 2, replace=False)
+    return np.sort(np.concatenate([[0, M - 1], mid]))
+
+
+ALL = ["tiny", "qkv4096", "down11008", "decode8192", "prefill8192x3"]
+
+
+def wl_inputs(name, m=None):
+    wl = W.WORKLOADS[name]
+    return wl, W.generate(wl, m=m)
+
+
+# ---- A1 calibration ----------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ALL)
+def test_calibrate_matches_oracle(sq, dev, orc, name):
+    wl, inp = wl_inputs(name, m=16 if name != "tiny" else None)
+    print(f"[calibrate] {name} T={inp.x_cal.shape[0]} K={wl.K}", flush=True)
+    ax = sq.calibrate(T(inp.x_cal, dev))
+    assert bits_equal(H(ax), orc.calibrate_absmax(inp.x_cal))
+    # streamed in two uneven batches
+    half = inp.x_cal.shape[0] // 3 + 1
+    ax2 = sq.calibrate(T(inp.x_cal[:half], dev))
+    sq.calibrate(T(inp.x_cal[half:], dev), ax2)
+    assert bits_equal(H(ax2), orc.calibrate_absmax(inp.x_cal))
+
+
+@pytest.mark.parametrize("T_,K,ld", [(1, 16, 16), (37, 48, 48), (5, 80, 96), (300, 528, 536)])
+def test_calibrate_ragged_and_strided(sq, dev, orc, T_, K, ld):
+    x = W.random_f16(100 + K, T_, ld, scale=4.0)
+    xv = T(x, dev)[:, :K]
+    ax = sq.calibrate(xv)
+    assert bits_equal(H(ax), orc.calibrate_absmax(np.ascontiguousarray(x[:, :K])))
+
+
+def test_calibrate_nonfinite_and_empty(sq, dev, orc):
+    import torch
+    x = W.random_f16(7, 64, 64)
+    x[3, 5] = np.nan
+    x[60, 9] = -np.inf
+    ax = sq.calibrate(T(x, dev))
+    ref = orc.calibrate_absmax(x)
+    assert bits_equal(np.isnan(H(ax)), np.isnan(ref)) and np.isinf(H(ax)[9])
+    assert bits_equal(H(ax)[~np.isnan(ref)], ref[~np.isnan(ref)])
+    # T = 0: zeros, or unchanged when accumulating
+    buf = torch.full((64,), 3.0, device=dev)
+    sq.sq_calibrate_absmax(T(x, dev)[:0], buf, accumulate=True)
+    assert np.all(H(buf) == 3.0)
+    sq.sq_calibrate_absmax(T(x, dev)[:0], buf, accumulate=False)
+    assert np.all(H(buf) == 0.0)
+
+
+# ---- A2 + A3 fold ----------------------------------------------------------------------
+
+FOLD_CASES = [("tiny", 0.5), ("qkv4096", 0.5), ("down11008", 0.5), ("down11008", 0.8),
+              ("decode8192", 0.5), ("prefill8192x3", 0.5)]
+
+
+@pytest.mark.parametrize("name,alpha", FOLD_CASES)
+def test_fold_matches_oracle(sq, dev, orc, name, alpha):
+    wl, inp = wl_inputs(name, m=16 if name != "tiny" else None)
+    print(f"[fold] {name} alpha={alpha} K={wl.K} N={wl.N}", flush=True)
+    ax = orc.calibrate_absmax(inp.x_cal)
+    w = inp.w
+    f = sq.fold(T(w, dev), T(ax, dev), alpha)
+    s, inv, st = orc.smoothing_factors(ax, orc.row_absmax(w), alpha)
+    assert st == 0
+    assert bits_equal(H(f.smooth), s)
+    assert bits_equal(H(f.inv_smooth), inv)
+    wq, wsc = orc.fold_quant_weights(w, s)
+    assert bits_equal(H(f.w_scale), wsc)
+    assert np.array_equal(H(f.wq), wq)
+
+
+def test_fold_given_factors_and_consumer_slices(sq, dev, orc):
+    """One smoothed X feeding three projections: the fold of the concatenated
+    weights equals three folds with the shared factors (smooth_in)."""
+    K = 256
+    ws = [W.random_f16(200 + i, K, n, 0.015) for i, n in enumerate((96, 40, 136))]
+    wcat = np.concatenate(ws, axis=1)
+    ax = orc.calibrate_absmax(W.random_f16(210, 64, K, 5.0))
+    fcat = sq.fold(T(wcat, dev), T(ax, dev), 0.5)
+    wq_cat = H(fcat.wq)
+    ws_cat = H(fcat.w_scale)
+    off = 0
+    for w in ws:
+        f1 = sq.fold(T(w, dev), None, 0.5, smooth_in=fcat.smooth)
+        n = w.shape[1]
+        assert np.array_equal(H(f1.wq), wq_cat[off:off + n])
+        assert bits_equal(H(f1.w_scale), ws_cat[off:off + n])
+        assert bits_equal(H(f1.smooth), H(fcat.smooth))
+        q1, s1 = orc.fold_quant_weights(w, H(fcat.smooth))
+        assert np.array_equal(H(f1.wq), q1)
+        off += n
+
+
+@pytest.mark.parametrize("K,N,ldw", [(16, 1, 8), (48, 13, 16), (272, 100, 104), (528, 64, 64),
+                                     (1040, 520, 520)])
+def test_fold_ragged_and_strided(sq, dev, orc, K, N, ldw):
+    w = W.random_f16(300 + N, K, ldw, 0.05)
+    ax = orc.calibrate_absmax(W.random_f16(301, 20, K, 3.0))
+    f = sq.fold(T(w, dev)[:, :N], T(ax, dev), 0.5)
+    wc = np.ascontiguousarray(w[:, :N])
+    s, inv, _ = orc.smoothing_factors(ax, orc.row_absmax(wc), 0.5)
+    wq, wsc = orc.fold_quant_weights(wc, s)
+    assert bits_equal(H(f.smooth), s)
+    assert np.array_equal(H(f.wq), wq) and bits_equal(H(f.w_scale), wsc)
+
+
+def test_fold_degenerate_channels(sq, dev, orc):
+    """Dead activation channels and all-zero weight rows take s = 1; an
+    all-zero output column gets scale 0 and codes 0."""
+    K, N = 64, 48
+    w = W.random_f16(400, K, N, 0.02)
+    w[5, :] = 0
+    w[:, 7] = 0
+    ax = orc.calibrate_absmax(W.random_f16(401, 16, K, 2.0))
+    ax[9] = 0
+    f = sq.fold(T(w, dev), T(ax, dev), 0.5)
+    s, inv, _ = orc.smoothing_factors(ax, orc.row_absmax(w), 0.5)
+    assert H(f.smooth)[5] == 1.0 and H(f.smooth)[9] == 1.0
+    wq, wsc = orc.fold_quant_weights(w, s)
+    assert np.array_equal(H(f.wq), wq) and bits_equal(H(f.w_scale), wsc)
+    assert H(f.w_scale)[7] == 0 and np.all(H(f.wq)[7] == 0)
+
+
+def test_fold_data_errors_leave_codes_untouched(sq, dev, orc):
+    import torch
+    K, N = 64, 32
+    w = W.random_f16(500, K, N, 0.02)
+    ax = orc.calibrate_absmax(W.random_f16(501, 8, K))
+
+    def run(w_, ax_, alpha=0.5, sin=None):
+        f = sq.Folded(torch.empty(K, device=dev), torch.empty(K, device=dev),
+                      torch.full((N, K), 55, dtype=torch.int8, device=dev),
+                      torch.empty(N, device=dev))
+        with pytest.raises(sq.SqError) as ei:
+            sq.sq_smooth_fold_weights(T(w_, dev), None if ax_ is None else T(ax_, dev), alpha,
+                                      None if sin is None else T(sin, dev), f.smooth,
+                                      f.inv_smooth, f.wq, f.w_scale)
+        assert np.all(H(f.wq) == 55)
+        return ei.value.status
+
+    a = ax.copy(); a[3] = np.nan
+    assert run(w, a) == sq.SQ_ERR_NONFINITE
+    a = ax.copy(); a[3] = np.inf
+    assert run(w, a) == sq.SQ_ERR_NONFINITE
+    a = ax.copy(); a[3] = -1.0
+    assert run(w, a) == sq.SQ_ERR_NONFINITE
+    w2 = w.copy(); w2[4, 6] = np.inf
+    assert run(w2, ax) == sq.SQ_ERR_NONFINITE
+    w2 = w.copy(); w2[4, 6] = np.nan
+    assert run(w2, ax) == sq.SQ_ERR_NONFINITE
+    a = ax.copy(); a[3] = 3e38
+    assert run(w, a, alpha=1.0) == sq.SQ_ERR_RANGE        # 1/s subnormal
+    sin = np.ones(K, np.float32); sin[2] = 0.0
+    assert run(w, None, sin=sin) == sq.SQ_ERR_RANGE
+    sin = np.ones(K, np.float32); sin[2] = -2.0
+    assert run(w, None, sin=sin) == sq.SQ_ERR_NONFINITE
+
+
+# ---- A4 per-token quantization --------------------------------------------------------
+
+@pytest.mark.parametrize("name", ALL)
+def test_quant_matches_oracle(sq, dev, orc, name):
+    wl, inp = wl_inputs(name)
+    print(f"[quant] {name} M={inp.x.shape[0]} K={wl.K}", flush=True)
+    ax = orc.calibrate_absmax(inp.x_cal)
+    _, inv, _ = orc.smoothing_factors(ax, orc.row_absmax(inp.ws[0][:, :64]), wl.alpha)
+    xq, xs = sq.quant(T(inp.x, dev), T(inv, dev))
+    rq, rs = orc.quant_act_per_token(inp.x, inv)
+    assert bits_equal(H(xs), rs)
+    assert np.array_equal(H(xq), rq)
+
+
+@pytest.mark.parametrize("M,K,ld", [(1, 16, 16), (3, 48, 56), (17, 2064, 2064), (2, 4112, 4128),
+                                    (5, 32784, 32784), (2, 40000, 40000), (1, 131056, 131056)])
+def test_quant_ragged_long_and_strided(sq, dev, orc, M, K, ld):
+    x = W.random_f16(600 + K, M, ld, 2.0)
+    inv = W.random_scales(601, K, 0.05, 3.0)
+    xq, xs = sq.quant(T(x, dev)[:, :K], T(inv, dev))
+    rq, rs = orc.quant_act_per_token(np.ascontiguousarray(x[:, :K]), inv)
+    assert bits_equal(H(xs), rs) and np.array_equal(H(xq), rq)
+
+
+def test_quant_ties_and_degenerate_rows(sq, dev, orc):
+    row = np.array([127, 2.5, 3.5, -2.5, 0.5, 1.5, -0.5, 126.5,
+                    -126.5, 5.5, -5.5, 0.25, 7.5, -7.5, 64.5, 0], np.float16)
+    x = np.zeros((5, 16), np.float16)
+    x[0] = row
+    x[2] = row
+    x[2, 3] = np.nan
+    x[3] = row
+    x[3, 0] = np.inf
+    x[4] = -row
+    ones = np.ones(16, np.float32)
+    xq, xs = sq.quant(T(x, dev), T(ones, dev))
+    rq, rs = orc.quant_act_per_token(x, ones)
+    assert bits_equal(H(xs), rs) and np.array_equal(H(xq), rq)
+    assert H(xq)[0].tolist() == [127, 2, 4, -2, 0, 2, 0, 126, -126, 6, -6, 0, 8, -8, 64, 0]
+    assert H(xs)[1] == 0 and np.isnan(H(xs)[2]) and np.isnan(H(xs)[3])
+
+
+# ---- A5 + A6 the product -----------------------------------------------------------------
+
+GEMM_SHAPES = [(1, 1, 16), (3, 5, 48), (17, 100, 80), (100, 200, 64), (128, 128, 4096),
+               (130, 129, 1040), (256, 384, 2048), (1, 28672, 128), (16, 300, 8192), (513, 77, 112)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_i32_bit_exact(sq, dev, orc, M, N, K):
+    xq = W.random_i8(700 + M, M, K, -128, 127)
+    wq = W.random_i8(701 + N, N, K, -128, 127)
+    acc = sq.gemm(T(xq, dev), None, T(wq, dev), None, out_kind=sq.SQ_OUT_I32)
+    assert np.array_equal(H(acc), orc.gemm_i32(xq, wq))
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_f16_epilogue(sq, dev, orc, M, N, K):
+    xq = W.random_i8(800 + M, M, K)
+    wq = W.random_i8(801 + N, N, K)
+    xs = W.random_scales(802, M, 1e-3, 2e-2)
+    ws = W.random_scales(803, N, 1e-3, 2e-2)
+    y = sq.gemm(T(xq, dev), T(xs, dev), T(wq, dev), T(ws, dev))
+    assert_f16_close(H(y), orc.dequant(orc.gemm_i32(xq, wq), xs, ws))
+
+
+def test_gemm_extreme_sums_and_strided_output(sq, dev, orc):
+    import torch
+    K = 131056
+    xq = np.full((2, K), 127, np.int8)
+    xq[1] = -128
+    wq = np.full((3, K), -127, np.int8)
+    wq[1] = 127
+    wq[2] = -128
+    acc = sq.gemm(T(xq, dev), None, T(wq, dev), None, out_kind=sq.SQ_OUT_I32)
+    assert np.array_equal(H(acc), orc.gemm_i32(xq, wq))
+    # output rows with a stride larger than N
+    xq = W.random_i8(900, 40, 64)
+    wq = W.random_i8(901, 24, 64)
+    xs = W.random_scales(902, 40)
+    ws = W.random_scales(903, 24)
+    big = torch.full((40, 32), 7.0, dtype=torch.float16, device=dev)
+    sq.sq_w8a8_gemm(T(xq, dev), T(xs, dev), T(wq, dev), T(ws, dev), big[:, :24])
+    out = H(big)
+    assert np.all(out[:, 24:] == 7.0)
+    assert_f16_close(out[:, :24], orc.dequant(orc.gemm_i32(xq, wq), xs, ws))
+
+
+def test_gemm_nan_row_propagates(sq, dev, orc):
+    xq = W.random_i8(910, 4, 64)
+    wq = W.random_i8(911, 8, 64)
+    xs = W.random_scales(912, 4)
+    xs[2] = np.nan
+    ws = W.random_scales(913, 8)
+    y = H(sq.gemm(T(xq, dev), T(xs, dev), T(wq, dev), T(ws, dev)))
+    assert np.isnan(y[2]).all() and np.isfinite(np.delete(y, 2, axis=0)).all()
+
+
+# ---- the whole chain ------------------------------------------------------------------------
+
+E2E = [("tiny", 0.5, 16), ("qkv4096", 0.5, 24), ("down11008", 0.5, 16), ("down11008", 0.8, 16),
+       ("decode8192", 0.5, 16), ("prefill8192x3", 0.5, 6)]
+
+
+@pytest.mark.parametrize("name,alpha,nrows", E2E)
+def test_end_to_end(sq, dev, orc, name, alpha, nrows):
+    wl, inp = wl_inputs(name)
+    print(f"[e2e] {name} alpha={alpha} M={wl.M} K={wl.K} N={wl.N}", flush=True)
+    xg = T(inp.x, dev)
+    ax = sq.calibrate(T(inp.x_cal, dev))
+    f = sq.fold(T(inp.w, dev), ax, alpha)
+    xq, xs = sq.quant(xg, f.inv_smooth)
+    y = sq.gemm(xq, xs, f.wq, f.w_scale)
+    acc = sq.gemm(xq, xs, f.wq, f.w_scale, out_kind=sq.SQ_OUT_I32)
+    rows = sample_rows(wl.M, nrows, 17)
+    ref = orc.smoothed_linear(inp.x, inp.x_cal, inp.w, alpha, rows=rows)
+    assert ref.status == 0
+    assert bits_equal(H(ax), ref.ax)
+    assert bits_equal(H(f.smooth), ref.s) and bits_equal(H(f.inv_smooth), ref.inv_s)
+    assert bits_equal(H(f.w_scale), ref.w_scale) and np.array_equal(H(f.wq), ref.wq)
+    assert bits_equal(H(xs), ref.x_scale) and np.array_equal(H(xq), ref.xq)
+    accg = H(acc)[rows]
+    assert np.array_equal(accg, ref.acc)
+    err = assert_f16_close(H(y)[rows], ref.y64)
+    print(f"[e2e] {name}: max rel err {err.max():.3g}, "
+          f"{np.mean(H(y)[rows].astype(np.float64) == ref.y16.astype(np.float64)):.4f} bit-equal",
+          flush=True)
+
+
+def test_repeat_runs_are_bitwise_identical(sq, dev, orc):
+    wl, inp = wl_inputs("qkv4096")
+    ax1 = H(sq.calibrate(T(inp.x_cal, dev)))
+    ax2 = H(sq.calibrate(T(inp.x_cal, dev)))
+    assert bits_equal(ax1, ax2)
+    f = sq.fold(T(inp.w, dev), T(ax1, dev), 0.5)
+    xq, xs = sq.quant(T(inp.x, dev), f.inv_smooth)
+    y1 = H(sq.gemm(xq, xs, f.wq, f.w_scale))
+    y2 = H(sq.gemm(xq, xs, f.wq, f.w_scale))
+    assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))

@@ -1,0 +1,247 @@
+"""Python binding of the MI355X SmoothQuant-smoothed W8A8 linear layer.
+
+A thin ctypes layer over the C ABI in include/sq.h (libsq.so, built in-tree
+by ``build.py``).  It only marshals torch tensors into device pointers,
+strides and the current HIP stream; every step of the layer runs in the
+library's gfx950 kernels.  There is no CPU fallback: without the built
+library, or without a GPU, the calls raise.
+
+Same-name calls (caller-allocated outputs, as in the C ABI):
+    sq_calibrate_absmax, sq_smooth_fold_weights, sq_quant_act_per_token,
+    sq_w8a8_gemm
+Allocating helpers built on them:
+    calibrate, fold, quant, gemm, smoothed_linear
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsq.so")
+
+SQ_OK = 0
+SQ_ERR_NULL = 1
+SQ_ERR_SHAPE = 2
+SQ_ERR_ALIGN = 3
+SQ_ERR_ALPHA = 4
+SQ_ERR_NONFINITE = 5
+SQ_ERR_RANGE = 6
+SQ_ERR_HIP = 7
+SQ_ERR_KIND = 8
+SQ_OUT_F16 = 0
+SQ_OUT_I32 = 1
+SQ_MAX_K = 131056
+
+EXPORTS = ("sq_status_str", "sq_version", "sq_calibrate_absmax", "sq_smooth_fold_weights",
+           "sq_quant_act_per_token", "sq_w8a8_gemm")
+
+_LIB = None
+
+
+class SqError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = int(status)
+        super().__init__(f"{call}: {status_str(status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libsq.so.  Raises if it has not been built: there is no fallback."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m w8a8_post_quantization_sq_amd.build` "
+                              "or __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, f32, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+        L.sq_status_str.restype = ctypes.c_char_p
+        L.sq_status_str.argtypes = [ci]
+        L.sq_version.restype = ci
+        L.sq_version.argtypes = []
+        L.sq_calibrate_absmax.restype = ci
+        L.sq_calibrate_absmax.argtypes = [vp, i64, i64, i64, vp, ci, vp]
+        L.sq_smooth_fold_weights.restype = ci
+        L.sq_smooth_fold_weights.argtypes = [vp, i64, i64, i64, vp, f32, vp, vp, vp, vp, vp, vp]
+        L.sq_quant_act_per_token.restype = ci
+        L.sq_quant_act_per_token.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
+        L.sq_w8a8_gemm.restype = ci
+        L.sq_w8a8_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i64, ci, vp]
+        _LIB = L
+    return _LIB
+
+
+def status_str(status: int) -> str:
+    return lib().sq_status_str(int(status)).decode()
+
+
+def _check(st: int, call: str) -> None:
+    if st != SQ_OK:
+        raise SqError(st, call)
+
+
+# ---- marshalling helpers ------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t, dtype, name, ndim=None):
+    torch = _torch()
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a GPU tensor (there is no CPU path)")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got {t.dim()}")
+    if t.dim() >= 1 and t.stride(-1) != 1 and t.numel() > 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    return t
+
+
+def _ld(t) -> int:
+    return int(t.stride(0)) if t.dim() == 2 and t.shape[0] > 1 else int(t.shape[-1])
+
+
+# ---- the four calls, same names as the C ABI -----------------------------------
+
+def sq_calibrate_absmax(x_cal, act_absmax, accumulate: bool = False, stream=None) -> None:
+    """act_absmax[j] (float32 [K]) := max_t |x_cal[t][j]| (with accumulate: also
+    over its previous contents).  x_cal: float16 [T][K]."""
+    torch = _torch()
+    _need(x_cal, torch.float16, "x_cal", 2)
+    _need(act_absmax, torch.float32, "act_absmax", 1)
+    T, K = x_cal.shape
+    _check(lib().sq_calibrate_absmax(_ptr(x_cal), T, K, _ld(x_cal), _ptr(act_absmax),
+                                     1 if accumulate else 0, _stream(stream, x_cal.device)),
+           "sq_calibrate_absmax")
+
+
+def sq_smooth_fold_weights(w, act_absmax, alpha: float, smooth_in, smooth_out, inv_smooth_out,
+                           wq, w_scale, stream=None) -> None:
+    """Smoothing factors and the offline fold.  w: float16 [K][N] (input x
+    output channels); wq: int8 [N][K]; w_scale: float32 [N]; smooth_out,
+    inv_smooth_out: float32 [K]; smooth_in: None or float32 [K]."""
+    torch = _torch()
+    _need(w, torch.float16, "w", 2)
+    K, N = w.shape
+    for t, n in ((smooth_out, "smooth_out"), (inv_smooth_out, "inv_smooth_out"),
+                 (w_scale, "w_scale")):
+        _need(t, torch.float32, n, 1)
+    if act_absmax is not None:
+        _need(act_absmax, torch.float32, "act_absmax", 1)
+    if smooth_in is not None:
+        _need(smooth_in, torch.float32, "smooth_in", 1)
+    _need(wq, torch.int8, "wq", 2)
+    if tuple(wq.shape) != (N, K) or not wq.is_contiguous():
+        raise ValueError("wq must be a contiguous int8 [N][K] tensor")
+    _check(lib().sq_smooth_fold_weights(_ptr(w), K, N, _ld(w), _ptr(act_absmax), float(alpha),
+                                        _ptr(smooth_in), _ptr(smooth_out), _ptr(inv_smooth_out),
+                                        _ptr(wq), _ptr(w_scale), _stream(stream, w.device)),
+           "sq_smooth_fold_weights")
+
+
+def sq_quant_act_per_token(x, inv_smooth, xq, x_scale, stream=None) -> None:
+    """xq (int8 [M][K]) and x_scale (float32 [M]) of x (float16 [M][K]) * inv_smooth."""
+    torch = _torch()
+    _need(x, torch.float16, "x", 2)
+    _need(inv_smooth, torch.float32, "inv_smooth", 1)
+    _need(xq, torch.int8, "xq", 2)
+    _need(x_scale, torch.float32, "x_scale", 1)
+    M, K = x.shape
+    if tuple(xq.shape) != (M, K) or not xq.is_contiguous():
+        raise ValueError("xq must be a contiguous int8 [M][K] tensor")
+    _check(lib().sq_quant_act_per_token(_ptr(x), M, K, _ld(x), _ptr(inv_smooth), _ptr(xq),
+                                        _ptr(x_scale), _stream(stream, x.device)),
+           "sq_quant_act_per_token")
+
+
+def sq_w8a8_gemm(xq, x_scale, wq, w_scale, y, out_kind: int = SQ_OUT_F16, stream=None) -> None:
+    """y [M][N] (float16, or int32 raw sums) = dequant(xq [M][K] . wq [N][K]^T)."""
+    torch = _torch()
+    _need(xq, torch.int8, "xq", 2)
+    _need(wq, torch.int8, "wq", 2)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or not xq.is_contiguous() or not wq.is_contiguous():
+        raise ValueError("xq [M][K] and wq [N][K] must be contiguous with the same K")
+    if out_kind == SQ_OUT_F16:
+        _need(x_scale, torch.float32, "x_scale", 1)
+        _need(w_scale, torch.float32, "w_scale", 1)
+        _need(y, torch.float16, "y", 2)
+    else:
+        _need(y, torch.int32, "y", 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("y must be [M][N]")
+    _check(lib().sq_w8a8_gemm(_ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), M, N, K,
+                              _ptr(y), _ld(y), int(out_kind), _stream(stream, xq.device)),
+           "sq_w8a8_gemm")
+
+
+# ---- allocating helpers ---------------------------------------------------------
+
+@dataclass
+class Folded:
+    """The exported representation of one smoothed, quantized linear layer."""
+    smooth: "object"       # float32 [K]  s
+    inv_smooth: "object"   # float32 [K]  1/s
+    wq: "object"           # int8 [N][K]
+    w_scale: "object"      # float32 [N]
+
+
+def calibrate(x_cal, act_absmax=None, stream=None):
+    torch = _torch()
+    out = act_absmax if act_absmax is not None else torch.empty(
+        x_cal.shape[1], dtype=torch.float32, device=x_cal.device)
+    sq_calibrate_absmax(x_cal, out, accumulate=act_absmax is not None, stream=stream)
+    return out
+
+
+def fold(w, act_absmax, alpha: float, smooth_in=None, stream=None) -> Folded:
+    torch = _torch()
+    K, N = w.shape
+    dev = w.device
+    f = Folded(torch.empty(K, dtype=torch.float32, device=dev),
+               torch.empty(K, dtype=torch.float32, device=dev),
+               torch.empty((N, K), dtype=torch.int8, device=dev),
+               torch.empty(N, dtype=torch.float32, device=dev))
+    sq_smooth_fold_weights(w, act_absmax, alpha, smooth_in, f.smooth, f.inv_smooth, f.wq,
+                           f.w_scale, stream=stream)
+    return f
+
+
+def quant(x, inv_smooth, stream=None):
+    torch = _torch()
+    M, K = x.shape
+    xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    xs = torch.empty(M, dtype=torch.float32, device=x.device)
+    sq_quant_act_per_token(x, inv_smooth, xq, xs, stream=stream)
+    return xq, xs
+
+
+def gemm(xq, x_scale, wq, w_scale, out_kind: int = SQ_OUT_F16, stream=None):
+    torch = _torch()
+    dt = torch.float16 if out_kind == SQ_OUT_F16 else torch.int32
+    y = torch.empty((xq.shape[0], wq.shape[0]), dtype=dt, device=xq.device)
+    sq_w8a8_gemm(xq, x_scale, wq, w_scale, y, out_kind, stream=stream)
+    return y
+
+
+def smoothed_linear(x, folded: Folded, stream=None):
+    """Serving-time layer: per-token quantization of x, then the W8A8 product."""
+    xq, xs = quant(x, folded.inv_smooth, stream=stream)
+    return gemm(xq, xs, folded.wq, folded.w_scale, stream=stream)

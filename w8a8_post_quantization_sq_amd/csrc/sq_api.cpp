@@ -1,0 +1,145 @@
+// C ABI of the smoothed W8A8 linear layer: argument checks, then launches on
+// the caller's stream.  Every check runs before the first HIP call, so a call
+// rejected for its arguments has no side effects.  The only host-side data
+// work is the fold's check of the smoothing factors it has just computed.
+#include <math.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "sq.h"
+#include "sq_internal.h"
+
+#define SQ_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;   // M, N, T < 2^31
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline sq_status hip_status(hipError_t e) { return e == hipSuccess ? SQ_OK : SQ_ERR_HIP; }
+
+// K: 16 <= K <= SQ_MAX_K, K % 16 == 0 (int8 rows are whole 16-byte chunks).
+inline bool k_ok(int64_t K) { return K >= 16 && K <= SQ_MAX_K && (K % 16) == 0; }
+
+}  // namespace
+
+SQ_API const char *sq_status_str(int status) {
+    switch (status) {
+        case SQ_OK: return "SQ_OK";
+        case SQ_ERR_NULL: return "SQ_ERR_NULL: a required pointer is NULL";
+        case SQ_ERR_SHAPE: return "SQ_ERR_SHAPE: a size or stride is out of range";
+        case SQ_ERR_ALIGN: return "SQ_ERR_ALIGN: a pointer or stride breaks the 16-byte alignment rules";
+        case SQ_ERR_ALPHA: return "SQ_ERR_ALPHA: alpha must lie in [0, 1]";
+        case SQ_ERR_NONFINITE: return "SQ_ERR_NONFINITE: a statistic or factor is NaN, infinite or negative";
+        case SQ_ERR_RANGE: return "SQ_ERR_RANGE: a factor or its reciprocal is zero, infinite or subnormal";
+        case SQ_ERR_HIP: return "SQ_ERR_HIP: the HIP runtime reported an error";
+        case SQ_ERR_KIND: return "SQ_ERR_KIND: unknown out_kind";
+        default: return "unknown sq_status";
+    }
+}
+
+SQ_API int sq_version(void) { return 10000; }
+
+SQ_API sq_status sq_calibrate_absmax(const void *x_cal_f16, int64_t T, int64_t K, int64_t ldx,
+                                     float *act_absmax, int accumulate, void *stream) {
+    if (!act_absmax || (T > 0 && !x_cal_f16)) return SQ_ERR_NULL;
+    if (T < 0 || T >= kMaxDim || !k_ok(K) || ldx < K) return SQ_ERR_SHAPE;
+    if (!aligned16(act_absmax) || (x_cal_f16 && !aligned16(x_cal_f16)) || (ldx % 8) != 0)
+        return SQ_ERR_ALIGN;
+    const hipStream_t st = as_stream(stream);
+    if (!accumulate) {
+        sq_status s = hip_status(sq::launch_fill_f32(act_absmax, K, 0.0f, st));
+        if (s != SQ_OK) return s;
+    }
+    return hip_status(sq::launch_calib_absmax(static_cast<const uint16_t *>(x_cal_f16), T, K, ldx,
+                                              act_absmax, st));
+}
+
+SQ_API sq_status sq_smooth_fold_weights(const void *w_f16, int64_t K, int64_t N, int64_t ldw,
+                                        const float *act_absmax, float alpha,
+                                        const float *smooth_in, float *smooth_out,
+                                        float *inv_smooth_out, int8_t *wq, float *w_scale,
+                                        void *stream) {
+    if (!smooth_out || !inv_smooth_out || (!smooth_in && !act_absmax)) return SQ_ERR_NULL;
+    if (N > 0 && (!w_f16 || !wq || !w_scale)) return SQ_ERR_NULL;
+    if (N < 0 || N >= kMaxDim || !k_ok(K) || (N > 0 && ldw < N)) return SQ_ERR_SHAPE;
+    if (!aligned16(smooth_out) || !aligned16(inv_smooth_out) ||
+        (act_absmax && !aligned16(act_absmax)) || (smooth_in && !aligned16(smooth_in)))
+        return SQ_ERR_ALIGN;
+    if (N > 0 && (!aligned16(w_f16) || !aligned16(wq) || !aligned16(w_scale) || (ldw % 8) != 0))
+        return SQ_ERR_ALIGN;
+    if (!smooth_in && !(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_ALPHA;
+
+    const hipStream_t st = as_stream(stream);
+    const uint16_t *w = static_cast<const uint16_t *>(w_f16);
+    hipError_t e;
+    // aw_j into inv_smooth_out (also run with given factors: it checks W is finite)
+    if (N > 0) {
+        e = sq::launch_row_absmax(w, K, N, ldw, inv_smooth_out, st);
+    } else {
+        e = sq::launch_fill_f32(inv_smooth_out, K, 0.0f, st);
+    }
+    if (e != hipSuccess) return SQ_ERR_HIP;
+    e = sq::launch_smooth_factors(act_absmax, smooth_in, inv_smooth_out, alpha, K, smooth_out,
+                                  w_scale, N, st);
+    if (e != hipSuccess) return SQ_ERR_HIP;
+
+    // The one host step: look at s and 1/s before anything is written to wq.
+    std::vector<float> hs((size_t)K), hi((size_t)K);
+    e = hipMemcpyAsync(hs.data(), smooth_out, (size_t)K * sizeof(float), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(hi.data(), inv_smooth_out, (size_t)K * sizeof(float),
+                           hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return SQ_ERR_HIP;
+    bool nonfinite = false, range = false;
+    for (int64_t j = 0; j < K; ++j) {
+        if (isnan(hs[j])) nonfinite = true;
+        else if (!isnormal(hs[j]) || !isnormal(hi[j]) || hs[j] < 0.0f) range = true;
+    }
+    if (nonfinite) return SQ_ERR_NONFINITE;
+    if (range) return SQ_ERR_RANGE;
+    if (N == 0) return SQ_OK;
+
+    e = sq::launch_fold_colabsmax(w, K, N, ldw, smooth_out, w_scale, st);
+    if (e == hipSuccess) e = sq::launch_fold_quant(w, K, N, ldw, smooth_out, w_scale, wq, st);
+    if (e == hipSuccess) e = sq::launch_fold_finalize(w_scale, N, st);
+    return hip_status(e);
+}
+
+SQ_API sq_status sq_quant_act_per_token(const void *x_f16, int64_t M, int64_t K, int64_t ldx,
+                                        const float *inv_smooth, int8_t *xq, float *x_scale,
+                                        void *stream) {
+    if (!inv_smooth || (M > 0 && (!x_f16 || !xq || !x_scale))) return SQ_ERR_NULL;
+    if (M < 0 || M >= kMaxDim || !k_ok(K) || ldx < K) return SQ_ERR_SHAPE;
+    if (!aligned16(inv_smooth) || (ldx % 8) != 0) return SQ_ERR_ALIGN;
+    if (M > 0 && (!aligned16(x_f16) || !aligned16(xq) || !aligned16(x_scale))) return SQ_ERR_ALIGN;
+    return hip_status(sq::launch_quant_act(static_cast<const uint16_t *>(x_f16), M, K, ldx,
+                                           inv_smooth, xq, x_scale, as_stream(stream)));
+}
+
+SQ_API sq_status sq_w8a8_gemm(const int8_t *xq, const float *x_scale, const int8_t *wq,
+                              const float *w_scale, int64_t M, int64_t N, int64_t K, void *y,
+                              int64_t ldy, int out_kind, void *stream) {
+    if (out_kind != SQ_OUT_F16 && out_kind != SQ_OUT_I32) return SQ_ERR_KIND;
+    const bool work = M > 0 && N > 0;
+    if (work && (!xq || !wq || !y)) return SQ_ERR_NULL;
+    if (work && out_kind == SQ_OUT_F16 && (!x_scale || !w_scale)) return SQ_ERR_NULL;
+    if (M < 0 || N < 0 || M >= kMaxDim || N >= kMaxDim || !k_ok(K)) return SQ_ERR_SHAPE;
+    if (work && ldy < N) return SQ_ERR_SHAPE;
+    // one workgroup per 128 x 128 output tile: the tile count must fit a 1-D grid
+    if (work && ((M + 127) / 128) * ((N + 127) / 128) >= kMaxDim) return SQ_ERR_SHAPE;
+    if (work) {
+        if (!aligned16(xq) || !aligned16(wq)) return SQ_ERR_ALIGN;
+        if (out_kind == SQ_OUT_F16 && (!aligned16(x_scale) || !aligned16(w_scale))) return SQ_ERR_ALIGN;
+        // y needs only its element alignment; any ldy >= N works
+        if (((uintptr_t)y % (out_kind == SQ_OUT_F16 ? 2u : 4u)) != 0) return SQ_ERR_ALIGN;
+    }
+    if (!work) return SQ_OK;
+    return hip_status(sq::launch_gemm(xq, x_scale, wq, w_scale, M, N, K, y, ldy, out_kind,
+                                      as_stream(stream)));
+}

@@ -1,0 +1,38 @@
+// Library-internal declarations shared by the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sq {
+
+// ---- launchers (one per kernel family) -------------------------------------
+
+hipError_t launch_fill_f32(float *p, int64_t n, float v, hipStream_t st);
+
+hipError_t launch_calib_absmax(const uint16_t *x, int64_t T, int64_t K, int64_t ldx,
+                               float *ax, hipStream_t st);
+
+hipError_t launch_row_absmax(const uint16_t *w, int64_t K, int64_t N, int64_t ldw,
+                             float *aw, hipStream_t st);
+
+hipError_t launch_smooth_factors(const float *ax, const float *smooth_in, float *aw_in_inv_out,
+                                 float alpha, int64_t K, float *s_out, float *w_scale_zero,
+                                 int64_t N, hipStream_t st);
+
+hipError_t launch_fold_colabsmax(const uint16_t *w, int64_t K, int64_t N, int64_t ldw,
+                                 const float *s, float *amax, hipStream_t st);
+
+hipError_t launch_fold_quant(const uint16_t *w, int64_t K, int64_t N, int64_t ldw,
+                             const float *s, const float *amax, int8_t *wq, hipStream_t st);
+
+hipError_t launch_fold_finalize(float *w_scale, int64_t N, hipStream_t st);
+
+hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                            const float *inv_s, int8_t *xq, float *x_scale, hipStream_t st);
+
+hipError_t launch_gemm(const int8_t *xq, const float *x_scale, const int8_t *wq,
+                       const float *w_scale, int64_t M, int64_t N, int64_t K, void *y,
+                       int64_t ldy, int out_kind, hipStream_t st);
+
+}  // namespace sq
