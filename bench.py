@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of the SmoothQuant-smoothed W8A8 linear layer on one MI355X.
+
+One step is one pass of every stage of the layer over one batch of synthetic
+input, each through the C ABI on one HIP stream:
+  A1 sq_calibrate_absmax     per-channel max |X| over the 512 calibration tokens
+  A2+A3 sq_smooth_fold_weights  smoothing factors, fold into W, int8 per channel
+  A4 sq_quant_act_per_token  per-token int8 quantization of the batch X
+  A5+A6 sq_w8a8_gemm         int8 matrix-core product + fp16 epilogue
+The default workload is the LLaMA-7B q/k/v-style layer: X fp16 2048 x 4096
+(1% of channels x U(50, 100)), W fp16 4096 x 4096 ~ N(0, 0.02^2), alpha 0.5,
+calibration on a separate 512-token draw.
+
+Printed: one JSON line with the whole-step throughput (2MNK per step / wall
+time), the per-stage GPU times from HIP events recorded on the library's
+stream, the serving-time layer (A4 + A5/A6, the two calls a deployed layer
+makes per batch), the product kernel against the int8 matrix-core roofline,
+and the CPU oracle timed on a bounded sample as a baseline.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 matrix-core peak, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_qkv4096.txt")
+GEMM_SRC = os.path.join(ROOT, "w8a8_post_quantization_sq_amd", "csrc", "k_gemm.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """HBM bytes per product launch from the committed rocprofv3 counter
+    summary, or None when it is missing, for another workload, or was taken
+    on a different version of the product kernel."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("workload") != workload or kv.get("k_gemm_sha256_16") != source_hash(GEMM_SRC):
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, wl, budget_s):
+    """The CPU oracle, as it stands, on a bounded sample of the same step:
+    A1-A3 in full, then A4-A6 on blocks of 64 tokens until the time budget is
+    spent; the step time is scaled to the whole batch."""
+    import numpy as np
+    import oracle
+    t0 = time.perf_counter()
+    ax = oracle.calibrate_absmax(inp.x_cal)
+    s, inv, st = oracle.smoothing_factors(ax, oracle.row_absmax(inp.w), wl.alpha)
+    wq, wsc = oracle.fold_quant_weights(inp.w, s)
+    t_off = time.perf_counter() - t0
+    rows = 0
+    t1 = time.perf_counter()
+    while rows < wl.M:
+        r1 = min(wl.M, rows + 64)
+        oracle.layer_block(np.ascontiguousarray(inp.x[rows:r1]), inv, wq, wsc)
+        rows = r1
+        if time.perf_counter() - t1 > budget_s:
+            break
+    t_layer = time.perf_counter() - t1
+    t_step = t_off + t_layer * (wl.M / rows)
+    ops = 2.0 * wl.M * wl.N * wl.K
+    return {
+        "value": ops / t_step / 1e12, "unit": "TOP/s", "cores": 1, "kind": "oracle",
+        "sample": (f"single-threaded C oracle: calibration, factors and fold in full "
+                   f"({t_off:.2f} s), quantization + int32 product + dequantization on the "
+                   f"first {rows} of {wl.M} tokens ({t_layer:.2f} s), scaled to the batch: "
+                   f"{t_step:.1f} s per step"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qkv4096",
+                    help="qkv4096 | down11008 | prefill8192x3 | tiny")
+    ap.add_argument("--alpha", type=float, default=None)
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle layer work in the CPU baseline (0: skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; multi-GPU runs are not part of it "
+              "(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import w8a8_post_quantization_sq_amd as sq
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    L = sq.lib()     # raises if the HIP library is not built: there is no fallback
+    dev = torch.device("cuda:0")
+    wl = workloads.WORKLOADS[args.workload]
+    if args.alpha is not None:
+        wl = wl.with_alpha(args.alpha)
+    M, K, N, T = wl.M, wl.K, wl.N, wl.T_cal or wl.M
+    log(f"workload {wl.name}: M={M} K={K} N={N} T_cal={T} alpha={wl.alpha}")
+    inp = workloads.generate(wl)
+
+    # inputs resident in HBM before the timed region
+    x = torch.from_numpy(inp.x).to(dev)
+    xcal = torch.from_numpy(inp.x_cal).to(dev)
+    w = torch.from_numpy(inp.w).to(dev)
+    ax = torch.empty(K, dtype=torch.float32, device=dev)
+    s = torch.empty(K, dtype=torch.float32, device=dev)
+    inv = torch.empty(K, dtype=torch.float32, device=dev)
+    wq = torch.empty(sq.packed_bytes(N, K), dtype=torch.int8, device=dev)   # packed codes
+    wsc = torch.empty(N, dtype=torch.float32, device=dev)
+    xq = torch.empty(sq.packed_bytes(M, K), dtype=torch.int8, device=dev)
+    xsc = torch.empty(M, dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    hs = stream.cuda_stream
+    p = {k: t.data_ptr() for k, t in dict(x=x, xcal=xcal, w=w, ax=ax, s=s, inv=inv, wq=wq,
+                                            wsc=wsc, xq=xq, xsc=xsc, y=y).items()}
+    alpha = float(wl.alpha)
+
+    def step(ev=None):
+        # each call goes straight through the C ABI with the tensors' device pointers
+        if ev: ev[0].record(stream)
+        st = L.sq_calibrate_absmax(p["xcal"], T, K, K, p["ax"], 0, hs)
+        if ev: ev[1].record(stream)
+        st |= L.sq_smooth_fold_weights(p["w"], K, N, N, p["ax"], alpha, None, p["s"], p["inv"],
+                                       p["wq"], p["wsc"], hs)
+        if ev: ev[2].record(stream)
+        st |= L.sq_quant_act_per_token(p["x"], M, K, K, p["inv"], p["xq"], p["xsc"], hs)
+        if ev: ev[3].record(stream)
+        st |= L.sq_w8a8_gemm(p["xq"], p["xsc"], p["wq"], p["wsc"], M, N, K, p["y"], N,
+                             sq.SQ_OUT_F16, hs)
+        if ev: ev[4].record(stream)
+        if st:
+            raise RuntimeError(f"library call failed: status bits {st}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"timed {args.steps} steps in {wall:.3f} s")
+
+    names = ["calibrate", "fold", "quant", "gemm"]
+    per = {n: 0.0 for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            per[n] += ev[j].elapsed_time(ev[j + 1])
+    per = {n: v / args.steps for n, v in per.items()}    # ms per call
+
+    ops = 2.0 * M * N * K
+    ms_step = wall * 1e3 / args.steps
+    gemm_tops = ops / (per["gemm"] * 1e-3) / 1e12
+    layer_ms = per["quant"] + per["gemm"]
+    layer_tops = ops / (layer_ms * 1e-3) / 1e12
+    traffic = read_traffic(wl.name)
+    # algorithmic HBM bytes of the runtime layer per batch (int8 weights and
+    # scales, fp16 X in, 1/s, fp16 Y out)
+    layer_bytes = K * N + 4 * N + 2 * M * K + 4 * K + 2 * M * N
+
+    out = {
+        "metric": "W8A8 smoothed-linear TOPS (M>=2048) & GB/s (M<=16), % of MI355X roofline",
+        "value": round(ops * args.steps / wall / 1e12, 3),
+        "unit": "TOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic (seeded, outlier structure of the workload; no trained weights)",
+        "config": {"workload": f"{wl.name}: {wl.description}", "M": M, "K": K, "N": N,
+                   "alpha": wl.alpha, "calibration_tokens": T, "seed": wl.seed,
+                   "step": "calibrate + smooth/fold + per-token quant + W8A8 GEMM"},
+        "stage_ms": {n: round(v, 4) for n, v in per.items()},
+        "layer": {"what": "serving-time layer: per-token quant + W8A8 GEMM (weights folded offline)",
+                  "ms": round(layer_ms, 4), "tops": round(layer_tops, 2),
+                  "frac_int8_peak": round(layer_tops / PEAK_INT8_TOPS, 4),
+                  "hbm_gbs_algorithmic": round(layer_bytes / (layer_ms * 1e-3) / 1e9, 1)},
+        "roofline": {"kernel": "k_gemm_w8a8 (sq_w8a8_gemm)", "bound": "mfma",
+                     "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                     "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": traffic,
+                     "per_launch": f"2*M*N*K = {ops:.4g} int8 ops per launch"},
+        "cpu_baseline": None,
+    }
+    if args.cpu_budget > 0:
+        log("timing the CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -32,6 +32,18 @@
  *   - Stateless and reentrant: calls on different streams may run
  *     concurrently; calls that write the same buffers must be ordered by the
  *     caller.
+ *
+ * Packed int8 operands.  The int8 codes of activations (xq) and folded
+ * weights (wq) are stored in the operand order of the gfx950 int8 matrix
+ * instruction (v_mfma_i32_16x16x64_i8), so that every 16-row x 64-byte
+ * fragment is one contiguous, naturally aligned 1 KiB run:
+ *   for a code matrix R[rows][K] (K % 16 == 0), KW = ceil(K / 64),
+ *   element R[r][k] lives at byte
+ *       ((r / 16) * KW + k / 64) * 1024 + ((k % 64) / 16) * 256 + (r % 16) * 16 + k % 16
+ *   and the buffer holds sq_packed_bytes(rows, K) = ceil(rows / 16) * KW * 1024
+ *   bytes.  Padding bytes (rows >= `rows` of the last row block, k >= K of the
+ *   last window) must be zero; the library's producers write them as zero.
+ * sq_pack_i8 / sq_unpack_i8 convert between this layout and row-major codes.
  */
 #ifndef SQ_H
 #define SQ_H
@@ -64,6 +76,10 @@ enum {
 
 /* Largest K: 131056 * 128 * 128 < 2^31, so int32 sums of any int8 codes are exact. */
 #define SQ_MAX_K 131056
+
+/* Bytes of a packed int8 operand with `rows` rows of K codes (0 when an
+ * argument is out of range). */
+int64_t sq_packed_bytes(int64_t rows, int64_t K);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *sq_status_str(int status);
@@ -114,7 +130,8 @@ sq_status sq_calibrate_absmax(const void *x_cal_f16, int64_t T, int64_t K, int64
  *   smooth_out      float [K], written: s
  *   inv_smooth_out  float [K], written: 1.0f / s  (the input of
  *                   sq_quant_act_per_token)
- *   wq          int8 [N][K], written: K-contiguous folded codes
+ *   wq          int8, packed (sq_packed_bytes(N, K) bytes), written: the folded
+ *               codes wq[n][j], padding zero
  *   w_scale     float [N], written
  * Several consumers of one activation: pass their weights side by side as one
  * K x (N1 + N2 + ...) matrix (ldw = total), so s uses the maximum over all of
@@ -144,7 +161,8 @@ sq_status sq_smooth_fold_weights(const void *w_f16, int64_t K, int64_t N, int64_
  *
  *   x           fp16 [M][ldx]
  *   inv_smooth  float [K] (inv_smooth_out of the fold)
- *   xq          int8 [M][K], written
+ *   xq          int8, packed (sq_packed_bytes(M, K) bytes), written: the codes
+ *               xq[m][j], padding zero
  *   x_scale     float [M], written
  * Asynchronous.
  */
@@ -160,14 +178,24 @@ sq_status sq_quant_act_per_token(const void *x_f16, int64_t M, int64_t K, int64_
  *   SQ_OUT_F16: y[m][n] = fp16_rne((float(acc) * x_scale[m]) * w_scale[n])
  *   SQ_OUT_I32: y[m][n] = acc                     (x_scale, w_scale may be NULL)
  *
- *   xq       int8 [M][K]      (row stride K)
- *   wq       int8 [N][K]      (row stride K)
+ *   xq       int8 packed codes of M tokens (sq_quant_act_per_token's output)
+ *   wq       int8 packed codes of N output channels (the fold's output)
  *   y        fp16 or int32 [M][ldy]
  * Asynchronous.
  */
 sq_status sq_w8a8_gemm(const int8_t *xq, const float *x_scale, const int8_t *wq,
                        const float *w_scale, int64_t M, int64_t N, int64_t K,
                        void *y, int64_t ldy, int out_kind, void *stream);
+
+/*
+ * Layout helpers (not part of the layer's arithmetic): row-major int8 codes
+ * src[rows][ld] -> packed dst (padding written as zero), and back.  For
+ * callers that hold codes in row-major order.  Asynchronous.
+ */
+sq_status sq_pack_i8(const int8_t *src, int64_t rows, int64_t K, int64_t ld, int8_t *dst,
+                     void *stream);
+sq_status sq_unpack_i8(const int8_t *src, int64_t rows, int64_t K, int8_t *dst, int64_t ld,
+                       void *stream);
 
 #ifdef __cplusplus
 }

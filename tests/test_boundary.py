@@ -56,7 +56,7 @@ def test_status_strings_and_version(sq):
         s = sq.status_str(code)
         assert s.startswith("SQ_")
     assert sq.status_str(99) == "unknown sq_status"
-    assert sq.lib().sq_version() == 10000
+    assert sq.lib().sq_version() == 10100
     assert sq.SQ_MAX_K * 128 * 128 < 2 ** 31 and sq.SQ_MAX_K % 16 == 0
 
 
@@ -187,3 +187,58 @@ def test_binding_refuses_cpu_tensors(sq):
         sq.sq_calibrate_absmax(x, ax)
     with pytest.raises(TypeError):
         sq.sq_calibrate_absmax(x.float(), ax)
+
+
+# ---- packed layout ----------------------------------------------------------------
+
+def test_packed_bytes(sq):
+    L = sq.lib()
+    assert L.sq_packed_bytes(16, 64) == 1024
+    assert L.sq_packed_bytes(17, 64) == 2048
+    assert L.sq_packed_bytes(1, 80) == 2048
+    assert L.sq_packed_bytes(0, 64) == 0
+    assert L.sq_packed_bytes(2048, 4096) == 2048 * 4096
+    assert L.sq_packed_bytes(5, 40) == 0          # K % 16 != 0
+    assert L.sq_packed_bytes(-1, 64) == 0
+
+
+@pytest.mark.parametrize("fn", ["sq_pack_i8", "sq_unpack_i8"])
+@pytest.mark.parametrize("args,expect", [
+    ((None, 4, 64, 64, P), "SQ_ERR_NULL"),
+    ((P, 4, 64, 64, None), "SQ_ERR_NULL"),
+    ((P, -1, 64, 64, Q), "SQ_ERR_SHAPE"),
+    ((P, 4, 72, 80, Q), "SQ_ERR_SHAPE"),
+    ((P, 4, 64, 48, Q), "SQ_ERR_SHAPE"),
+    ((MIS, 4, 64, 64, Q), "SQ_ERR_ALIGN"),
+    ((P, 4, 64, 64, MIS), "SQ_ERR_ALIGN"),
+    ((P, 4, 64, 72, Q), "SQ_ERR_ALIGN"),      # row stride % 16
+])
+def test_pack_helpers_reject(sq, fn, args, expect):
+    src, rows, K, ld, dst = args
+    if fn == "sq_pack_i8":
+        st = sq.lib().sq_pack_i8(src, rows, K, ld, dst, None)
+    else:
+        st = sq.lib().sq_unpack_i8(src, rows, K, dst, ld, None)
+    assert sq.status_str(st).startswith(expect)
+
+
+def test_layout_helper_matches_header_formula():
+    """tests/layout.py against the element formula stated in include/sq.h,
+    element by element, for ragged rows and K."""
+    import numpy as np
+    from layout import pack, packed_bytes, unpack
+    text = open(HEADER).read()
+    assert "((r / 16) * KW + k / 64) * 1024 + ((k % 64) / 16) * 256 + (r % 16) * 16 + k % 16" in text
+    for rows, K in [(1, 16), (17, 80), (35, 208)]:
+        R = np.random.default_rng(rows).integers(-128, 128, (rows, K)).astype(np.int8)
+        buf = pack(R)
+        KW = -(-K // 64)
+        assert buf.size == packed_bytes(rows, K) == -(-rows // 16) * KW * 1024
+        seen = np.zeros(buf.size, bool)
+        for r in range(rows):
+            for k in range(K):
+                off = ((r // 16) * KW + k // 64) * 1024 + ((k % 64) // 16) * 256 + (r % 16) * 16 + k % 16
+                assert buf[off] == R[r, k]
+                seen[off] = True
+        assert np.all(buf[~seen] == 0)
+        assert np.array_equal(unpack(buf, rows, K), R)

@@ -7,11 +7,16 @@ statistics, factors and int32 sums must be bit-exact; fp16 outputs within
 workloads run at their real sizes in the launch configuration the benchmark
 times; where the oracle's O(MNK) product would be slow, a seeded sample of
 rows (always including the first and last token) is compared.
+
+The library stores int8 codes in its packed operand order; the tests unpack
+them with an independent numpy permutation (tests/layout.py) before
+comparing, and check that the padding is zero.
 """
 import numpy as np
 import pytest
 
 import workloads as W
+from layout import pack, packed_bytes, padding_is_zero, unpack
 
 pytestmark = pytest.mark.gpu
 
@@ -143,7 +148,9 @@ def test_fold_matches_oracle(sq, dev, orc, name, alpha):
     assert bits_equal(H(f.inv_smooth), inv)
     wq, wsc = orc.fold_quant_weights(w, s)
     assert bits_equal(H(f.w_scale), wsc)
-    assert np.array_equal(H(f.wq), wq)
+    g = H(f.wq)
+    assert np.array_equal(unpack(g, wl.N, wl.K), wq)
+    assert padding_is_zero(g, wl.N, wl.K)
 
 
 def test_fold_given_factors_and_consumer_slices(sq, dev, orc):
@@ -154,17 +161,17 @@ def test_fold_given_factors_and_consumer_slices(sq, dev, orc):
     wcat = np.concatenate(ws, axis=1)
     ax = orc.calibrate_absmax(W.random_f16(210, 64, K, 5.0))
     fcat = sq.fold(T(wcat, dev), T(ax, dev), 0.5)
-    wq_cat = H(fcat.wq)
+    wq_cat = unpack(H(fcat.wq), wcat.shape[1], K)
     ws_cat = H(fcat.w_scale)
     off = 0
     for w in ws:
         f1 = sq.fold(T(w, dev), None, 0.5, smooth_in=fcat.smooth)
         n = w.shape[1]
-        assert np.array_equal(H(f1.wq), wq_cat[off:off + n])
+        assert np.array_equal(unpack(H(f1.wq), n, K), wq_cat[off:off + n])
         assert bits_equal(H(f1.w_scale), ws_cat[off:off + n])
         assert bits_equal(H(f1.smooth), H(fcat.smooth))
         q1, s1 = orc.fold_quant_weights(w, H(fcat.smooth))
-        assert np.array_equal(H(f1.wq), q1)
+        assert np.array_equal(unpack(H(f1.wq), n, K), q1)
         off += n
 
 
@@ -178,7 +185,9 @@ def test_fold_ragged_and_strided(sq, dev, orc, K, N, ldw):
     s, inv, _ = orc.smoothing_factors(ax, orc.row_absmax(wc), 0.5)
     wq, wsc = orc.fold_quant_weights(wc, s)
     assert bits_equal(H(f.smooth), s)
-    assert np.array_equal(H(f.wq), wq) and bits_equal(H(f.w_scale), wsc)
+    g = H(f.wq)
+    assert np.array_equal(unpack(g, N, K), wq) and bits_equal(H(f.w_scale), wsc)
+    assert padding_is_zero(g, N, K)
 
 
 def test_fold_degenerate_channels(sq, dev, orc):
@@ -194,8 +203,9 @@ def test_fold_degenerate_channels(sq, dev, orc):
     s, inv, _ = orc.smoothing_factors(ax, orc.row_absmax(w), 0.5)
     assert H(f.smooth)[5] == 1.0 and H(f.smooth)[9] == 1.0
     wq, wsc = orc.fold_quant_weights(w, s)
-    assert np.array_equal(H(f.wq), wq) and bits_equal(H(f.w_scale), wsc)
-    assert H(f.w_scale)[7] == 0 and np.all(H(f.wq)[7] == 0)
+    g = unpack(H(f.wq), N, K)
+    assert np.array_equal(g, wq) and bits_equal(H(f.w_scale), wsc)
+    assert H(f.w_scale)[7] == 0 and np.all(g[7] == 0)
 
 
 def test_fold_data_errors_leave_codes_untouched(sq, dev, orc):
@@ -206,8 +216,8 @@ def test_fold_data_errors_leave_codes_untouched(sq, dev, orc):
 
     def run(w_, ax_, alpha=0.5, sin=None):
         f = sq.Folded(torch.empty(K, device=dev), torch.empty(K, device=dev),
-                      torch.full((N, K), 55, dtype=torch.int8, device=dev),
-                      torch.empty(N, device=dev))
+                      torch.full((packed_bytes(N, K),), 55, dtype=torch.int8, device=dev),
+                      torch.empty(N, device=dev), K, N)
         with pytest.raises(sq.SqError) as ei:
             sq.sq_smooth_fold_weights(T(w_, dev), None if ax_ is None else T(ax_, dev), alpha,
                                       None if sin is None else T(sin, dev), f.smooth,
@@ -244,7 +254,9 @@ def test_quant_matches_oracle(sq, dev, orc, name):
     xq, xs = sq.quant(T(inp.x, dev), T(inv, dev))
     rq, rs = orc.quant_act_per_token(inp.x, inv)
     assert bits_equal(H(xs), rs)
-    assert np.array_equal(H(xq), rq)
+    g = H(xq)
+    assert np.array_equal(unpack(g, inp.x.shape[0], wl.K), rq)
+    assert padding_is_zero(g, inp.x.shape[0], wl.K)
 
 
 @pytest.mark.parametrize("M,K,ld", [(1, 16, 16), (3, 48, 56), (17, 2064, 2064), (2, 4112, 4128),
@@ -254,7 +266,9 @@ def test_quant_ragged_long_and_strided(sq, dev, orc, M, K, ld):
     inv = W.random_scales(601, K, 0.05, 3.0)
     xq, xs = sq.quant(T(x, dev)[:, :K], T(inv, dev))
     rq, rs = orc.quant_act_per_token(np.ascontiguousarray(x[:, :K]), inv)
-    assert bits_equal(H(xs), rs) and np.array_equal(H(xq), rq)
+    g = H(xq)
+    assert bits_equal(H(xs), rs) and np.array_equal(unpack(g, M, K), rq)
+    assert padding_is_zero(g, M, K)
 
 
 def test_quant_ties_and_degenerate_rows(sq, dev, orc):
@@ -270,8 +284,9 @@ def test_quant_ties_and_degenerate_rows(sq, dev, orc):
     ones = np.ones(16, np.float32)
     xq, xs = sq.quant(T(x, dev), T(ones, dev))
     rq, rs = orc.quant_act_per_token(x, ones)
-    assert bits_equal(H(xs), rs) and np.array_equal(H(xq), rq)
-    assert H(xq)[0].tolist() == [127, 2, 4, -2, 0, 2, 0, 126, -126, 6, -6, 0, 8, -8, 64, 0]
+    g = unpack(H(xq), 5, 16)
+    assert bits_equal(H(xs), rs) and np.array_equal(g, rq)
+    assert g[0].tolist() == [127, 2, 4, -2, 0, 2, 0, 126, -126, 6, -6, 0, 8, -8, 64, 0]
     assert H(xs)[1] == 0 and np.isnan(H(xs)[2]) and np.isnan(H(xs)[3])
 
 
@@ -285,7 +300,7 @@ GEMM_SHAPES = [(1, 1, 16), (3, 5, 48), (17, 100, 80), (100, 200, 64), (128, 128,
 def test_gemm_i32_bit_exact(sq, dev, orc, M, N, K):
     xq = W.random_i8(700 + M, M, K, -128, 127)
     wq = W.random_i8(701 + N, N, K, -128, 127)
-    acc = sq.gemm(T(xq, dev), None, T(wq, dev), None, out_kind=sq.SQ_OUT_I32)
+    acc = sq.gemm(T(pack(xq), dev), None, T(pack(wq), dev), None, M, N, K, out_kind=sq.SQ_OUT_I32)
     assert np.array_equal(H(acc), orc.gemm_i32(xq, wq))
 
 
@@ -295,7 +310,7 @@ def test_gemm_f16_epilogue(sq, dev, orc, M, N, K):
     wq = W.random_i8(801 + N, N, K)
     xs = W.random_scales(802, M, 1e-3, 2e-2)
     ws = W.random_scales(803, N, 1e-3, 2e-2)
-    y = sq.gemm(T(xq, dev), T(xs, dev), T(wq, dev), T(ws, dev))
+    y = sq.gemm(T(pack(xq), dev), T(xs, dev), T(pack(wq), dev), T(ws, dev), M, N, K)
     assert_f16_close(H(y), orc.dequant(orc.gemm_i32(xq, wq), xs, ws))
 
 
@@ -307,7 +322,7 @@ def test_gemm_extreme_sums_and_strided_output(sq, dev, orc):
     wq = np.full((3, K), -127, np.int8)
     wq[1] = 127
     wq[2] = -128
-    acc = sq.gemm(T(xq, dev), None, T(wq, dev), None, out_kind=sq.SQ_OUT_I32)
+    acc = sq.gemm(T(pack(xq), dev), None, T(pack(wq), dev), None, 2, 3, K, out_kind=sq.SQ_OUT_I32)
     assert np.array_equal(H(acc), orc.gemm_i32(xq, wq))
     # output rows with a stride larger than N
     xq = W.random_i8(900, 40, 64)
@@ -315,7 +330,7 @@ def test_gemm_extreme_sums_and_strided_output(sq, dev, orc):
     xs = W.random_scales(902, 40)
     ws = W.random_scales(903, 24)
     big = torch.full((40, 32), 7.0, dtype=torch.float16, device=dev)
-    sq.sq_w8a8_gemm(T(xq, dev), T(xs, dev), T(wq, dev), T(ws, dev), big[:, :24])
+    sq.sq_w8a8_gemm(T(pack(xq), dev), T(xs, dev), T(pack(wq), dev), T(ws, dev), big[:, :24], 64)
     out = H(big)
     assert np.all(out[:, 24:] == 7.0)
     assert_f16_close(out[:, :24], orc.dequant(orc.gemm_i32(xq, wq), xs, ws))
@@ -327,7 +342,7 @@ def test_gemm_nan_row_propagates(sq, dev, orc):
     xs = W.random_scales(912, 4)
     xs[2] = np.nan
     ws = W.random_scales(913, 8)
-    y = H(sq.gemm(T(xq, dev), T(xs, dev), T(wq, dev), T(ws, dev)))
+    y = H(sq.gemm(T(pack(xq), dev), T(xs, dev), T(pack(wq), dev), T(ws, dev), 4, 8, 64))
     assert np.isnan(y[2]).all() and np.isfinite(np.delete(y, 2, axis=0)).all()
 
 
@@ -345,15 +360,17 @@ def test_end_to_end(sq, dev, orc, name, alpha, nrows):
     ax = sq.calibrate(T(inp.x_cal, dev))
     f = sq.fold(T(inp.w, dev), ax, alpha)
     xq, xs = sq.quant(xg, f.inv_smooth)
-    y = sq.gemm(xq, xs, f.wq, f.w_scale)
-    acc = sq.gemm(xq, xs, f.wq, f.w_scale, out_kind=sq.SQ_OUT_I32)
+    y = sq.gemm(xq, xs, f.wq, f.w_scale, wl.M, wl.N, wl.K)
+    acc = sq.gemm(xq, xs, f.wq, f.w_scale, wl.M, wl.N, wl.K, out_kind=sq.SQ_OUT_I32)
     rows = sample_rows(wl.M, nrows, 17)
     ref = orc.smoothed_linear(inp.x, inp.x_cal, inp.w, alpha, rows=rows)
     assert ref.status == 0
     assert bits_equal(H(ax), ref.ax)
     assert bits_equal(H(f.smooth), ref.s) and bits_equal(H(f.inv_smooth), ref.inv_s)
-    assert bits_equal(H(f.w_scale), ref.w_scale) and np.array_equal(H(f.wq), ref.wq)
-    assert bits_equal(H(xs), ref.x_scale) and np.array_equal(H(xq), ref.xq)
+    assert bits_equal(H(f.w_scale), ref.w_scale)
+    assert np.array_equal(unpack(H(f.wq), wl.N, wl.K), ref.wq)
+    assert bits_equal(H(xs), ref.x_scale)
+    assert np.array_equal(unpack(H(xq), wl.M, wl.K), ref.xq)
     accg = H(acc)[rows]
     assert np.array_equal(accg, ref.acc)
     err = assert_f16_close(H(y)[rows], ref.y64)
@@ -369,6 +386,40 @@ def test_repeat_runs_are_bitwise_identical(sq, dev, orc):
     assert bits_equal(ax1, ax2)
     f = sq.fold(T(inp.w, dev), T(ax1, dev), 0.5)
     xq, xs = sq.quant(T(inp.x, dev), f.inv_smooth)
-    y1 = H(sq.gemm(xq, xs, f.wq, f.w_scale))
-    y2 = H(sq.gemm(xq, xs, f.wq, f.w_scale))
+    y1 = H(sq.gemm(xq, xs, f.wq, f.w_scale, wl.M, wl.N, wl.K))
+    y2 = H(sq.gemm(xq, xs, f.wq, f.w_scale, wl.M, wl.N, wl.K))
     assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+
+
+# ---- layout helpers -------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,K,ld", [(1, 16, 16), (17, 80, 96), (64, 4096, 4096), (33, 11008, 11024)])
+def test_pack_unpack_helpers(sq, dev, rows, K, ld):
+    import torch
+    codes = W.random_i8(1000 + rows, rows, ld, -128, 127)
+    src = T(codes, dev)[:, :K]
+    packed = sq.pack_i8(src)
+    ref = pack(np.ascontiguousarray(codes[:, :K]))
+    assert np.array_equal(H(packed)[:ref.size], ref)
+    back = torch.full((rows, ld), 9, dtype=torch.int8, device=dev)
+    sq.sq_unpack_i8(packed, back[:, :K])
+    out = H(back)
+    assert np.array_equal(out[:, :K], codes[:, :K]) and np.all(out[:, K:] == 9)
+
+
+@pytest.mark.parametrize("M,N,ldy,off", [(100, 72, 80, 0), (300, 130, 136, 8), (257, 64, 72, 4)])
+def test_gemm_tile_path_strided_and_offset_output(sq, dev, orc, M, N, ldy, off):
+    """Token counts on the tile kernel with output rows of stride ldy >= N,
+    starting `off` elements into the buffer (8- or 16-byte aligned or not)."""
+    import torch
+    K = 192
+    xq = W.random_i8(1100 + M, M, K)
+    wq = W.random_i8(1101 + N, N, K)
+    xs = W.random_scales(1102, M)
+    ws = W.random_scales(1103, N)
+    big = torch.full((M * ldy + 64,), 5.0, dtype=torch.float16, device=dev)
+    view = big[off:off + M * ldy].view(M, ldy)[:, :N]
+    sq.sq_w8a8_gemm(T(pack(xq), dev), T(xs, dev), T(pack(wq), dev), T(ws, dev), view, K)
+    out = H(big)[off:off + M * ldy].reshape(M, ldy)
+    assert_f16_close(out[:, :N], orc.dequant(orc.gemm_i32(xq, wq), xs, ws))
+    assert np.all(out[:, N:] == 5.0) and np.all(H(big)[:off] == 5.0)

@@ -8,9 +8,13 @@ library, or without a GPU, the calls raise.
 
 Same-name calls (caller-allocated outputs, as in the C ABI):
     sq_calibrate_absmax, sq_smooth_fold_weights, sq_quant_act_per_token,
-    sq_w8a8_gemm
+    sq_w8a8_gemm, sq_packed_bytes, sq_pack_i8, sq_unpack_i8
 Allocating helpers built on them:
-    calibrate, fold, quant, gemm, smoothed_linear
+    calibrate, fold, quant, gemm, smoothed_linear, pack_i8, unpack_i8
+
+The int8 codes (xq, wq) travel as flat int8 tensors in the packed operand
+order the C ABI documents (16-row x 64-byte fragments of 1 KiB); their sizes
+are packed_bytes(rows, K).
 """
 from __future__ import annotations
 
@@ -35,8 +39,9 @@ SQ_OUT_F16 = 0
 SQ_OUT_I32 = 1
 SQ_MAX_K = 131056
 
-EXPORTS = ("sq_status_str", "sq_version", "sq_calibrate_absmax", "sq_smooth_fold_weights",
-           "sq_quant_act_per_token", "sq_w8a8_gemm")
+EXPORTS = ("sq_status_str", "sq_version", "sq_packed_bytes", "sq_calibrate_absmax",
+           "sq_smooth_fold_weights", "sq_quant_act_per_token", "sq_w8a8_gemm", "sq_pack_i8",
+           "sq_unpack_i8")
 
 _LIB = None
 
@@ -69,12 +74,23 @@ def lib() -> ctypes.CDLL:
         L.sq_quant_act_per_token.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
         L.sq_w8a8_gemm.restype = ci
         L.sq_w8a8_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i64, ci, vp]
+        L.sq_packed_bytes.restype = i64
+        L.sq_packed_bytes.argtypes = [i64, i64]
+        L.sq_pack_i8.restype = ci
+        L.sq_pack_i8.argtypes = [vp, i64, i64, i64, vp, vp]
+        L.sq_unpack_i8.restype = ci
+        L.sq_unpack_i8.argtypes = [vp, i64, i64, vp, i64, vp]
         _LIB = L
     return _LIB
 
 
 def status_str(status: int) -> str:
     return lib().sq_status_str(int(status)).decode()
+
+
+def packed_bytes(rows: int, K: int) -> int:
+    """Bytes of a packed int8 operand of `rows` rows of K codes."""
+    return int(lib().sq_packed_bytes(int(rows), int(K)))
 
 
 def _check(st: int, call: str) -> None:
@@ -131,11 +147,20 @@ def sq_calibrate_absmax(x_cal, act_absmax, accumulate: bool = False, stream=None
            "sq_calibrate_absmax")
 
 
+def _need_packed(t, rows, K, name):
+    torch = _torch()
+    _need(t, torch.int8, name, 1)
+    if not t.is_contiguous() or t.numel() < packed_bytes(rows, K):
+        raise ValueError(f"{name}: expected a contiguous int8 buffer of "
+                         f"{packed_bytes(rows, K)} bytes (packed {rows} x {K} codes)")
+
+
 def sq_smooth_fold_weights(w, act_absmax, alpha: float, smooth_in, smooth_out, inv_smooth_out,
                            wq, w_scale, stream=None) -> None:
     """Smoothing factors and the offline fold.  w: float16 [K][N] (input x
-    output channels); wq: int8 [N][K]; w_scale: float32 [N]; smooth_out,
-    inv_smooth_out: float32 [K]; smooth_in: None or float32 [K]."""
+    output channels); wq: packed int8 buffer of packed_bytes(N, K); w_scale:
+    float32 [N]; smooth_out, inv_smooth_out: float32 [K]; smooth_in: None or
+    float32 [K]."""
     torch = _torch()
     _need(w, torch.float16, "w", 2)
     K, N = w.shape
@@ -146,9 +171,7 @@ def sq_smooth_fold_weights(w, act_absmax, alpha: float, smooth_in, smooth_out, i
         _need(act_absmax, torch.float32, "act_absmax", 1)
     if smooth_in is not None:
         _need(smooth_in, torch.float32, "smooth_in", 1)
-    _need(wq, torch.int8, "wq", 2)
-    if tuple(wq.shape) != (N, K) or not wq.is_contiguous():
-        raise ValueError("wq must be a contiguous int8 [N][K] tensor")
+    _need_packed(wq, N, K, "wq")
     _check(lib().sq_smooth_fold_weights(_ptr(w), K, N, _ld(w), _ptr(act_absmax), float(alpha),
                                         _ptr(smooth_in), _ptr(smooth_out), _ptr(inv_smooth_out),
                                         _ptr(wq), _ptr(w_scale), _stream(stream, w.device)),
@@ -156,40 +179,56 @@ def sq_smooth_fold_weights(w, act_absmax, alpha: float, smooth_in, smooth_out, i
 
 
 def sq_quant_act_per_token(x, inv_smooth, xq, x_scale, stream=None) -> None:
-    """xq (int8 [M][K]) and x_scale (float32 [M]) of x (float16 [M][K]) * inv_smooth."""
+    """xq (packed int8, packed_bytes(M, K)) and x_scale (float32 [M]) of
+    x (float16 [M][K]) times inv_smooth."""
     torch = _torch()
     _need(x, torch.float16, "x", 2)
     _need(inv_smooth, torch.float32, "inv_smooth", 1)
-    _need(xq, torch.int8, "xq", 2)
     _need(x_scale, torch.float32, "x_scale", 1)
     M, K = x.shape
-    if tuple(xq.shape) != (M, K) or not xq.is_contiguous():
-        raise ValueError("xq must be a contiguous int8 [M][K] tensor")
+    _need_packed(xq, M, K, "xq")
     _check(lib().sq_quant_act_per_token(_ptr(x), M, K, _ld(x), _ptr(inv_smooth), _ptr(xq),
                                         _ptr(x_scale), _stream(stream, x.device)),
            "sq_quant_act_per_token")
 
 
-def sq_w8a8_gemm(xq, x_scale, wq, w_scale, y, out_kind: int = SQ_OUT_F16, stream=None) -> None:
-    """y [M][N] (float16, or int32 raw sums) = dequant(xq [M][K] . wq [N][K]^T)."""
+def sq_w8a8_gemm(xq, x_scale, wq, w_scale, y, K: int, out_kind: int = SQ_OUT_F16,
+                 stream=None) -> None:
+    """y [M][N] (float16, or int32 raw sums) from packed xq (M tokens) and
+    packed wq (N channels) of K codes each."""
     torch = _torch()
-    _need(xq, torch.int8, "xq", 2)
-    _need(wq, torch.int8, "wq", 2)
-    M, K = xq.shape
-    N = wq.shape[0]
-    if wq.shape[1] != K or not xq.is_contiguous() or not wq.is_contiguous():
-        raise ValueError("xq [M][K] and wq [N][K] must be contiguous with the same K")
     if out_kind == SQ_OUT_F16:
         _need(x_scale, torch.float32, "x_scale", 1)
         _need(w_scale, torch.float32, "w_scale", 1)
         _need(y, torch.float16, "y", 2)
     else:
         _need(y, torch.int32, "y", 2)
-    if tuple(y.shape) != (M, N):
-        raise ValueError("y must be [M][N]")
-    _check(lib().sq_w8a8_gemm(_ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), M, N, K,
+    M, N = y.shape
+    _need_packed(xq, M, K, "xq")
+    _need_packed(wq, N, K, "wq")
+    _check(lib().sq_w8a8_gemm(_ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), M, N, int(K),
                               _ptr(y), _ld(y), int(out_kind), _stream(stream, xq.device)),
            "sq_w8a8_gemm")
+
+
+def sq_pack_i8(src, dst, stream=None) -> None:
+    """Row-major int8 codes src [rows][K] -> packed dst (padding zeroed)."""
+    torch = _torch()
+    _need(src, torch.int8, "src", 2)
+    rows, K = src.shape
+    _need_packed(dst, rows, K, "dst")
+    _check(lib().sq_pack_i8(_ptr(src), rows, K, _ld(src), _ptr(dst), _stream(stream, src.device)),
+           "sq_pack_i8")
+
+
+def sq_unpack_i8(src, dst, stream=None) -> None:
+    """Packed src -> row-major int8 codes dst [rows][K]."""
+    torch = _torch()
+    _need(dst, torch.int8, "dst", 2)
+    rows, K = dst.shape
+    _need_packed(src, rows, K, "src")
+    _check(lib().sq_unpack_i8(_ptr(src), rows, K, _ptr(dst), _ld(dst), _stream(stream, dst.device)),
+           "sq_unpack_i8")
 
 
 # ---- allocating helpers ---------------------------------------------------------
@@ -199,8 +238,10 @@ class Folded:
     """The exported representation of one smoothed, quantized linear layer."""
     smooth: "object"       # float32 [K]  s
     inv_smooth: "object"   # float32 [K]  1/s
-    wq: "object"           # int8 [N][K]
+    wq: "object"           # packed int8 codes of the N x K folded weights
     w_scale: "object"      # float32 [N]
+    K: int = 0
+    N: int = 0
 
 
 def calibrate(x_cal, act_absmax=None, stream=None):
@@ -217,31 +258,48 @@ def fold(w, act_absmax, alpha: float, smooth_in=None, stream=None) -> Folded:
     dev = w.device
     f = Folded(torch.empty(K, dtype=torch.float32, device=dev),
                torch.empty(K, dtype=torch.float32, device=dev),
-               torch.empty((N, K), dtype=torch.int8, device=dev),
-               torch.empty(N, dtype=torch.float32, device=dev))
+               torch.empty(packed_bytes(N, K), dtype=torch.int8, device=dev),
+               torch.empty(N, dtype=torch.float32, device=dev), K, N)
     sq_smooth_fold_weights(w, act_absmax, alpha, smooth_in, f.smooth, f.inv_smooth, f.wq,
                            f.w_scale, stream=stream)
     return f
 
 
 def quant(x, inv_smooth, stream=None):
+    """Returns (packed xq, x_scale)."""
     torch = _torch()
     M, K = x.shape
-    xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    xq = torch.empty(packed_bytes(M, K), dtype=torch.int8, device=x.device)
     xs = torch.empty(M, dtype=torch.float32, device=x.device)
     sq_quant_act_per_token(x, inv_smooth, xq, xs, stream=stream)
     return xq, xs
 
 
-def gemm(xq, x_scale, wq, w_scale, out_kind: int = SQ_OUT_F16, stream=None):
+def gemm(xq, x_scale, wq, w_scale, M: int, N: int, K: int, out_kind: int = SQ_OUT_F16,
+         stream=None):
     torch = _torch()
     dt = torch.float16 if out_kind == SQ_OUT_F16 else torch.int32
-    y = torch.empty((xq.shape[0], wq.shape[0]), dtype=dt, device=xq.device)
-    sq_w8a8_gemm(xq, x_scale, wq, w_scale, y, out_kind, stream=stream)
+    y = torch.empty((M, N), dtype=dt, device=xq.device)
+    sq_w8a8_gemm(xq, x_scale, wq, w_scale, y, K, out_kind, stream=stream)
     return y
+
+
+def pack_i8(codes, stream=None):
+    torch = _torch()
+    rows, K = codes.shape
+    dst = torch.empty(packed_bytes(rows, K), dtype=torch.int8, device=codes.device)
+    sq_pack_i8(codes, dst, stream=stream)
+    return dst
+
+
+def unpack_i8(packed, rows: int, K: int, stream=None):
+    torch = _torch()
+    dst = torch.empty((rows, K), dtype=torch.int8, device=packed.device)
+    sq_unpack_i8(packed, dst, stream=stream)
+    return dst
 
 
 def smoothed_linear(x, folded: Folded, stream=None):
     """Serving-time layer: per-token quantization of x, then the W8A8 product."""
     xq, xs = quant(x, folded.inv_smooth, stream=stream)
-    return gemm(xq, xs, folded.wq, folded.w_scale, stream=stream)
+    return gemm(xq, xs, folded.wq, folded.w_scale, x.shape[0], folded.N, folded.K, stream=stream)

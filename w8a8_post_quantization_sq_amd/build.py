@@ -7,6 +7,9 @@ Flags:
                                          to contract today; this keeps it so)
   -Xclang -target-feature -Xclang -packed-fp32-ops
                                          no packed fp32 instructions
+  -mllvm -amdgpu-mfma-vgpr-form=1        matrix-core accumulators in arch VGPRs: the
+                                         product's working set fits the 256 VGPRs
+                                         without accumulator copies in its loop
   -fvisibility=hidden                    only the extern "C" sq_* symbols export
 The compiler's default IEEE-correct float division and sqrt are kept (no
 fast-math).
@@ -22,12 +25,13 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libsq.so")
 
-SOURCES = ["sq_api.cpp", "k_calib.hip", "k_fold.hip", "k_quant.hip", "k_gemm.hip"]
+SOURCES = ["sq_api.cpp", "k_calib.hip", "k_fold.hip", "k_quant.hip", "k_gemm.hip", "k_pack.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-fvisibility=hidden", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

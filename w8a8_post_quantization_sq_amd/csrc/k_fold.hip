@@ -13,8 +13,10 @@
 //   k_smooth_factors  s_j, 1/s_j in float; zeroes w_scale (one lane per channel)
 //   -- the host checks s and 1/s here --
 //   k_fold_colabsmax  amax_n = max_j |float(W[j][n]) * s_j|  (into w_scale, atomics)
-//   k_fold_quant      Wq[n][j] = clamp(rint((W*s) * (127/amax_n)), +-127), written
-//                     transposed (K contiguous) through LDS
+//   k_fold_quant      Wq[n][j] = clamp(rint((W*s) * (127/amax_n)), +-127), transposed
+//                     through LDS and written as packed 16 x 64-byte fragments
+//                     (the operand order of the int8 matrix instruction), with
+//                     the padding rows and windows written as zero
 //   k_fold_finalize   w_scale[n] = amax_n / 127
 #include <math.h>
 
@@ -168,7 +170,9 @@ hipError_t launch_fold_colabsmax(const uint16_t *w, int64_t K, int64_t N, int64_
 // Tile: 64 output channels x 256 input channels.  A work item is 4 consecutive
 // rows j x 8 consecutive columns n (four 16-byte loads); each of its 8 columns
 // yields 4 consecutive codes of one Wq row, packed into a 32-bit LDS store.
-// The tile then leaves as 64 Wq rows of 256 contiguous bytes (16-byte stores).
+// The tile then leaves as 4 x 4 packed fragments of 1 KiB (16 channels x 64
+// input channels each), one 16-byte store per lane.  Out-of-range channels and
+// input channels hold zero codes, so the padding of the packed buffer is zero.
 constexpr int FQ_TN = 64;
 constexpr int FQ_TK = 256;
 constexpr int FQ_LDS = FQ_TK + 16;   // row pitch in bytes; breaks power-of-two strides
@@ -229,17 +233,22 @@ k_fold_quant(const uint16_t *__restrict__ w, int64_t K, int64_t N, int64_t ldw,
             *reinterpret_cast<uint32_t *>(tile + (oct * 8 + c) * FQ_LDS + quad * 4) = packed[c];
     }
     __syncthreads();
-    // 64 rows x 16 chunks of 16 bytes = 1024 chunks, 4 per thread
+    // 16 fragments x 64 lanes of 16 bytes = 1024 chunks, 4 per thread
+    const int64_t KW = (K + 63) >> 6;
+    const int64_t RB = (N + 15) >> 4;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int item = threadIdx.x + it * 256;
-        const int ch = item & 15;
-        const int rn = item >> 4;
-        const int64_t n = n0 + rn;
-        const int64_t j = k0 + ch * 16;
-        if (n < N && j < K)   // K % 16 == 0: a chunk is wholly inside or outside
-            *reinterpret_cast<uint4 *>(wq + n * K + j) =
-                *reinterpret_cast<const uint4 *>(tile + rn * FQ_LDS + ch * 16);
+        const int l = item & 63;
+        const int f = item >> 6;             // fragment: 4 channel blocks x 4 windows
+        const int rbl = f >> 2, kwl = f & 3;
+        const int64_t rb = (n0 >> 4) + rbl;
+        const int64_t kw = (k0 >> 6) + kwl;
+        const int rn = rbl * 16 + (l & 15);
+        const int kk = kwl * 64 + (l >> 4) * 16;
+        if (rb < RB && kw < KW)
+            *reinterpret_cast<uint4 *>(wq + ((rb * KW + kw) << 10) + l * 16) =
+                *reinterpret_cast<const uint4 *>(tile + rn * FQ_LDS + kk);
     }
 }
 

@@ -7,141 +7,359 @@
 // path ("Quantization", learn-kernels.com, para. 2: W8A8 lets the matrix
 // multiply itself use faster low-precision hardware, not only save traffic).
 //
-// Both operands are K-contiguous (xq [M][K], wq [N][K]), which is the natural
-// operand layout of v_mfma_i32_32x32x32_i8: lane l supplies 16 bytes of row
-// (l % 32) of the A block and 16 bytes of column (l % 32) of the B block, the
-// two lane halves covering the two 16-byte halves of the 32-deep k slice.
-// The accumulator of lane l holds column l % 32 and rows
-// 8 * (r / 4) + 4 * (l / 32) + r % 4, r = 0..15.  Integer sums do not depend
-// on the order of the k terms, so any k permutation that A and B share gives
-// the same exact result.
+// Instruction: v_mfma_i32_16x16x64_i8.  Lane l supplies 16 bytes of row
+// (l % 16) of the A block and of column (l % 16) of the B block, quarter l / 16
+// of the 64-deep k window; the accumulator of lane l holds column l % 16,
+// rows 4 * (l / 16) + r, r = 0..3.  Both operands arrive packed in exactly
+// this order (each 16-row x 64-byte fragment is 1 KiB, lane l's 16 bytes at
+// l * 16), so every fragment load is one contiguous 1 KiB run, and the packed
+// padding is zero, so ragged M, N and K need no masks in the main loop.
 //
-// Workgroup: 256 threads = 4 waves in a 2 x 2 grid, output tile BM x BN,
-// k step 64 bytes.  Tiles of both operands pass through LDS, double-buffered
-// (one barrier per k step); the next step's tiles are fetched into registers
-// while the matrix cores work on the current one.  LDS rows are padded from
-// 64 to 80 bytes so the 8 lanes of a 16-byte LDS read phase hit disjoint banks.
+// Operand roles: A = weight fragment (16 output channels n), B = activation
+// fragment (16 tokens m); each lane ends with one token and four consecutive
+// channels: one x_scale, a 16-byte w_scale load and an 8-byte fp16 store per
+// 16 x 16 block.
+//
+// k_gemm_tile (M > 64): output tile 256 tokens x 128 channels per workgroup
+// of 4 waves; wave w owns tokens [64w, 64w + 64) and all 128 channels.
+//   - activation fragments are private to a wave and go straight from global
+//     memory into a register ring, 3 k-steps ahead;
+//   - the 8 KiB weight slice of a k-step is shared by the 4 waves: staged
+//     through registers into a ring of 4 LDS buffers (copied as is, in lane
+//     order, so reads and writes are conflict-free);
+//   - the loop is software-pipelined: while the matrix cores work on step t,
+//     each wave already reads step t+1's weight fragments from LDS (one
+//     fragment after the 4 products that used its register), and stores step
+//     t+2's slice; one barrier per step, and no LDS wait sits in front of the
+//     first product of a step;
+//   - workgroups are numbered so that the 32 tiles one XCD (and its L2) runs
+//     form a 4 x 8 block of the tile grid, which shares activation and weight
+//     rows.
+// k_gemm_skinny (M <= 64, decode): one workgroup per 16 output channels; its
+// 4 waves split the k windows, stream the weight fragments (the dominant HBM
+// traffic) with several 1 KiB loads in flight each, and combine their partial
+// sums through LDS.
 #include "sq_device.h"
 #include "sq.h"
 
 namespace sq {
 
-constexpr int G_BK = 64;
-constexpr int G_LDS_PITCH = G_BK + 16;
+constexpr uint32_t OOB = 0x80000000u;        // an offset past any buffer extent used here
+constexpr uint32_t OOB_BASE = 0x40000000u;   // row base past the buffer (sums stay < 2^31)
+constexpr uint32_t OOB_WIN = 0x40000000u;    // window offset past the buffer
 
-template <int BM, int BN, bool F16OUT>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const int32_t n = bytes > 0x7fffffff ? 0x7fffffff : (int32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+
+// 16-byte buffer load; offsets at or past the buffer's extent read as zero.
+__device__ __forceinline__ v4i bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ v4i mfma(const v4i &a, const v4i &b, const v4i &c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// XCD-aware tile order.  Workgroup b runs on XCD b % 8.  Tile ids are dealt
+// out so that XCD x receives a contiguous run of ids, and ids are laid out in
+// groups of 4 tile rows (m) walked column-major, so a run of 32 ids is a
+// 4 x 8 block of tiles.
+__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int &tm, int &tn) {
+    const int total = tiles_m * tiles_n;
+    int t = b;
+    if ((total & 7) == 0) t = (b & 7) * (total >> 3) + (b >> 3);
+    constexpr int G = 4;
+    const int per_group = G * tiles_n;
+    const int g = t / per_group;
+    const int first_m = g * G;
+    const int gm = (tiles_m - first_m) < G ? (tiles_m - first_m) : G;
+    const int r = t - g * per_group;
+    tm = first_m + r % gm;
+    tn = r / gm;
+}
+
+// Dequantizes and stores the four outputs (m, n .. n + 3) a lane holds.
+template <bool F16OUT>
+__device__ __forceinline__ void store4(void *Y, int64_t ldy, bool vec_ok, int m, int n, int M,
+                                       int N, const v4i &acc, float xsm,
+                                       const float *__restrict__ ws) {
+    if (m >= M || n >= N) return;
+    if (F16OUT) {
+        uint16_t *row = reinterpret_cast<uint16_t *>(Y) + (int64_t)m * ldy;
+        if (vec_ok && n + 3 < N) {
+            const float4 w4 = *reinterpret_cast<const float4 *>(ws + n);
+            const uint32_t lo = (uint32_t)f2h_bits(((float)acc[0] * xsm) * w4.x) |
+                                ((uint32_t)f2h_bits(((float)acc[1] * xsm) * w4.y) << 16);
+            const uint32_t hi = (uint32_t)f2h_bits(((float)acc[2] * xsm) * w4.z) |
+                                ((uint32_t)f2h_bits(((float)acc[3] * xsm) * w4.w) << 16);
+            *reinterpret_cast<uint2 *>(row + n) = make_uint2(lo, hi);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (n + r < N) row[n + r] = f2h_bits(((float)acc[r] * xsm) * ws[n + r]);
+        }
+    } else {
+        int32_t *row = reinterpret_cast<int32_t *>(Y) + (int64_t)m * ldy;
+        if (vec_ok && n + 3 < N) {
+            *reinterpret_cast<v4i *>(row + n) = acc;
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (n + r < N) row[n + r] = acc[r];
+        }
+    }
+}
+
+// ---- large token counts --------------------------------------------------------------
+
+constexpr int T_BM = 256;            // tokens per tile (16 row blocks, 4 per wave)
+constexpr int T_BN = 128;            // channels per tile (8 row blocks)
+constexpr int T_FRAG = 1024;         // bytes per packed fragment
+constexpr int T_SLICE = 8 * T_FRAG;  // weight bytes per k-step
+
+template <bool F16OUT>
 __global__ void __launch_bounds__(256)
-k_gemm_w8a8(const int8_t *__restrict__ A, const int8_t *__restrict__ B,
+k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
             const float *__restrict__ xs, const float *__restrict__ ws, int M, int N, int K,
-            void *__restrict__ Y, int64_t ldy) {
-    constexpr int WM = BM / 2, WN = BN / 2;      // wave tile
-    constexpr int FM = WM / 32, FN = WN / 32;    // 32 x 32 blocks per wave
-    constexpr int A_LD = BM * 4 / 256;           // 16-byte chunks per thread per k step
-    constexpr int B_LD = BN * 4 / 256;
-    static_assert(A_LD >= 1 && B_LD >= 1 && FM >= 1 && FN >= 1, "tile too small");
-    __shared__ __align__(16) int8_t lds[2][(BM + BN) * G_LDS_PITCH];
+            void *__restrict__ Y, int64_t ldy, int tiles_m, int tiles_n, int vec_ok) {
+    // LDS: 4 weight slices during the k loop, then 4 wave tiles of the epilogue
+    constexpr int EPI_PITCH = 128 * 2 + 16;            // bytes per row of 128 fp16, padded
+    constexpr int EPI_WAVE = 64 * EPI_PITCH;            // 64 rows per wave
+    constexpr int LDS_BYTES = (4 * T_SLICE > 4 * EPI_WAVE) ? 4 * T_SLICE : 4 * EPI_WAVE;
+    __shared__ __align__(16) int8_t lds_raw[LDS_BYTES];
+    int8_t (*ldsw)[T_SLICE] = reinterpret_cast<int8_t (*)[T_SLICE]>(lds_raw);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int tiles_n = (N + BN - 1) / BN;
-    const int m0 = (int)(blockIdx.x / tiles_n) * BM;
-    const int n0 = (int)(blockIdx.x % tiles_n) * BN;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * T_BM;
+    const int n0 = tn * T_BN;
+    const int KW = (K + 63) >> 6;
+    const int rbx = (M + 15) >> 4, rbw = (N + 15) >> 4;    // row blocks in the buffers
+    const int nbx = min(16, rbx - (m0 >> 4));               // ... present in this tile
+    const int nbw = min(8, rbw - (n0 >> 4));
+    const __amdgpu_buffer_rsrc_t rx =
+        make_rsrc(X + (int64_t)(m0 >> 4) * KW * T_FRAG, (int64_t)nbx * KW * T_FRAG);
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(W + (int64_t)(n0 >> 4) * KW * T_FRAG, (int64_t)nbw * KW * T_FRAG);
 
-    v16i acc[FM][FN];
+    // activation fragments: this wave's row blocks 4w + i
+    uint32_t xbase[4];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < 4; ++i) {
+        const int b = wave * 4 + i;
+        xbase[i] = b < nbx ? (uint32_t)(b * KW * T_FRAG + lane * 16) : OOB_BASE;
+    }
+    // weight slice: 512 chunks of 16 bytes, 2 per thread; chunk idx = fragment idx / 64, lane idx % 64
+    uint32_t wbase[2];
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+    for (int s = 0; s < 2; ++s) {
+        const int idx = tid + s * 256;
+        const int b = idx >> 6;
+        wbase[s] = b < nbw ? (uint32_t)(b * KW * T_FRAG + (idx & 63) * 16) : OOB_BASE;
+    }
+    // Offset of k window t (uniform): windows past the last one get OOB_WIN, so
+    // every lane's base + offset falls past the buffer and reads zero.  Bases
+    // are < 2^25 or OOB_BASE, offsets < 2^21 or OOB_WIN, so sums never wrap.
+    auto win = [&](int t) -> uint32_t { return t < KW ? (uint32_t)t * T_FRAG : OOB_WIN; };
 
-    v4i ra[A_LD], rb[B_LD];
-    const v4i zero4 = {0, 0, 0, 0};
-    auto gload = [&](int k0) {
+    v4i acc[4][8];
 #pragma unroll
-        for (int i = 0; i < A_LD; ++i) {
-            const int idx = tid + i * 256;
-            const int row = idx >> 2, kk = k0 + (idx & 3) * 16;
-            const int gm = m0 + row;
-            ra[i] = (gm < M && kk < K)
-                        ? *reinterpret_cast<const v4i *>(A + (int64_t)gm * K + kk)
-                        : zero4;
-        }
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < B_LD; ++i) {
-            const int idx = tid + i * 256;
-            const int row = idx >> 2, kk = k0 + (idx & 3) * 16;
-            const int gn = n0 + row;
-            rb[i] = (gn < N && kk < K)
-                        ? *reinterpret_cast<const v4i *>(B + (int64_t)gn * K + kk)
-                        : zero4;
-        }
+        for (int j = 0; j < 8; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+    v4i xr[4][4];    // activation ring: steps t .. t+3
+    v4i wst[2][2];   // weight staging ring: steps t+2, t+3
+    v4i wf[8];       // weight fragments of the current step
+    auto load_x = [&](int slot, int t) {
+        const uint32_t wo = win(t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xr[slot][i] = bload(rx, xbase[i] + wo);
     };
-    auto lstore = [&](int buf) {
+    auto load_w = [&](int slot, int t) {
+        const uint32_t wo = win(t);
 #pragma unroll
-        for (int i = 0; i < A_LD; ++i) {
-            const int idx = tid + i * 256;
-            *reinterpret_cast<v4i *>(&lds[buf][(idx >> 2) * G_LDS_PITCH + (idx & 3) * 16]) = ra[i];
-        }
+        for (int s = 0; s < 2; ++s) wst[slot][s] = bload(rw, wbase[s] + wo);
+    };
+    auto store_w = [&](int slot, int buf) {
 #pragma unroll
-        for (int i = 0; i < B_LD; ++i) {
-            const int idx = tid + i * 256;
-            *reinterpret_cast<v4i *>(&lds[buf][(BM + (idx >> 2)) * G_LDS_PITCH + (idx & 3) * 16]) =
-                rb[i];
-        }
+        for (int s = 0; s < 2; ++s)
+            *reinterpret_cast<v4i *>(&ldsw[buf][(tid + s * 256) * 16]) = wst[slot][s];
     };
 
-    const int nk = (K + G_BK - 1) / G_BK;
-    gload(0);
-    lstore(0);
+    // prologue: weight slices 0 and 1 in LDS, slice 2 staged, activations 0..2 in flight
+#pragma unroll
+    for (int s = 0; s < 3; ++s) load_x(s, s);
+    load_w(0, 0);
+    load_w(1, 1);
+    store_w(0, 0);
+    store_w(1, 1);
+    load_w(0, 2);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * G_BK);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int chunk = ks * 2 + (lane >> 5);
-            v4i af[FM], bf[FN];
+    for (int j = 0; j < 8; ++j) wf[j] = *reinterpret_cast<const v4i *>(&ldsw[0][j * T_FRAG + lane * 16]);
+
+    const int nsteps = (KW + 3) & ~3;
+    for (int t0 = 0; t0 < nsteps; t0 += 4) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const v4i *>(
-                    &lds[cur][(wm * WM + i * 32 + (lane & 31)) * G_LDS_PITCH + chunk * 16]);
+        for (int u = 0; u < 4; ++u) {
+            const int t = t0 + u;
+            // this step's loads go out first and stay first: the weight slice
+            // stored into LDS at the end of the step was issued a whole step
+            // earlier, with this step's six loads behind it, so its wait does
+            // not drain the activation prefetch
+            load_w((u + 1) & 1, t + 3);
+            load_x((u + 3) & 3, t + 3);
+            __builtin_amdgcn_sched_barrier(0);
+            const int nb = (u + 1) & 3;
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                bf[j] = *reinterpret_cast<const v4i *>(
-                    &lds[cur][(BM + wn * WN + j * 32 + (lane & 31)) * G_LDS_PITCH + chunk * 16]);
+            for (int j = 0; j < 8; ++j) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+                for (int i = 0; i < 4; ++i) acc[i][j] = mfma(wf[j], xr[u][i], acc[i][j]);
+                wf[j] = *reinterpret_cast<const v4i *>(&ldsw[nb][j * T_FRAG + lane * 16]);
+            }
+            store_w(u & 1, (u + 2) & 3);
+            __syncthreads();
         }
-        if (kt + 1 < nk) lstore(cur ^ 1);
-        __syncthreads();
     }
 
-    // epilogue: lane holds column (lane % 32) of each 32 x 32 block
+    // epilogue.  Scales first, in one batch of loads.  fp16 output then goes
+    // through LDS (the weight buffers are free now): each wave converts its
+    // 64 x 128 block into a padded LDS tile and writes it back as rows of 256
+    // contiguous bytes, 16 bytes per lane.
+    float xsv[4];
+    float4 wsv[8];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn * WN + j * 32 + (lane & 31);
-        if (col >= N) continue;
-        const float wsc = F16OUT ? ws[col] : 0.0f;
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wave * 64 + i * 16 + (lane & 15);
+        xsv[i] = (F16OUT && m < M) ? xs[m] : 0.0f;
+    }
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
+    for (int j = 0; j < 8; ++j) {
+        const int n = n0 + j * 16 + (lane >> 4) * 4;
+        wsv[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (F16OUT) {
+            if (n + 3 < N) {
+                wsv[j] = make_float4(ws[n], ws[n + 1], ws[n + 2], ws[n + 3]);
+            } else {
+                if (n < N) wsv[j].x = ws[n];
+                if (n + 1 < N) wsv[j].y = ws[n + 1];
+                if (n + 2 < N) wsv[j].z = ws[n + 2];
+            }
+        }
+    }
+    if (F16OUT && (vec_ok & 2)) {
+        constexpr int PITCH = EPI_PITCH;
+        int8_t *tile = lds_raw + wave * EPI_WAVE;     // this wave's 17 KiB
+        __syncthreads();                              // every wave is done with the slices
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                if (row >= M) continue;
-                if (F16OUT) {
-                    const float y = ((float)acc[i][j][r] * xs[row]) * wsc;
-                    reinterpret_cast<uint16_t *>(Y)[(int64_t)row * ldy + col] = f2h_bits(y);
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const v4i &a = acc[i][j];
+                const uint32_t lo = (uint32_t)f2h_bits(((float)a[0] * xsv[i]) * wsv[j].x) |
+                                    ((uint32_t)f2h_bits(((float)a[1] * xsv[i]) * wsv[j].y) << 16);
+                const uint32_t hi = (uint32_t)f2h_bits(((float)a[2] * xsv[i]) * wsv[j].z) |
+                                    ((uint32_t)f2h_bits(((float)a[3] * xsv[i]) * wsv[j].w) << 16);
+                *reinterpret_cast<uint2 *>(tile + (i * 16 + (lane & 15)) * PITCH +
+                                           (j * 16 + (lane >> 4) * 4) * 2) = make_uint2(lo, hi);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0): this wave's LDS writes done
+        // 64 rows x 16 chunks of 16 bytes, 16 per lane; 4 rows per instruction
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const int r = c * 4 + (lane >> 4);
+            const int m = m0 + wave * 64 + r;
+            const int n = n0 + (lane & 15) * 8;
+            const uint4 v = *reinterpret_cast<const uint4 *>(tile + r * PITCH + (lane & 15) * 16);
+            if (m < M) {
+                uint16_t *dst = reinterpret_cast<uint16_t *>(Y) + (int64_t)m * ldy + n;
+                if (n + 7 < N) {
+                    *reinterpret_cast<uint4 *>(dst) = v;
                 } else {
-                    reinterpret_cast<int32_t *>(Y)[(int64_t)row * ldy + col] = acc[i][j][r];
+                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (n + e < N) dst[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
                 }
             }
         }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = m0 + wave * 64 + i * 16 + (lane & 15);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                store4<F16OUT>(Y, ldy, (vec_ok & 1) != 0, m, n0 + j * 16 + (lane >> 4) * 4, M, N,
+                               acc[i][j], xsv[i], ws);
+        }
+    }
+}
+
+// ---- small token counts (decode) ---------------------------------------------------------
+
+constexpr int S_UNROLL = 4;   // k windows in flight per wave
+
+template <int MB, bool F16OUT>
+__global__ void __launch_bounds__(256)
+k_gemm_skinny(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
+              const float *__restrict__ xs, const float *__restrict__ ws, int M, int N, int K,
+              void *__restrict__ Y, int64_t ldy, int vec_ok) {
+    __shared__ __align__(16) v4i part[3][MB][64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int nb = blockIdx.x;                   // 16-channel block
+    const int KW = (K + 63) >> 6;
+    const int rbx = (M + 15) >> 4;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (int64_t)rbx * KW * T_FRAG);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (int64_t)nb * KW * T_FRAG, (int64_t)KW * T_FRAG);
+
+    v4i acc[MB];
+#pragma unroll
+    for (int b = 0; b < MB; ++b) acc[b] = v4i{0, 0, 0, 0};
+    // wave w takes windows w, w + 4, w + 8, ...: the 4 waves stream adjacent KiB
+    for (int t0 = wave; t0 < KW; t0 += 4 * S_UNROLL) {
+        v4i wf[S_UNROLL], xf[S_UNROLL][MB];
+#pragma unroll
+        for (int u = 0; u < S_UNROLL; ++u) {
+            const int t = t0 + 4 * u;
+            const uint32_t off = t < KW ? (uint32_t)(t * T_FRAG + lane * 16) : OOB;
+            wf[u] = bload(rw, off);
+#pragma unroll
+            for (int b = 0; b < MB; ++b)
+                xf[u][b] = bload(rx, (t < KW && b < rbx) ? (uint32_t)((b * KW + t) * T_FRAG + lane * 16) : OOB);
+        }
+#pragma unroll
+        for (int u = 0; u < S_UNROLL; ++u)
+#pragma unroll
+            for (int b = 0; b < MB; ++b) acc[b] = mfma(wf[u], xf[u][b], acc[b]);
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int b = 0; b < MB; ++b) part[wave - 1][b][lane] = acc[b];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+#pragma unroll
+        for (int w = 0; w < 3; ++w) {
+            const v4i p = part[w][b][lane];
+            acc[b][0] += p[0];
+            acc[b][1] += p[1];
+            acc[b][2] += p[2];
+            acc[b][3] += p[3];
+        }
+        const int m = b * 16 + (lane & 15);
+        const float xsm = (F16OUT && m < M) ? xs[m] : 0.0f;
+        store4<F16OUT>(Y, ldy, (vec_ok & 1) != 0, m, nb * 16 + (lane >> 4) * 4, M, N, acc[b], xsm, ws);
     }
 }
 
@@ -149,14 +367,38 @@ hipError_t launch_gemm(const int8_t *xq, const float *x_scale, const int8_t *wq,
                        const float *w_scale, int64_t M, int64_t N, int64_t K, void *y,
                        int64_t ldy, int out_kind, hipStream_t st) {
     if (M <= 0 || N <= 0) return hipSuccess;
-    constexpr int BM = 128, BN = 128;
-    const dim3 grid((unsigned)(((N + BN - 1) / BN) * ((M + BM - 1) / BM)));
-    if (out_kind == SQ_OUT_F16)
-        k_gemm_w8a8<BM, BN, true><<<grid, dim3(256), 0, st>>>(xq, wq, x_scale, w_scale, (int)M,
-                                                               (int)N, (int)K, y, ldy);
-    else
-        k_gemm_w8a8<BM, BN, false><<<grid, dim3(256), 0, st>>>(xq, wq, x_scale, w_scale, (int)M,
-                                                                (int)N, (int)K, y, ldy);
+    const bool f16 = out_kind == SQ_OUT_F16;
+    // bit 0: stores of 4 elements (8-byte fp16 / 16-byte int32) line up with
+    // every row; bit 1: 16-byte stores of 8 fp16 do
+    const int elem = f16 ? 2 : 4;
+    const int vec_ok = (((ldy % 4) == 0 && ((uintptr_t)y % (uintptr_t)(4 * elem)) == 0 &&
+                         (!f16 || ((uintptr_t)w_scale % 16) == 0)) ? 1 : 0) |
+                       ((f16 && (ldy % 8) == 0 && ((uintptr_t)y % 16) == 0) ? 2 : 0);
+    const int m = (int)M, n = (int)N, k = (int)K;
+    if (M > 64) {
+        const int tiles_m = (m + T_BM - 1) / T_BM;
+        const int tiles_n = (n + T_BN - 1) / T_BN;
+        const dim3 grid((unsigned)(tiles_m * tiles_n));
+        if (f16)
+            k_gemm_tile<true><<<grid, dim3(256), 0, st>>>(xq, wq, x_scale, w_scale, m, n, k, y, ldy,
+                                                          tiles_m, tiles_n, vec_ok);
+        else
+            k_gemm_tile<false><<<grid, dim3(256), 0, st>>>(xq, wq, x_scale, w_scale, m, n, k, y, ldy,
+                                                           tiles_m, tiles_n, vec_ok);
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)((n + 15) / 16));
+#define SQ_SK(MB)                                                                                  \
+    (f16 ? (k_gemm_skinny<MB, true><<<grid, dim3(256), 0, st>>>(xq, wq, x_scale, w_scale, m, n, k, \
+                                                                y, ldy, vec_ok), 0)                \
+         : (k_gemm_skinny<MB, false><<<grid, dim3(256), 0, st>>>(xq, wq, x_scale, w_scale, m, n,   \
+                                                                 k, y, ldy, vec_ok), 0))
+    const int64_t mb = (M + 15) / 16;
+    if (mb == 1) SQ_SK(1);
+    else if (mb == 2) SQ_SK(2);
+    else if (mb == 3) SQ_SK(3);
+    else SQ_SK(4);
+#undef SQ_SK
     return hipGetLastError();
 }
 

@@ -17,6 +17,11 @@
 // (wave shuffles, then 4 waves through LDS) and the quantization, so X is read
 // from HBM exactly once.  Rows longer than 256 * 8 * 16 channels take a
 // streaming variant that reads the row twice.
+//
+// The codes are written in the packed operand order of the int8 matrix
+// instruction (16-row x 64-byte fragments of 1 KiB): 8 consecutive codes of a
+// row are 8 contiguous bytes there.  The grid covers the padded rows and
+// windows too, writing their codes as zero.
 #include "sq_device.h"
 
 namespace sq {
@@ -39,6 +44,11 @@ __device__ __forceinline__ void load8(const uint16_t *__restrict__ x, const floa
         const uint32_t b = __float_as_uint(v[i]) & 0x7fffffffu;
         amax = amax > b ? amax : b;
     }
+}
+
+// Byte offset of codes (m, k .. k + 7), k % 8 == 0, in the packed layout.
+__device__ __forceinline__ int64_t packed_off(int64_t m, int64_t k, int64_t KW) {
+    return (((m >> 4) * KW + (k >> 6)) << 10) + (((k >> 4) & 3) << 8) + ((m & 15) << 4) + (k & 15);
 }
 
 __device__ __forceinline__ uint2 quant8(const float v[8], float r, bool zero) {
@@ -85,63 +95,76 @@ __device__ __forceinline__ void row_params(uint32_t abits, float &scale, float &
     }
 }
 
+// Block m < M quantizes token m; blocks M .. 16 * ceil(M / 16) - 1 write the
+// zero codes of the padding rows.  Chunks at k >= K are padding too.
 template <int CPT>
 __global__ void __launch_bounds__(256)
-k_quant_act(const uint16_t *__restrict__ x, int64_t K, int64_t ldx,
+k_quant_act(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
             const float *__restrict__ inv_s, int8_t *__restrict__ xq,
             float *__restrict__ x_scale) {
     const int64_t m = blockIdx.x;
     const int64_t nch = K >> 3;
-    const uint16_t *row = x + m * ldx;
+    const int64_t KW = (K + 63) >> 6;
+    const int64_t nch_pad = KW << 3;
+    const bool real = m < M;
+    const uint16_t *row = x + (real ? m : 0) * ldx;
     float v[CPT][8];
     uint32_t amax = 0;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
         const int64_t ch = threadIdx.x + c * 256;
-        if (ch < nch) load8(row, inv_s, ch * 8, v[c], amax);
+        if (real && ch < nch) load8(row, inv_s, ch * 8, v[c], amax);
     }
     float scale, r;
     bool zero;
     row_params(block_max_256(amax), scale, r, zero);
-    if (threadIdx.x == 0) x_scale[m] = scale;
-    int8_t *qrow = xq + m * K;
+    if (real && threadIdx.x == 0) x_scale[m] = scale;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
         const int64_t ch = threadIdx.x + c * 256;
-        if (ch < nch) *reinterpret_cast<uint2 *>(qrow + ch * 8) = quant8(v[c], r, zero);
+        if (ch < nch_pad)
+            *reinterpret_cast<uint2 *>(xq + packed_off(m, ch * 8, KW)) =
+                (real && ch < nch) ? quant8(v[c], r, zero) : make_uint2(0u, 0u);
     }
 }
 
 // Long rows: first pass for the maximum, second pass (from cache) for the codes.
 __global__ void __launch_bounds__(256)
-k_quant_act_stream(const uint16_t *__restrict__ x, int64_t K, int64_t ldx,
+k_quant_act_stream(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
                    const float *__restrict__ inv_s, int8_t *__restrict__ xq,
                    float *__restrict__ x_scale) {
     const int64_t m = blockIdx.x;
     const int64_t nch = K >> 3;
-    const uint16_t *row = x + m * ldx;
+    const int64_t KW = (K + 63) >> 6;
+    const int64_t nch_pad = KW << 3;
+    const bool real = m < M;
+    const uint16_t *row = x + (real ? m : 0) * ldx;
     uint32_t amax = 0;
     float v[8];
-    for (int64_t ch = threadIdx.x; ch < nch; ch += 256) load8(row, inv_s, ch * 8, v, amax);
+    if (real)
+        for (int64_t ch = threadIdx.x; ch < nch; ch += 256) load8(row, inv_s, ch * 8, v, amax);
     float scale, r;
     bool zero;
     row_params(block_max_256(amax), scale, r, zero);
-    if (threadIdx.x == 0) x_scale[m] = scale;
-    int8_t *qrow = xq + m * K;
-    for (int64_t ch = threadIdx.x; ch < nch; ch += 256) {
-        uint32_t dummy = 0;
-        load8(row, inv_s, ch * 8, v, dummy);
-        *reinterpret_cast<uint2 *>(qrow + ch * 8) = quant8(v, r, zero);
+    if (real && threadIdx.x == 0) x_scale[m] = scale;
+    for (int64_t ch = threadIdx.x; ch < nch_pad; ch += 256) {
+        uint2 q = make_uint2(0u, 0u);
+        if (real && ch < nch) {
+            uint32_t dummy = 0;
+            load8(row, inv_s, ch * 8, v, dummy);
+            q = quant8(v, r, zero);
+        }
+        *reinterpret_cast<uint2 *>(xq + packed_off(m, ch * 8, KW)) = q;
     }
 }
 
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                             const float *inv_s, int8_t *xq, float *x_scale, hipStream_t st) {
     if (M <= 0) return hipSuccess;
-    const int64_t nch = K / 8;
-    const int64_t cpt = (nch + 255) / 256;
-    const dim3 grid((unsigned)M), block(256);
-#define SQ_Q(C) k_quant_act<C><<<grid, block, 0, st>>>(x, K, ldx, inv_s, xq, x_scale)
+    const int64_t nch_pad = ((K + 63) / 64) * 8;
+    const int64_t cpt = (nch_pad + 255) / 256;
+    const dim3 grid((unsigned)((M + 15) / 16 * 16)), block(256);
+#define SQ_Q(C) k_quant_act<C><<<grid, block, 0, st>>>(x, M, K, ldx, inv_s, xq, x_scale)
     if (cpt <= 1) SQ_Q(1);
     else if (cpt <= 2) SQ_Q(2);
     else if (cpt <= 3) SQ_Q(3);
@@ -150,7 +173,7 @@ hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx
     else if (cpt <= 8) SQ_Q(8);
     else if (cpt <= 12) SQ_Q(12);
     else if (cpt <= 16) SQ_Q(16);
-    else k_quant_act_stream<<<grid, block, 0, st>>>(x, K, ldx, inv_s, xq, x_scale);
+    else k_quant_act_stream<<<grid, block, 0, st>>>(x, M, K, ldx, inv_s, xq, x_scale);
 #undef SQ_Q
     return hipGetLastError();
 }

@@ -42,7 +42,12 @@ SQ_API const char *sq_status_str(int status) {
     }
 }
 
-SQ_API int sq_version(void) { return 10000; }
+SQ_API int sq_version(void) { return 10100; }
+
+SQ_API int64_t sq_packed_bytes(int64_t rows, int64_t K) {
+    if (rows < 0 || rows >= kMaxDim || !k_ok(K)) return 0;
+    return ((rows + 15) / 16) * ((K + 63) / 64) * 1024;
+}
 
 SQ_API sq_status sq_calibrate_absmax(const void *x_cal_f16, int64_t T, int64_t K, int64_t ldx,
                                      float *act_absmax, int accumulate, void *stream) {
@@ -131,8 +136,8 @@ SQ_API sq_status sq_w8a8_gemm(const int8_t *xq, const float *x_scale, const int8
     if (work && out_kind == SQ_OUT_F16 && (!x_scale || !w_scale)) return SQ_ERR_NULL;
     if (M < 0 || N < 0 || M >= kMaxDim || N >= kMaxDim || !k_ok(K)) return SQ_ERR_SHAPE;
     if (work && ldy < N) return SQ_ERR_SHAPE;
-    // one workgroup per 128 x 128 output tile: the tile count must fit a 1-D grid
-    if (work && ((M + 127) / 128) * ((N + 127) / 128) >= kMaxDim) return SQ_ERR_SHAPE;
+    // one workgroup per 256 x 128 output tile: the tile count must fit a 1-D grid
+    if (work && ((M + 255) / 256) * ((N + 127) / 128) >= kMaxDim) return SQ_ERR_SHAPE;
     if (work) {
         if (!aligned16(xq) || !aligned16(wq)) return SQ_ERR_ALIGN;
         if (out_kind == SQ_OUT_F16 && (!aligned16(x_scale) || !aligned16(w_scale))) return SQ_ERR_ALIGN;
@@ -142,4 +147,22 @@ SQ_API sq_status sq_w8a8_gemm(const int8_t *xq, const float *x_scale, const int8
     if (!work) return SQ_OK;
     return hip_status(sq::launch_gemm(xq, x_scale, wq, w_scale, M, N, K, y, ldy, out_kind,
                                       as_stream(stream)));
+}
+
+SQ_API sq_status sq_pack_i8(const int8_t *src, int64_t rows, int64_t K, int64_t ld, int8_t *dst,
+                            void *stream) {
+    if (rows > 0 && (!src || !dst)) return SQ_ERR_NULL;
+    if (rows < 0 || rows >= kMaxDim || !k_ok(K) || ld < K) return SQ_ERR_SHAPE;
+    if (rows > 0 && (!aligned16(src) || !aligned16(dst) || (ld % 16) != 0)) return SQ_ERR_ALIGN;
+    if (rows == 0) return SQ_OK;
+    return hip_status(sq::launch_pack_i8(src, rows, K, ld, dst, as_stream(stream)));
+}
+
+SQ_API sq_status sq_unpack_i8(const int8_t *src, int64_t rows, int64_t K, int8_t *dst, int64_t ld,
+                              void *stream) {
+    if (rows > 0 && (!src || !dst)) return SQ_ERR_NULL;
+    if (rows < 0 || rows >= kMaxDim || !k_ok(K) || ld < K) return SQ_ERR_SHAPE;
+    if (rows > 0 && (!aligned16(src) || !aligned16(dst) || (ld % 16) != 0)) return SQ_ERR_ALIGN;
+    if (rows == 0) return SQ_OK;
+    return hip_status(sq::launch_unpack_i8(src, rows, K, dst, ld, as_stream(stream)));
 }

@@ -31,6 +31,12 @@ hipError_t launch_fold_finalize(float *w_scale, int64_t N, hipStream_t st);
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                             const float *inv_s, int8_t *xq, float *x_scale, hipStream_t st);
 
+hipError_t launch_pack_i8(const int8_t *src, int64_t rows, int64_t K, int64_t ld, int8_t *dst,
+                          hipStream_t st);
+
+hipError_t launch_unpack_i8(const int8_t *src, int64_t rows, int64_t K, int8_t *dst, int64_t ld,
+                            hipStream_t st);
+
 hipError_t launch_gemm(const int8_t *xq, const float *x_scale, const int8_t *wq,
                        const float *w_scale, int64_t M, int64_t N, int64_t K, void *y,
                        int64_t ldy, int out_kind, hipStream_t st);
