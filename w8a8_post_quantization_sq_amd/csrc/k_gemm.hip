@@ -222,9 +222,25 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[i][j] = mfma(wf[j], xr[u][i], acc[i][j]);
                 wf[j] = *reinterpret_cast<const v4i *>(&ldsw[nb][j * T_FRAG + lane * 16]);
+                if (j == 3) {
+                    // the staged slice t+2 goes to LDS mid-step, pinned between
+                    // the reads of fragments 3 and 4 (it was loaded a step and a
+                    // half ago)
+                    __builtin_amdgcn_sched_barrier(0);
+                    store_w(u & 1, (u + 2) & 3);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
-            store_w(u & 1, (u + 2) & 3);
-            __syncthreads();
+            // Before the barrier only the two stores must be complete: LDS
+            // operations of a wave complete in order, so at most the 4 later
+            // fragment reads may still be in flight (they read slice t+1,
+            // which nobody overwrites before two more barriers).
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(0xc07f | (4 << 8));   // lgkmcnt(4)
+            __builtin_amdgcn_s_barrier();
+            // keep each step's products inside the step: hoisting them above
+            // the barrier would put them right behind the LDS reads they use
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
