@@ -39,8 +39,14 @@ def log(msg):
 
 
 def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a source file's code: comments and whitespace do not count, so
+    the recorded counters stay valid across comment-only edits."""
+    import re
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"\s+", "", text)
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def read_traffic(workload):
@@ -103,6 +109,9 @@ def main():
     ap.add_argument("--alpha", type=float, default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle layer work in the CPU baseline (0: skip)")
+    ap.add_argument("--copy-kernel", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run 3 plain device copies of MIB MiB "
+                         "(the reference for calibrating rocprofv3's FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -119,6 +128,15 @@ def main():
         sys.exit(1)
     L = sq.lib()     # raises if the HIP library is not built: there is no fallback
     dev = torch.device("cuda:0")
+    if args.copy_kernel > 0:
+        n = args.copy_kernel << 20
+        a = torch.ones(n // 4, dtype=torch.int32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_kernel_bytes": n, "launches": 3}), flush=True)
+        return
     wl = workloads.WORKLOADS[args.workload]
     if args.alpha is not None:
         wl = wl.with_alpha(args.alpha)

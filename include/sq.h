@@ -9,8 +9,8 @@
  * map", para. 1).  The factors come from calibration statistics, the weights
  * are folded and quantized offline, and at serving time the activations are
  * quantized per token and multiplied on int8 matrix cores (SmoothQuant
- * glossary entry: W8A8, calibration-based; "Quantization", learn-kernels.com,
- * para. 2: both operands int8, transform applied offline before serving).
+ * glossary entry: W8A8, factors from calibration statistics; "Quantization",
+ * learn-kernels.com, para. 2: both operands int8, transform applied offline).
  *
  * Conventions for every call:
  *   - All array arguments are caller-owned DEVICE pointers on the current HIP

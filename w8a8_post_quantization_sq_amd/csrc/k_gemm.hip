@@ -3,9 +3,9 @@
 //   acc[m][n] = sum_j xq[m][j] * wq[n][j]        (exact int32)
 //   y[m][n]   = fp16_rne((float(acc) * x_scale[m]) * w_scale[n])
 //
-// Both operands are int8, so the product runs on the low-precision matrix
-// path ("Quantization", learn-kernels.com, para. 2: W8A8 lets the matrix
-// multiply itself use faster low-precision hardware, not only save traffic).
+// Both operands are int8, so the product runs on the int8 matrix cores
+// ("Quantization", learn-kernels.com, para. 2: with both operands quantized
+// the product itself runs at low precision, beyond the saving in bytes).
 //
 // Instruction: v_mfma_i32_16x16x64_i8.  Lane l supplies 16 bytes of row
 // (l % 16) of the A block and of column (l % 16) of the B block, quarter l / 16

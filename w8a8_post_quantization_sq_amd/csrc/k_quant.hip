@@ -11,17 +11,11 @@
 // no fast-math), the products single float multiplies, so the codes are the
 // ones the plain definition gives.
 //
-// One 256-thread workgroup per token row.  Each lane owns CPT chunks of 8
-// channels (a 16-byte fp16 load, two 16-byte loads of inv_s, an 8-byte int8
-// store); the scaled row stays in registers between the absmax reduction
-// (wave shuffles, then 4 waves through LDS) and the quantization, so X is read
-// from HBM exactly once.  Rows longer than 256 * 8 * 16 channels take a
-// streaming variant that reads the row twice.
-//
 // The codes are written in the packed operand order of the int8 matrix
-// instruction (16-row x 64-byte fragments of 1 KiB): 8 consecutive codes of a
-// row are 8 contiguous bytes there.  The grid covers the padded rows and
-// windows too, writing their codes as zero.
+// instruction (16-row x 64-byte fragments of 1 KiB, lane order quarter-major,
+// row-minor), so 16 consecutive codes of a row are one 16-byte piece and the
+// pieces of 16 consecutive rows for one quarter of a 64-code window are
+// contiguous.  X is read from HBM once (the second pass hits L2).
 #include "sq_device.h"
 
 namespace sq {
@@ -46,11 +40,6 @@ __device__ __forceinline__ void load8(const uint16_t *__restrict__ x, const floa
     }
 }
 
-// Byte offset of codes (m, k .. k + 7), k % 8 == 0, in the packed layout.
-__device__ __forceinline__ int64_t packed_off(int64_t m, int64_t k, int64_t KW) {
-    return (((m >> 4) * KW + (k >> 6)) << 10) + (((k >> 4) & 3) << 8) + ((m & 15) << 4) + (k & 15);
-}
-
 __device__ __forceinline__ uint2 quant8(const float v[8], float r, bool zero) {
     uint32_t lo = 0, hi = 0;
 #pragma unroll
@@ -62,19 +51,6 @@ __device__ __forceinline__ uint2 quant8(const float v[8], float r, bool zero) {
         else hi |= b << (8 * (i - 4));
     }
     return make_uint2(lo, hi);
-}
-
-// Reduces the per-lane magnitude maxima of one row to the whole workgroup.
-__device__ __forceinline__ uint32_t block_max_256(uint32_t v) {
-    __shared__ uint32_t part[4];
-    v = wave_max_u32(v);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
-    __syncthreads();
-    uint32_t a = part[0];
-    a = a > part[1] ? a : part[1];
-    a = a > part[2] ? a : part[2];
-    a = a > part[3] ? a : part[3];
-    return a;
 }
 
 // Turns the row maximum into (scale, multiplier, all-zero-codes flag).
@@ -95,86 +71,167 @@ __device__ __forceinline__ void row_params(uint32_t abits, float &scale, float &
     }
 }
 
-// Block m < M quantizes token m; blocks M .. 16 * ceil(M / 16) - 1 write the
-// zero codes of the padding rows.  Chunks at k >= K are padding too.
-template <int CPT>
-__global__ void __launch_bounds__(256)
-k_quant_act(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
-            const float *__restrict__ inv_s, int8_t *__restrict__ xq,
-            float *__restrict__ x_scale) {
-    const int64_t m = blockIdx.x;
-    const int64_t nch = K >> 3;
+// Row-group kernel: a workgroup of 8 waves owns 8 consecutive token rows
+// (half a packed row block).
+//   pass 1: wave w streams row m0 + w once from HBM (16-byte loads) and
+//           reduces max |x * inv_s| with wave shuffles; lane 0 stores the
+//           scale and keeps (multiplier, zero-row flag) in LDS;
+//   pass 2: the rows are now in L2; lane p of the group makes one 16-code piece
+//           (row p % 8, quarter (p / 8) % 4, window p / 32), so consecutive
+//           lanes write consecutive 16-byte pieces of a fragment quarter: a
+//           wave stores 8 contiguous runs of 128 bytes.
+// Rows past M and chunks past K are padding and get zero codes.
+constexpr int QR = 8;   // rows per workgroup
+
+__global__ void __launch_bounds__(512)
+k_quant_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
+             const float *__restrict__ inv_s, int8_t *__restrict__ xq,
+             float *__restrict__ x_scale) {
+    __shared__ float s_r[QR];
+    __shared__ int s_zero[QR];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t m0 = (int64_t)blockIdx.x * QR;
     const int64_t KW = (K + 63) >> 6;
-    const int64_t nch_pad = KW << 3;
-    const bool real = m < M;
-    const uint16_t *row = x + (real ? m : 0) * ldx;
-    float v[CPT][8];
-    uint32_t amax = 0;
+    {
+        const int64_t m = m0 + wave;
+        uint32_t amax = 0;
+        if (m < M) {
+            const uint16_t *row = x + m * ldx;
+            // 4 chunks per lane in flight at a time (the loop is latency-bound otherwise)
+            for (int64_t c0 = (int64_t)lane * 8; c0 < K; c0 += 4 * 512) {
+                float v[4][8];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-        const int64_t ch = threadIdx.x + c * 256;
-        if (real && ch < nch) load8(row, inv_s, ch * 8, v[c], amax);
+                for (int u = 0; u < 4; ++u)
+                    if (c0 + u * 512 < K) load8(row, inv_s, c0 + u * 512, v[u], amax);
+            }
+        }
+        amax = wave_max_u32(amax);
+        float scale, r;
+        bool zero;
+        row_params(amax, scale, r, zero);
+        if (lane == 0) {
+            if (m < M) x_scale[m] = scale;
+            s_r[wave] = r;
+            s_zero[wave] = (m < M && !zero) ? 0 : 1;
+        }
     }
-    float scale, r;
-    bool zero;
-    row_params(block_max_256(amax), scale, r, zero);
-    if (real && threadIdx.x == 0) x_scale[m] = scale;
+    __syncthreads();
+    const int64_t rb = m0 >> 4;                 // packed row block
+    const int half = (int)(m0 & 15);            // 0 or 8: which half of it
+    const int64_t pieces = (int64_t)QR * 4 * KW;
+    int8_t *base = xq + ((rb * KW) << 10);
+    // a lane's row is fixed (512 is a multiple of 8), so its multiplier is too
+    const int r = threadIdx.x & 7;
+    const float rr = s_r[r];
+    const bool skip = s_zero[r] != 0;
+    const uint16_t *row = x + (m0 + r) * ldx;
+    for (int64_t p0 = threadIdx.x; p0 < pieces; p0 += 4 * 512) {
+        float v[4][16];
+        uint32_t dummy = 0;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-        const int64_t ch = threadIdx.x + c * 256;
-        if (ch < nch_pad)
-            *reinterpret_cast<uint2 *>(xq + packed_off(m, ch * 8, KW)) =
-                (real && ch < nch) ? quant8(v[c], r, zero) : make_uint2(0u, 0u);
+        for (int u = 0; u < 4; ++u) {   // all loads of 4 pieces first
+            const int64_t p = p0 + u * 512;
+            const int64_t k = (p >> 5) * 64 + ((p >> 3) & 3) * 16;
+            if (!skip && p < pieces && k < K) {
+                load8(row, inv_s, k, &v[u][0], dummy);
+                load8(row, inv_s, k + 8, &v[u][8], dummy);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t p = p0 + u * 512;
+            if (p >= pieces) break;
+            const int q = (int)((p >> 3) & 3);
+            const int64_t kw = p >> 5;
+            const int64_t k = kw * 64 + q * 16;
+            uint4 out = make_uint4(0u, 0u, 0u, 0u);
+            if (!skip && k < K) {
+                const uint2 a = quant8(&v[u][0], rr, false);
+                const uint2 b = quant8(&v[u][8], rr, false);
+                out = make_uint4(a.x, a.y, b.x, b.y);
+            }
+            // piece (window kw, quarter q, row half + r) of the packed row block
+            *reinterpret_cast<uint4 *>(base + ((kw * 64 + q * 16 + half + r) << 4)) = out;
+        }
     }
 }
 
-// Long rows: first pass for the maximum, second pass (from cache) for the codes.
-__global__ void __launch_bounds__(256)
-k_quant_act_stream(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
-                   const float *__restrict__ inv_s, int8_t *__restrict__ xq,
-                   float *__restrict__ x_scale) {
-    const int64_t m = blockIdx.x;
-    const int64_t nch = K >> 3;
+// Register-resident variant for K <= 8192: 1024 threads, 8 rows, 2 waves per
+// row.  Every lane loads all its chunks of its row at once (the only HBM read
+// of X), keeps x * inv_s in registers through the row reduction (wave
+// shuffles, then the 2 waves of a row through LDS), quantizes, and writes its
+// codes into an LDS copy of the 8 rows; the group then leaves LDS as packed
+// 16-byte pieces, consecutive lanes on consecutive rows (128-byte runs).
+template <int CPL>
+__global__ void __launch_bounds__(1024)
+k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
+                 const float *__restrict__ inv_s, int8_t *__restrict__ xq,
+                 float *__restrict__ x_scale) {
+    extern __shared__ __align__(16) int8_t codes[];     // [8][KW * 64]
+    __shared__ uint32_t s_max[16];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;                   // 0..15
+    const int r = wave >> 1;                             // row of the group
+    const int h = wave & 1;                              // which half of the row's chunks
+    const int64_t m0 = (int64_t)blockIdx.x * QR;
+    const int64_t m = m0 + r;
     const int64_t KW = (K + 63) >> 6;
-    const int64_t nch_pad = KW << 3;
+    const int64_t pitch = KW * 64;
     const bool real = m < M;
     const uint16_t *row = x + (real ? m : 0) * ldx;
+    float v[CPL][8];
     uint32_t amax = 0;
-    float v[8];
-    if (real)
-        for (int64_t ch = threadIdx.x; ch < nch; ch += 256) load8(row, inv_s, ch * 8, v, amax);
-    float scale, r;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int64_t k = ((int64_t)(c * 2 + h) * 64 + lane) * 8;
+        if (real && k < K) load8(row, inv_s, k, v[c], amax);
+    }
+    amax = wave_max_u32(amax);
+    if (lane == 0) s_max[wave] = amax;
+    __syncthreads();
+    const uint32_t a0 = s_max[2 * r], a1 = s_max[2 * r + 1];
+    float scale, rr;
     bool zero;
-    row_params(block_max_256(amax), scale, r, zero);
-    if (real && threadIdx.x == 0) x_scale[m] = scale;
-    for (int64_t ch = threadIdx.x; ch < nch_pad; ch += 256) {
-        uint2 q = make_uint2(0u, 0u);
-        if (real && ch < nch) {
-            uint32_t dummy = 0;
-            load8(row, inv_s, ch * 8, v, dummy);
-            q = quant8(v, r, zero);
-        }
-        *reinterpret_cast<uint2 *>(xq + packed_off(m, ch * 8, KW)) = q;
+    row_params(a0 > a1 ? a0 : a1, scale, rr, zero);
+    if (real && h == 0 && lane == 0) x_scale[m] = scale;
+    zero = zero || !real;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int64_t k = ((int64_t)(c * 2 + h) * 64 + lane) * 8;
+        if (k < pitch)   // codes past K (padding) are zero
+            *reinterpret_cast<uint2 *>(codes + r * pitch + k) =
+                (k < K) ? quant8(v[c], rr, zero) : make_uint2(0u, 0u);
+    }
+    __syncthreads();
+    const int64_t rb = m0 >> 4;
+    const int half = (int)(m0 & 15);
+    int8_t *base = xq + ((rb * KW) << 10);
+    const int64_t pieces = (int64_t)QR * 4 * KW;
+    for (int64_t p = threadIdx.x; p < pieces; p += 1024) {
+        const int pr = (int)(p & 7);
+        const int q = (int)((p >> 3) & 3);
+        const int64_t kw = p >> 5;
+        const uint4 val = *reinterpret_cast<const uint4 *>(codes + pr * pitch + kw * 64 + q * 16);
+        *reinterpret_cast<uint4 *>(base + ((kw * 64 + q * 16 + half + pr) << 4)) = val;
     }
 }
 
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                             const float *inv_s, int8_t *xq, float *x_scale, hipStream_t st) {
     if (M <= 0) return hipSuccess;
-    const int64_t nch_pad = ((K + 63) / 64) * 8;
-    const int64_t cpt = (nch_pad + 255) / 256;
-    const dim3 grid((unsigned)((M + 15) / 16 * 16)), block(256);
-#define SQ_Q(C) k_quant_act<C><<<grid, block, 0, st>>>(x, M, K, ldx, inv_s, xq, x_scale)
-    if (cpt <= 1) SQ_Q(1);
-    else if (cpt <= 2) SQ_Q(2);
-    else if (cpt <= 3) SQ_Q(3);
-    else if (cpt <= 4) SQ_Q(4);
-    else if (cpt <= 6) SQ_Q(6);
-    else if (cpt <= 8) SQ_Q(8);
-    else if (cpt <= 12) SQ_Q(12);
-    else if (cpt <= 16) SQ_Q(16);
-    else k_quant_act_stream<<<grid, block, 0, st>>>(x, M, K, ldx, inv_s, xq, x_scale);
-#undef SQ_Q
+    // every row of the padded row blocks, 8 rows per workgroup
+    const int64_t groups = (M + 15) / 16 * 2;
+    const int64_t cpl = (K + 1023) / 1024;        // chunks of 8 per lane, 2 waves per row
+    const size_t lds = (size_t)QR * ((K + 63) / 64) * 64;
+    const dim3 g((unsigned)groups);
+#define SQ_QR(C) k_quant_rows_reg<C><<<g, dim3(1024), lds, st>>>(x, M, K, ldx, inv_s, xq, x_scale)
+    if (cpl <= 1) SQ_QR(1);
+    else if (cpl <= 2) SQ_QR(2);
+    else if (cpl <= 4) SQ_QR(4);
+    else if (cpl <= 8) SQ_QR(8);     // up to 8192 channels: 100 VGPRs, 64 KiB LDS
+    else k_quant_rows<<<g, dim3(512), 0, st>>>(x, M, K, ldx, inv_s, xq, x_scale);
+#undef SQ_QR
     return hipGetLastError();
 }
 

@@ -93,18 +93,18 @@ SQ_API sq_status sq_smooth_fold_weights(const void *w_f16, int64_t K, int64_t N,
                                   w_scale, N, st);
     if (e != hipSuccess) return SQ_ERR_HIP;
 
-    // The one host step: look at s and 1/s before anything is written to wq.
-    std::vector<float> hs((size_t)K), hi((size_t)K);
+    // The one host step: look at s before anything is written to wq.  1/s is
+    // the IEEE float quotient on both sides, so the host recomputes it for
+    // the range check instead of copying it back.
+    std::vector<float> hs((size_t)K);
     e = hipMemcpyAsync(hs.data(), smooth_out, (size_t)K * sizeof(float), hipMemcpyDeviceToHost, st);
-    if (e == hipSuccess)
-        e = hipMemcpyAsync(hi.data(), inv_smooth_out, (size_t)K * sizeof(float),
-                           hipMemcpyDeviceToHost, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return SQ_ERR_HIP;
     bool nonfinite = false, range = false;
     for (int64_t j = 0; j < K; ++j) {
-        if (isnan(hs[j])) nonfinite = true;
-        else if (!isnormal(hs[j]) || !isnormal(hi[j]) || hs[j] < 0.0f) range = true;
+        const float sj = hs[j];
+        if (isnan(sj)) nonfinite = true;
+        else if (!isnormal(sj) || !isnormal(1.0f / sj) || sj < 0.0f) range = true;
     }
     if (nonfinite) return SQ_ERR_NONFINITE;
     if (range) return SQ_ERR_RANGE;
