@@ -37,8 +37,8 @@
 //     rows.
 // k_gemm_skinny (M <= 64, decode): one workgroup per 16 output channels; its
 // 4 waves split the k windows, stream the weight fragments (the dominant HBM
-// traffic) with several 1 KiB loads in flight each, and combine their partial
-// sums through LDS.
+// traffic) with 8 1 KiB loads in flight each (non-temporal for up to 32
+// tokens), and combine their partial sums through LDS.
 #include "sq_device.h"
 #include "sq.h"
 
@@ -320,7 +320,7 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
 
 // ---- small token counts (decode) ---------------------------------------------------------
 
-constexpr int S_UNROLL = 4;   // k windows in flight per wave
+constexpr int S_UNROLL = 8;   // k windows in flight per wave
 
 template <int MB, bool F16OUT>
 __global__ void __launch_bounds__(256)
@@ -346,8 +346,15 @@ k_gemm_skinny(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
 #pragma unroll
         for (int u = 0; u < S_UNROLL; ++u) {
             const int t = t0 + 4 * u;
-            const uint32_t off = t < KW ? (uint32_t)(t * T_FRAG + lane * 16) : OOB;
-            wf[u] = bload(rw, off);
+            // The weights are read exactly once.  Up to 32 tokens, non-temporal
+            // global loads stream them faster than buffer loads; with 64 tokens
+            // (4 activation fragments per window) the buffer loads measure faster.
+            if constexpr (MB <= 2)
+                wf[u] = t < KW ? __builtin_nontemporal_load(reinterpret_cast<const v4i *>(
+                                     W + ((int64_t)nb * KW + t) * T_FRAG + lane * 16))
+                               : v4i{0, 0, 0, 0};
+            else
+                wf[u] = bload(rw, t < KW ? (uint32_t)(t * T_FRAG + lane * 16) : OOB);
 #pragma unroll
             for (int b = 0; b < MB; ++b)
                 xf[u][b] = bload(rx, (t < KW && b < rbx) ? (uint32_t)((b * KW + t) * T_FRAG + lane * 16) : OOB);
