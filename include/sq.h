@@ -19,7 +19,7 @@
  *   - Matrices are row-major; "ld" arguments are row strides in elements.
  *   - fp16 data is IEEE binary16 passed as raw bits (const void*).
  *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
- *     Work is enqueued on that stream; only sq_smooth_fold_weights waits for it.
+ *     Work is enqueued on that stream; only sq_smooth_fold_weights waits (for s).
  *   - Every argument is checked before any HIP call or any write: a call that
  *     returns an argument error (SQ_ERR_NULL, _SHAPE, _ALIGN, _ALPHA, _KIND)
  *     has no side effects.
@@ -108,7 +108,7 @@ sq_status sq_calibrate_absmax(const void *x_cal_f16, int64_t T, int64_t K, int64
                               float *act_absmax, int accumulate, void *stream);
 
 /*
- * Smoothing factors and the offline fold of S into W (offline, synchronous).
+ * Smoothing factors and the offline fold of S into W (offline; waits for s).
  * s_j = act_absmax[j]^alpha / max_n|W[j][n]|^(1 - alpha), evaluated in double
  * and rounded once to float (alpha = 1/2 is the Pith review's
  * s_j = sqrt(max|X_j| / max|W_j|)); a channel whose activation or weight
@@ -138,11 +138,15 @@ sq_status sq_calibrate_absmax(const void *x_cal_f16, int64_t T, int64_t K, int64
  * them and each consumer's codes and scales are contiguous slices; or fold
  * each one with smooth_in set to the shared s.  Both give identical codes.
  *
- * The call waits for the stream once, to check the statistics and factors on
- * the host.  Data errors: SQ_ERR_NONFINITE when a statistic (or a smooth_in
- * entry) is NaN, infinite or negative; SQ_ERR_RANGE when a factor or its
- * reciprocal is zero, infinite or subnormal.  On a data error wq is not
- * written; smooth_out, inv_smooth_out and w_scale hold unspecified values.
+ * The call queues all its work on the stream, then waits once, until s has
+ * reached the host, and checks the statistics and factors there while the
+ * rest of the fold runs on; on return the outputs are complete in stream order
+ * (like the other calls).  Data errors: SQ_ERR_NONFINITE when a statistic (or
+ * a smooth_in entry) is NaN, infinite or negative; SQ_ERR_RANGE when a factor
+ * or its reciprocal is zero, infinite or subnormal.  On a data error all four
+ * outputs hold unspecified values (the kernels stay in bounds whatever the
+ * values).  Per (thread, device) the library keeps a pinned host buffer of
+ * 4*K bytes and an event for this check, made on first use.
  */
 sq_status sq_smooth_fold_weights(const void *w_f16, int64_t K, int64_t N, int64_t ldw,
                                  const float *act_absmax, float alpha, const float *smooth_in,

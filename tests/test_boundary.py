@@ -56,7 +56,7 @@ def test_status_strings_and_version(sq):
         s = sq.status_str(code)
         assert s.startswith("SQ_")
     assert sq.status_str(99) == "unknown sq_status"
-    assert sq.lib().sq_version() == 10100
+    assert sq.lib().sq_version() == 10200
     assert sq.SQ_MAX_K * 128 * 128 < 2 ** 31 and sq.SQ_MAX_K % 16 == 0
 
 

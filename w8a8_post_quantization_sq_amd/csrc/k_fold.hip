@@ -9,9 +9,9 @@
 // key machinery, Eq. 4 at alpha = 1/2).
 //
 // Kernels, in launch order:
-//   k_row_absmax      aw_j = max_n |W[j][n]|              (one wave per row)
-//   k_smooth_factors  s_j, 1/s_j in float; zeroes w_scale (one lane per channel)
-//   -- the host checks s and 1/s here --
+//   k_row_smooth      aw_j = max_n |W[j][n]| (one wave per row), then s_j and
+//                     1/s_j in float; zeroes w_scale
+//   (a copy of s to the host, which checks s and 1/s while the rest runs)
 //   k_fold_colabsmax  amax_n = max_j |float(W[j][n]) * s_j|  (into w_scale, atomics)
 //   k_fold_quant      Wq[n][j] = clamp(rint((W*s) * (127/amax_n)), +-127), transposed
 //                     through LDS and written as packed 16 x 64-byte fragments
@@ -24,144 +24,210 @@
 
 namespace sq {
 
-// ---- aw_j = max_n |W[j][n]| --------------------------------------------------
+// ---- aw_j = max_n |W[j][n]|, then s_j and 1/s_j ---------------------------------------
 
-__global__ void __launch_bounds__(256)
-k_row_absmax(const uint16_t *__restrict__ w, int64_t K, int64_t N, int64_t ldw,
-             float *__restrict__ aw) {
-    const int lane = threadIdx.x & 63;
-    const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (j >= K) return;
-    const uint16_t *row = w + j * ldw;
-    uint32_t m = 0;
-    for (int64_t c = (int64_t)lane * 8; c < N; c += 512) {
-        if (c + 8 <= N) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(row + c);
-            const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+// One single-wave workgroup per RS_ROWS rows; for each row a lane keeps RS_U
+// 16-byte loads (of 8 columns each, 512 columns apart) in flight, RS_ROWS x
+// RS_U in all, before reducing them.  Maxima are taken on the fp16 magnitude
+// bits, which order like the magnitudes and put NaN above +inf.  Lanes
+// 0..RS_ROWS-1 then form the factors of the wave's rows side by side: a
+// statistic that is NaN, infinite or negative (or such a given factor) yields
+// s = NaN; range problems (s or 1/s zero, infinite, subnormal) are left as
+// they come.  The host checks both.  The workgroups also clear w_scale, the
+// column maxima's accumulator.
+constexpr int RS_ROWS = 4;
+constexpr int RS_U = 4;
+
+// a^alpha / aw^(1 - alpha) in double, a and aw positive finite.  The general
+// power is long code that each wave runs once at its very end (measured: ~3.5
+// us added to the kernel), so the exponents with a short exact form take it:
+// alpha = 1/2 gives sqrt(a) / sqrt(aw) (the square-root form of the factor),
+// alpha = 1 gives a / 1 and alpha = 0 gives 1 / aw (x^0 = 1 and x^1 = x are
+// exact in pow).  The square roots and the power agree to about the last bit
+// of a double, which the rounding to float absorbs.
+__device__ __forceinline__ double pow_ratio(float a, float aw, double alpha) {
+    if (alpha == 0.5) return sqrt((double)a) / sqrt((double)aw);
+    if (alpha == 1.0) return (double)a;
+    if (alpha == 0.0) return 1.0 / (double)aw;
+    return pow((double)a, alpha) / pow((double)aw, 1.0 - alpha);
+}
+
+__global__ void __launch_bounds__(64)
+k_row_smooth(const uint16_t *__restrict__ w, int64_t K, int64_t N, int64_t ldw,
+             const float *__restrict__ ax, const float *__restrict__ smooth_in, double alpha,
+             float *__restrict__ s_out, float *__restrict__ inv_out, float *__restrict__ w_scale) {
+    for (int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x; i < N; i += (int64_t)gridDim.x * 64)
+        w_scale[i] = 0.0f;
+    const int lane = threadIdx.x;
+    const int64_t j0 = (int64_t)blockIdx.x * RS_ROWS;
+    const int64_t nfull = N & ~(int64_t)7;          // columns in whole octets
+    uint32_t m[RS_ROWS];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t lo = q[i] & 0x7fffu, hi = (q[i] >> 16) & 0x7fffu;
-                m = m > lo ? m : lo;
-                m = m > hi ? m : hi;
+    for (int r = 0; r < RS_ROWS; ++r) m[r] = 0;
+    for (int64_t base = (int64_t)lane * 8; base < nfull; base += RS_U * 512) {
+        uint4 v[RS_ROWS][RS_U];
+#pragma unroll
+        for (int r = 0; r < RS_ROWS; ++r) {
+#pragma unroll
+            for (int u = 0; u < RS_U; ++u) {
+                const int64_t c = base + (int64_t)u * 512;
+                v[r][u] = (j0 + r < K && c < nfull)
+                              ? *reinterpret_cast<const uint4 *>(w + (j0 + r) * ldw + c)
+                              : make_uint4(0, 0, 0, 0);
             }
-        } else {
-            for (int64_t e = c; e < N; ++e) {
-                const uint32_t b = row[e] & 0x7fffu;
-                m = m > b ? m : b;
+        }
+#pragma unroll
+        for (int r = 0; r < RS_ROWS; ++r) {
+#pragma unroll
+            for (int u = 0; u < RS_U; ++u) {
+                const uint32_t q[4] = {v[r][u].x, v[r][u].y, v[r][u].z, v[r][u].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t lo = q[i] & 0x7fffu, hi = (q[i] >> 16) & 0x7fffu;
+                    m[r] = m[r] > lo ? m[r] : lo;
+                    m[r] = m[r] > hi ? m[r] : hi;
+                }
             }
         }
     }
-    m = wave_max_u32(m);
-    if (lane == 0) aw[j] = h2f(m);   // NaN bits stay NaN, 0x7c00 becomes +inf
-}
-
-hipError_t launch_row_absmax(const uint16_t *w, int64_t K, int64_t N, int64_t ldw, float *aw,
-                             hipStream_t st) {
-    k_row_absmax<<<dim3((unsigned)((K + 3) / 4)), dim3(256), 0, st>>>(w, K, N, ldw, aw);
-    return hipGetLastError();
-}
-
-// ---- smoothing factors ---------------------------------------------------------
-
-// On entry aw_inv holds aw; on exit it holds 1/s.  A statistic that is NaN,
-// infinite or negative (or such a given factor) yields s = NaN, which the host
-// reports as non-finite; range problems (s or 1/s zero, infinite, subnormal)
-// are left for the host to see.  The division is IEEE-correct in float.
-__global__ void __launch_bounds__(256)
-k_smooth_factors(const float *__restrict__ ax, const float *__restrict__ smooth_in,
-                 float *__restrict__ aw_inv, double alpha, int64_t K, float *__restrict__ s_out,
-                 float *__restrict__ w_scale, int64_t N) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < K) {
-        const float aw = aw_inv[i];
-        float s;
-        if (!isfinite(aw)) {
+    // the last < 8 columns of each row: lane r takes row r
+    if (lane < RS_ROWS && j0 + lane < K) {
+        for (int64_t e = nfull; e < N; ++e) {
+#pragma unroll
+            for (int r = 0; r < RS_ROWS; ++r) {
+                if (r == lane) {
+                    const uint32_t b = w[(j0 + r) * ldw + e] & 0x7fffu;
+                    m[r] = m[r] > b ? m[r] : b;
+                }
+            }
+        }
+    }
+    uint32_t mine = 0;   // lane r ends with row r's maximum
+#pragma unroll
+    for (int r = 0; r < RS_ROWS; ++r) {
+        const uint32_t t = wave_max_u32(m[r]);
+        if (lane == r) mine = t;
+    }
+    const int64_t j = j0 + lane;
+    if (lane >= RS_ROWS || j >= K) return;
+    const float aw = h2f(mine);   // NaN bits stay NaN, 0x7c00 becomes +inf
+    float s;
+    if (!isfinite(aw)) {
+        s = __builtin_nanf("");
+    } else if (smooth_in) {
+        const float v = smooth_in[j];
+        s = (isfinite(v) && v >= 0.0f) ? v : __builtin_nanf("");
+    } else {
+        const float a = ax[j];
+        if (!isfinite(a) || a < 0.0f)
             s = __builtin_nanf("");
-        } else if (smooth_in) {
-            const float v = smooth_in[i];
-            s = (isfinite(v) && v >= 0.0f) ? v : __builtin_nanf("");
-        } else {
-            const float a = ax[i];
-            if (!isfinite(a) || a < 0.0f)
-                s = __builtin_nanf("");
-            else if (a == 0.0f || aw == 0.0f)
-                s = 1.0f;   // dead channel or zero row: the plainest positive factor
-            else
-                s = (float)(pow((double)a, alpha) / pow((double)aw, 1.0 - alpha));
-        }
-        s_out[i] = s;
-        aw_inv[i] = 1.0f / s;
+        else if (a == 0.0f || aw == 0.0f)
+            s = 1.0f;   // dead channel or zero row: the plainest positive factor
+        else
+            s = (float)(pow_ratio(a, aw, alpha));
     }
-    if (i < N) w_scale[i] = 0.0f;
+    s_out[j] = s;
+    inv_out[j] = 1.0f / s;   // IEEE-correct float division
 }
 
-hipError_t launch_smooth_factors(const float *ax, const float *smooth_in, float *aw_in_inv_out,
-                                 float alpha, int64_t K, float *s_out, float *w_scale_zero,
-                                 int64_t N, hipStream_t st) {
-    const int64_t n = K > N ? K : N;
-    k_smooth_factors<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(
-        ax, smooth_in, aw_in_inv_out, (double)alpha, K, s_out, w_scale_zero, N);
+hipError_t launch_row_smooth(const uint16_t *w, int64_t K, int64_t N, int64_t ldw,
+                             const float *ax, const float *smooth_in, float alpha, float *s_out,
+                             float *inv_out, float *w_scale, hipStream_t st) {
+    k_row_smooth<<<dim3((unsigned)((K + RS_ROWS - 1) / RS_ROWS)), dim3(64), 0, st>>>(
+        w, K, N, ldw, ax, smooth_in, (double)alpha, s_out, inv_out, w_scale);
     return hipGetLastError();
 }
 
 // ---- amax_n = max_j |float(W[j][n]) * s_j| ---------------------------------------
 
-// Same layout as the calibration kernel: 512 columns per workgroup, 8 per lane,
-// waves stride over a slice of rows, LDS combine, one atomicMax per column on
-// the (non-negative) float bits.  W has already been checked finite.
+// A workgroup covers 128 columns (16 lanes x 8, a 256-byte row segment) over a
+// slice of rows; a wave load spans 4 rows, and each lane keeps CA_U loads
+// (16 rows apart) in flight before reducing them.  The 16 row phases combine
+// through shuffles and LDS, then one atomicMax per column on the (non-negative)
+// float bits.  With factors that the host will reject, the values are
+// meaningless but every access stays in bounds.
+constexpr int CA_COLS = 128;
+constexpr int CA_U = 8;
+constexpr int CA_ROUND = 16 * CA_U;   // rows per workgroup round
+
 __global__ void __launch_bounds__(256)
 k_fold_colabsmax(const uint16_t *__restrict__ w, int64_t K, int64_t N, int64_t ldw,
-                 const float *__restrict__ s, int rows_per_block, float *__restrict__ amax) {
-    __shared__ uint32_t red[4][512];
+                 const float *__restrict__ s, int64_t rows_per_block, float *__restrict__ amax) {
+    __shared__ float red[4][CA_COLS];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t c0 = (int64_t)blockIdx.x * 512 + lane * 8;
+    const int64_t c0 = (int64_t)blockIdx.x * CA_COLS + (lane & 15) * 8;
+    const int sub = wave * 4 + (lane >> 4);          // row phase 0..15
     const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
     const int64_t r1 = r0 + rows_per_block < K ? r0 + rows_per_block : K;
+    const bool full = c0 + 8 <= N;
+    const int tail = full ? 0 : (c0 < N ? (int)(N - c0) : 0);   // columns of a partial octet
     float m[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) m[i] = 0.0f;
-    if (c0 < N) {
-        for (int64_t r = r0 + wave; r < r1; r += 4) {
-            const float sj = s[r];
-            const uint16_t *row = w + r * ldw + c0;
-            if (c0 + 8 <= N) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(row);
-                const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+    for (int64_t rb = r0 + sub; rb < r1; rb += CA_ROUND) {
+        uint4 v[CA_U];
+        float sj[CA_U];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    m[2 * i] = fmaxf(m[2 * i], fabsf(h2f(q[i] & 0xffffu) * sj));
-                    m[2 * i + 1] = fmaxf(m[2 * i + 1], fabsf(h2f(q[i] >> 16) * sj));
-                }
-            } else {
-                for (int i = 0; i < 8 && c0 + i < N; ++i)
-                    m[i] = fmaxf(m[i], fabsf(h2f(row[i]) * sj));
+        for (int u = 0; u < CA_U; ++u) {
+            const int64_t r = rb + 16 * u;
+            const bool ok = r < r1;
+            v[u] = (ok && full) ? *reinterpret_cast<const uint4 *>(w + r * ldw + c0)
+                                : make_uint4(0, 0, 0, 0);
+            sj[u] = ok ? s[r] : 0.0f;
+        }
+        if (tail) {   // the octet that N cuts: element loads, zeros past N
+#pragma unroll
+            for (int u = 0; u < CA_U; ++u) {
+                const int64_t r = rb + 16 * u;
+                uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                if (r < r1)
+                    for (int i = 0; i < tail; ++i) h[i] = w[r * ldw + c0 + i];
+                v[u] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                  h[6] | (h[7] << 16));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < CA_U; ++u) {
+            const uint32_t q[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                m[2 * i] = fmaxf(m[2 * i], fabsf(h2f(q[i] & 0xffffu) * sj[u]));
+                m[2 * i + 1] = fmaxf(m[2 * i + 1], fabsf(h2f(q[i] >> 16) * sj[u]));
             }
         }
     }
+    // lanes l, l+16, l+32, l+48 hold the same columns
 #pragma unroll
-    for (int i = 0; i < 8; ++i) red[wave][lane * 8 + i] = __float_as_uint(m[i]);
+    for (int i = 0; i < 8; ++i) {
+        m[i] = fmaxf(m[i], __shfl_xor(m[i], 16, 64));
+        m[i] = fmaxf(m[i], __shfl_xor(m[i], 32, 64));
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) red[wave][lane * 8 + i] = m[i];
+    }
     __syncthreads();
-    for (int c = threadIdx.x; c < 512; c += 256) {
-        uint32_t b = red[0][c];
-        b = b > red[1][c] ? b : red[1][c];
-        b = b > red[2][c] ? b : red[2][c];
-        b = b > red[3][c] ? b : red[3][c];
-        const int64_t col = (int64_t)blockIdx.x * 512 + c;
-        if (col < N && r1 > r0) atomicMax(reinterpret_cast<unsigned int *>(amax + col), b);
+    if (threadIdx.x < CA_COLS) {
+        const int c = threadIdx.x;
+        const float b = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
+        const int64_t col = (int64_t)blockIdx.x * CA_COLS + c;
+        if (col < N && r1 > r0)
+            atomicMax(reinterpret_cast<unsigned int *>(amax + col), __float_as_uint(b));
     }
 }
 
 hipError_t launch_fold_colabsmax(const uint16_t *w, int64_t K, int64_t N, int64_t ldw,
                                  const float *s, float *amax, hipStream_t st) {
-    const int64_t col_blocks = (N + 511) / 512;
-    int64_t want = 2048 / col_blocks;
+    const int64_t col_blocks = (N + CA_COLS - 1) / CA_COLS;
+    // about 512 workgroups: slices of whole rounds
+    const int64_t rounds = (K + CA_ROUND - 1) / CA_ROUND;
+    int64_t want = 512 / col_blocks;
     if (want < 1) want = 1;
-    int64_t rows = (K + want - 1) / want;
-    if (rows < 8) rows = 8;
+    const int64_t rows = CA_ROUND * ((rounds + want - 1) / want);
     const int64_t row_blocks = (K + rows - 1) / rows;
     k_fold_colabsmax<<<dim3((unsigned)col_blocks, (unsigned)row_blocks), dim3(256), 0, st>>>(
-        w, K, N, ldw, s, (int)rows, amax);
+        w, K, N, ldw, s, rows, amax);
     return hipGetLastError();
 }
 
@@ -170,67 +236,88 @@ hipError_t launch_fold_colabsmax(const uint16_t *w, int64_t K, int64_t N, int64_
 // Tile: 64 output channels x 256 input channels.  A work item is 4 consecutive
 // rows j x 8 consecutive columns n (four 16-byte loads); each of its 8 columns
 // yields 4 consecutive codes of one Wq row, packed into a 32-bit LDS store.
+// Each thread issues the loads of both its items before it converts any.  The
+// quotients 127 / amax_n are formed once per column and passed by shuffles.
 // The tile then leaves as 4 x 4 packed fragments of 1 KiB (16 channels x 64
 // input channels each), one 16-byte store per lane.  Out-of-range channels and
 // input channels hold zero codes, so the padding of the packed buffer is zero.
+//
+// LDS holds the tile as 64 rows (channels) of 16 chunks of 16 bytes (4 input
+// channels per word).  The chunk index is XOR-swizzled with bits of the row,
+// so the 32-bit stores (8 rows x 8 words per wave) and the 16-byte reads (16
+// rows of one chunk column per 16 lanes) both spread over the banks.
 constexpr int FQ_TN = 64;
 constexpr int FQ_TK = 256;
-constexpr int FQ_LDS = FQ_TK + 16;   // row pitch in bytes; breaks power-of-two strides
+
+__device__ __forceinline__ int fq_word(int row, int word) {   // word: 4-byte column 0..63
+    const int swz = (((row ^ (row >> 3)) & 7) << 1) | ((row >> 3) & 1);
+    return row * (FQ_TK / 4) + ((((word >> 2) ^ swz) << 2) | (word & 3));
+}
 
 __global__ void __launch_bounds__(256)
 k_fold_quant(const uint16_t *__restrict__ w, int64_t K, int64_t N, int64_t ldw,
              const float *__restrict__ s, const float *__restrict__ amax,
              int8_t *__restrict__ wq) {
-    __shared__ __align__(16) uint8_t tile[FQ_TN * FQ_LDS];
+    __shared__ __align__(16) uint32_t tile[FQ_TN * FQ_TK / 4];
     const int64_t n0 = (int64_t)blockIdx.x * FQ_TN;
     const int64_t k0 = (int64_t)blockIdx.y * FQ_TK;
-    // 64 row-quads x 8 column-octets = 512 work items, 2 per thread
+    // 64 row-quads x 8 column-octets = 512 work items, 2 per thread; both
+    // items of a thread share its column octet (threadIdx.x % 8)
+    const int lane = threadIdx.x & 63;
+    const int oct = threadIdx.x & 7;       // column octet within the tile
+    const int64_t n = n0 + oct * 8;
+    const bool full = n + 8 <= N;
+    uint4 raw[2][4];
+    float sj[2][4];
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-        const int item = threadIdx.x + it * 256;
-        const int oct = item & 7;          // column octet within the tile
-        const int quad = item >> 3;        // row quad within the tile
-        const int64_t n = n0 + oct * 8;
+        const int64_t j = k0 + ((threadIdx.x + it * 256) >> 3) * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const bool ok = j + q < K;
+            raw[it][q] = (ok && full) ? *reinterpret_cast<const uint4 *>(w + (j + q) * ldw + n)
+                                      : make_uint4(0, 0, 0, 0);
+            sj[it][q] = ok ? s[j + q] : 0.0f;
+        }
+    }
+    // 127 / amax: lane l divides for tile column l, and each lane picks up
+    // the 8 quotients of its octet from the lanes that made them
+    const float al = n0 + lane < N ? amax[n0 + lane] : 0.0f;
+    const float rl = al > 0.0f ? 127.0f / al : 0.0f;
+    float r[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) r[c] = __shfl(rl, oct * 8 + c, 64);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int quad = (threadIdx.x + it * 256) >> 3;   // row quad within the tile
         const int64_t j = k0 + quad * 4;
+        if (n < N && n + 8 > N) {   // the octet that N cuts: element loads, zeros past N
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                if (j + q < K)
+                    for (int i = 0; n + i < N; ++i) h[i] = w[(j + q) * ldw + n + i];
+                raw[it][q] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                        h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+            }
+        }
         uint32_t packed[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) packed[c] = 0;
-        float r[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const float a = (n + c < N) ? amax[n + c] : 0.0f;
-            r[c] = a > 0.0f ? 127.0f / a : 0.0f;
-        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int64_t jj = j + q;
-            if (jj >= K) break;
-            const float sj = s[jj];
-            float v[8];
-            const uint16_t *row = w + jj * ldw + n;
-            if (n + 8 <= N) {
-                const uint4 raw = *reinterpret_cast<const uint4 *>(row);
-                const uint32_t h[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    v[2 * i] = h2f(h[i] & 0xffffu);
-                    v[2 * i + 1] = h2f(h[i] >> 16);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = (n + i < N) ? h2f(row[i]) : 0.0f;
-            }
+            const uint32_t hq[4] = {raw[it][q].x, raw[it][q].y, raw[it][q].z, raw[it][q].w};
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                const float wt = v[c] * sj;                 // W~ = W * s_j (float)
+                const float v = h2f(c & 1 ? hq[c >> 1] >> 16 : hq[c >> 1] & 0xffffu);
+                const float wt = v * sj[it][q];             // W~ = W * s_j (float)
                 float qf = __builtin_rintf(wt * r[c]);      // round half to even
                 qf = fminf(fmaxf(qf, -127.0f), 127.0f);
                 packed[c] |= ((uint32_t)(int)qf & 0xffu) << (8 * q);
             }
         }
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-            *reinterpret_cast<uint32_t *>(tile + (oct * 8 + c) * FQ_LDS + quad * 4) = packed[c];
+        for (int c = 0; c < 8; ++c) tile[fq_word(oct * 8 + c, quad)] = packed[c];
     }
     __syncthreads();
     // 16 fragments x 64 lanes of 16 bytes = 1024 chunks, 4 per thread
@@ -245,10 +332,11 @@ k_fold_quant(const uint16_t *__restrict__ w, int64_t K, int64_t N, int64_t ldw,
         const int64_t rb = (n0 >> 4) + rbl;
         const int64_t kw = (k0 >> 6) + kwl;
         const int rn = rbl * 16 + (l & 15);
-        const int kk = kwl * 64 + (l >> 4) * 16;
+        const int word = kwl * 16 + (l >> 4) * 4;     // first of 4 words (16 codes)
+        // non-temporal: the codes are not read again by this pass
         if (rb < RB && kw < KW)
-            *reinterpret_cast<uint4 *>(wq + ((rb * KW + kw) << 10) + l * 16) =
-                *reinterpret_cast<const uint4 *>(tile + rn * FQ_LDS + kk);
+            __builtin_nontemporal_store(*reinterpret_cast<const v4i *>(tile + fq_word(rn, word)),
+                                        reinterpret_cast<v4i *>(wq + ((rb * KW + kw) << 10) + l * 16));
     }
 }
 

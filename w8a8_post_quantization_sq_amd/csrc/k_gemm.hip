@@ -297,7 +297,9 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
             if (m < M) {
                 uint16_t *dst = reinterpret_cast<uint16_t *>(Y) + (int64_t)m * ldy + n;
                 if (n + 7 < N) {
-                    *reinterpret_cast<uint4 *>(dst) = v;
+                    // non-temporal: the output is not read again here
+                    const v4i vv = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+                    __builtin_nontemporal_store(vv, reinterpret_cast<v4i *>(dst));
                 } else {
                     const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll

@@ -1,7 +1,8 @@
 // C ABI of the smoothed W8A8 linear layer: argument checks, then launches on
 // the caller's stream.  Every check runs before the first HIP call, so a call
 // rejected for its arguments has no side effects.  The only host-side data
-// work is the fold's check of the smoothing factors it has just computed.
+// work is the fold's check of the smoothing factors it has just computed,
+// which overlaps the rest of the fold on the device.
 #include <math.h>
 #include <stdint.h>
 
@@ -25,6 +26,62 @@ inline sq_status hip_status(hipError_t e) { return e == hipSuccess ? SQ_OK : SQ_
 // K: 16 <= K <= SQ_MAX_K, K % 16 == 0 (int8 rows are whole 16-byte chunks).
 inline bool k_ok(int64_t K) { return K >= 16 && K <= SQ_MAX_K && (K % 16) == 0; }
 
+// Host side of the fold's factor check: a pinned buffer that receives s and
+// an event that marks its arrival, one pair per (thread, device), made on
+// first use and kept until the process ends.  A thread's calls wait for their
+// copy before returning, so the next call may reuse the buffer.  (The copy
+// stays in line on the caller's stream: on a side stream, the cross-stream
+// event costs more than the copy it would hide.)
+struct Staging {
+    float *host = nullptr;
+    int64_t cap = 0;
+    hipEvent_t ready = nullptr;    // s on the host
+};
+
+hipError_t make_staging(Staging &g) {
+    return hipEventCreateWithFlags(&g.ready, hipEventDisableTiming);
+}
+
+hipError_t staging_for(hipStream_t st, int64_t K, Staging **out) {
+    static thread_local std::vector<Staging> per_device;
+    int cur = 0, dev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    dev = cur;
+    if (st) {
+        e = hipStreamGetDevice(st, &dev);
+        if (e != hipSuccess) return e;
+    }
+    if (dev < 0) return hipErrorInvalidDevice;
+    if ((int)per_device.size() <= dev) per_device.resize((size_t)dev + 1);
+    Staging &g = per_device[(size_t)dev];
+    if (!g.ready) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        Staging fresh;
+        e = make_staging(fresh);
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;   // (a partly made set is left to the process end)
+        fresh.host = g.host;
+        fresh.cap = g.cap;
+        g = fresh;
+    }
+    if (g.cap < K) {
+        if (g.host && (e = hipHostFree(g.host)) != hipSuccess) return e;
+        g.host = nullptr;
+        g.cap = 0;
+        void *p = nullptr;
+        e = hipHostMalloc(&p, (size_t)K * sizeof(float), hipHostMallocDefault);
+        if (e != hipSuccess) return e;
+        g.host = static_cast<float *>(p);
+        g.cap = K;
+    }
+    *out = &g;
+    return hipSuccess;
+}
+
 }  // namespace
 
 SQ_API const char *sq_status_str(int status) {
@@ -42,7 +99,7 @@ SQ_API const char *sq_status_str(int status) {
     }
 }
 
-SQ_API int sq_version(void) { return 10100; }
+SQ_API int sq_version(void) { return 10200; }
 
 SQ_API int64_t sq_packed_bytes(int64_t rows, int64_t K) {
     if (rows < 0 || rows >= kMaxDim || !k_ok(K)) return 0;
@@ -55,13 +112,8 @@ SQ_API sq_status sq_calibrate_absmax(const void *x_cal_f16, int64_t T, int64_t K
     if (T < 0 || T >= kMaxDim || !k_ok(K) || ldx < K) return SQ_ERR_SHAPE;
     if (!aligned16(act_absmax) || (x_cal_f16 && !aligned16(x_cal_f16)) || (ldx % 8) != 0)
         return SQ_ERR_ALIGN;
-    const hipStream_t st = as_stream(stream);
-    if (!accumulate) {
-        sq_status s = hip_status(sq::launch_fill_f32(act_absmax, K, 0.0f, st));
-        if (s != SQ_OK) return s;
-    }
     return hip_status(sq::launch_calib_absmax(static_cast<const uint16_t *>(x_cal_f16), T, K, ldx,
-                                              act_absmax, st));
+                                              act_absmax, accumulate != 0, as_stream(stream)));
 }
 
 SQ_API sq_status sq_smooth_fold_weights(const void *w_f16, int64_t K, int64_t N, int64_t ldw,
@@ -81,39 +133,41 @@ SQ_API sq_status sq_smooth_fold_weights(const void *w_f16, int64_t K, int64_t N,
 
     const hipStream_t st = as_stream(stream);
     const uint16_t *w = static_cast<const uint16_t *>(w_f16);
-    hipError_t e;
-    // aw_j into inv_smooth_out (also run with given factors: it checks W is finite)
-    if (N > 0) {
-        e = sq::launch_row_absmax(w, K, N, ldw, inv_smooth_out, st);
-    } else {
-        e = sq::launch_fill_f32(inv_smooth_out, K, 0.0f, st);
+    Staging *g = nullptr;
+    hipError_t e = staging_for(st, K, &g);
+    if (e != hipSuccess) return SQ_ERR_HIP;
+    // Everything is queued before the one wait: s goes to the host right after
+    // it is formed, and the column maxima and the codes follow on the stream
+    // while the host waits for it.  With N == 0 no row is read (aw = 0).
+    e = sq::launch_row_smooth(w, K, N, ldw, act_absmax, smooth_in, alpha, smooth_out,
+                              inv_smooth_out, w_scale, st);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(g->host, smooth_out, (size_t)K * sizeof(float), hipMemcpyDeviceToHost, st);
+    if (e != hipSuccess) return SQ_ERR_HIP;
+    e = hipEventRecord(g->ready, st);
+    if (e != hipSuccess) {
+        hipStreamSynchronize(st);   // the copy must land before the buffer is reused
+        return SQ_ERR_HIP;
     }
-    if (e != hipSuccess) return SQ_ERR_HIP;
-    e = sq::launch_smooth_factors(act_absmax, smooth_in, inv_smooth_out, alpha, K, smooth_out,
-                                  w_scale, N, st);
-    if (e != hipSuccess) return SQ_ERR_HIP;
+    if (N > 0) {
+        e = sq::launch_fold_colabsmax(w, K, N, ldw, smooth_out, w_scale, st);
+        if (e == hipSuccess) e = sq::launch_fold_quant(w, K, N, ldw, smooth_out, w_scale, wq, st);
+        if (e == hipSuccess) e = sq::launch_fold_finalize(w_scale, N, st);
+    }
+    const hipError_t ew = hipEventSynchronize(g->ready);
+    if (e != hipSuccess || ew != hipSuccess) return SQ_ERR_HIP;
 
-    // The one host step: look at s before anything is written to wq.  1/s is
-    // the IEEE float quotient on both sides, so the host recomputes it for
-    // the range check instead of copying it back.
-    std::vector<float> hs((size_t)K);
-    e = hipMemcpyAsync(hs.data(), smooth_out, (size_t)K * sizeof(float), hipMemcpyDeviceToHost, st);
-    if (e == hipSuccess) e = hipStreamSynchronize(st);
-    if (e != hipSuccess) return SQ_ERR_HIP;
+    // 1/s is the IEEE float quotient on both sides, so the host recomputes it
+    // for the range check instead of copying it back.
     bool nonfinite = false, range = false;
     for (int64_t j = 0; j < K; ++j) {
-        const float sj = hs[j];
+        const float sj = g->host[j];
         if (isnan(sj)) nonfinite = true;
         else if (!isnormal(sj) || !isnormal(1.0f / sj) || sj < 0.0f) range = true;
     }
     if (nonfinite) return SQ_ERR_NONFINITE;
     if (range) return SQ_ERR_RANGE;
-    if (N == 0) return SQ_OK;
-
-    e = sq::launch_fold_colabsmax(w, K, N, ldw, smooth_out, w_scale, st);
-    if (e == hipSuccess) e = sq::launch_fold_quant(w, K, N, ldw, smooth_out, w_scale, wq, st);
-    if (e == hipSuccess) e = sq::launch_fold_finalize(w_scale, N, st);
-    return hip_status(e);
+    return SQ_OK;
 }
 
 SQ_API sq_status sq_quant_act_per_token(const void *x_f16, int64_t M, int64_t K, int64_t ldx,

@@ -10,15 +10,14 @@ namespace sq {
 
 hipError_t launch_fill_f32(float *p, int64_t n, float v, hipStream_t st);
 
+// accumulate == 0: ax = the maximum (zeros for T == 0); else ax = max(ax, it)
 hipError_t launch_calib_absmax(const uint16_t *x, int64_t T, int64_t K, int64_t ldx,
-                               float *ax, hipStream_t st);
+                               float *ax, int accumulate, hipStream_t st);
 
-hipError_t launch_row_absmax(const uint16_t *w, int64_t K, int64_t N, int64_t ldw,
-                             float *aw, hipStream_t st);
-
-hipError_t launch_smooth_factors(const float *ax, const float *smooth_in, float *aw_in_inv_out,
-                                 float alpha, int64_t K, float *s_out, float *w_scale_zero,
-                                 int64_t N, hipStream_t st);
+// aw_j = max_n |W[j][n]| -> s_out[j] = s_j, inv_out[j] = 1/s_j; zeroes w_scale[0, N)
+hipError_t launch_row_smooth(const uint16_t *w, int64_t K, int64_t N, int64_t ldw,
+                             const float *ax, const float *smooth_in, float alpha, float *s_out,
+                             float *inv_out, float *w_scale, hipStream_t st);
 
 hipError_t launch_fold_colabsmax(const uint16_t *w, int64_t K, int64_t N, int64_t ldw,
                                  const float *s, float *amax, hipStream_t st);
