@@ -21,10 +21,11 @@
 // 16 x 16 block.
 //
 // k_gemm_tile (M > 64): output tile 256 tokens x 128 channels per workgroup
-// of 4 waves; wave w owns tokens [64w, 64w + 64) and all 128 channels.
+// of 8 waves, two per SIMD, so one wave's products cover the other's waits;
+// wave w owns tokens [32w, 32w + 32) and all 128 channels.
 //   - activation fragments are private to a wave and go straight from global
 //     memory into a register ring, 3 k-steps ahead;
-//   - the 8 KiB weight slice of a k-step is shared by the 4 waves: staged
+//   - the 8 KiB weight slice of a k-step is shared by the 8 waves: staged
 //     through registers into a ring of 4 LDS buffers (copied as is, in lane
 //     order, so reads and writes are conflict-free);
 //   - the loop is software-pipelined: while the matrix cores work on step t,
@@ -114,20 +115,21 @@ __device__ __forceinline__ void store4(void *Y, int64_t ldy, bool vec_ok, int m,
 
 // ---- large token counts --------------------------------------------------------------
 
-constexpr int T_BM = 256;            // tokens per tile (16 row blocks, 4 per wave)
+constexpr int T_BM = 256;            // tokens per tile (16 row blocks, 2 per wave)
 constexpr int T_BN = 128;            // channels per tile (8 row blocks)
 constexpr int T_FRAG = 1024;         // bytes per packed fragment
 constexpr int T_SLICE = 8 * T_FRAG;  // weight bytes per k-step
+constexpr int T_WAVES = 8;
 
 template <bool F16OUT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64 * T_WAVES)
 k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
             const float *__restrict__ xs, const float *__restrict__ ws, int M, int N, int K,
             void *__restrict__ Y, int64_t ldy, int tiles_m, int tiles_n, int vec_ok) {
-    // LDS: 4 weight slices during the k loop, then 4 wave tiles of the epilogue
+    // LDS: 4 weight slices during the k loop, then 8 wave tiles of the epilogue
     constexpr int EPI_PITCH = 128 * 2 + 16;            // bytes per row of 128 fp16, padded
-    constexpr int EPI_WAVE = 64 * EPI_PITCH;            // 64 rows per wave
-    constexpr int LDS_BYTES = (4 * T_SLICE > 4 * EPI_WAVE) ? 4 * T_SLICE : 4 * EPI_WAVE;
+    constexpr int EPI_WAVE = 32 * EPI_PITCH;            // 32 rows per wave
+    constexpr int LDS_BYTES = (4 * T_SLICE > T_WAVES * EPI_WAVE) ? 4 * T_SLICE : T_WAVES * EPI_WAVE;
     __shared__ __align__(16) int8_t lds_raw[LDS_BYTES];
     int8_t (*ldsw)[T_SLICE] = reinterpret_cast<int8_t (*)[T_SLICE]>(lds_raw);
 
@@ -147,49 +149,64 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
     const __amdgpu_buffer_rsrc_t rw =
         make_rsrc(W + (int64_t)(n0 >> 4) * KW * T_FRAG, (int64_t)nbw * KW * T_FRAG);
 
-    // activation fragments: this wave's row blocks 4w + i
-    uint32_t xbase[4];
+    // the epilogue's scales are loaded now and wait in registers
+    float xsv[2];
+    float4 wsv[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int b = wave * 4 + i;
+    for (int i = 0; i < 2; ++i) {
+        const int m = m0 + wave * 32 + i * 16 + (lane & 15);
+        xsv[i] = (F16OUT && m < M) ? xs[m] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int n = n0 + j * 16 + (lane >> 4) * 4;
+        wsv[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (F16OUT) {
+            if (n + 3 < N) {
+                wsv[j] = make_float4(ws[n], ws[n + 1], ws[n + 2], ws[n + 3]);
+            } else {
+                if (n < N) wsv[j].x = ws[n];
+                if (n + 1 < N) wsv[j].y = ws[n + 1];
+                if (n + 2 < N) wsv[j].z = ws[n + 2];
+            }
+        }
+    }
+
+    // activation fragments: this wave's row blocks 2w and 2w + 1
+    uint32_t xbase[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int b = wave * 2 + i;
         xbase[i] = b < nbx ? (uint32_t)(b * KW * T_FRAG + lane * 16) : OOB_BASE;
     }
-    // weight slice: 512 chunks of 16 bytes, 2 per thread; chunk idx = fragment idx / 64, lane idx % 64
-    uint32_t wbase[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        const int idx = tid + s * 256;
-        const int b = idx >> 6;
-        wbase[s] = b < nbw ? (uint32_t)(b * KW * T_FRAG + (idx & 63) * 16) : OOB_BASE;
+    // weight slice: 512 chunks of 16 bytes, one per thread; chunk tid = fragment tid / 64, lane tid % 64
+    uint32_t wbase;
+    {
+        const int b = tid >> 6;
+        wbase = b < nbw ? (uint32_t)(b * KW * T_FRAG + (tid & 63) * 16) : OOB_BASE;
     }
     // Offset of k window t (uniform): windows past the last one get OOB_WIN, so
     // every lane's base + offset falls past the buffer and reads zero.  Bases
     // are < 2^25 or OOB_BASE, offsets < 2^21 or OOB_WIN, so sums never wrap.
     auto win = [&](int t) -> uint32_t { return t < KW ? (uint32_t)t * T_FRAG : OOB_WIN; };
 
-    v4i acc[4][8];
+    v4i acc[2][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-    v4i xr[4][4];    // activation ring: steps t .. t+3
-    v4i wst[2][2];   // weight staging ring: steps t+2, t+3
+    v4i xr[4][2];    // activation ring: steps t .. t+3
+    v4i wst[2];      // weight staging ring: steps t+2, t+3
     v4i wf[8];       // weight fragments of the current step
     auto load_x = [&](int slot, int t) {
         const uint32_t wo = win(t);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xr[slot][i] = bload(rx, xbase[i] + wo);
+        for (int i = 0; i < 2; ++i) xr[slot][i] = bload(rx, xbase[i] + wo);
     };
-    auto load_w = [&](int slot, int t) {
-        const uint32_t wo = win(t);
-#pragma unroll
-        for (int s = 0; s < 2; ++s) wst[slot][s] = bload(rw, wbase[s] + wo);
-    };
+    auto load_w = [&](int slot, int t) { wst[slot] = bload(rw, wbase + win(t)); };
     auto store_w = [&](int slot, int buf) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-            *reinterpret_cast<v4i *>(&ldsw[buf][(tid + s * 256) * 16]) = wst[slot][s];
+        *reinterpret_cast<v4i *>(&ldsw[buf][tid * 16]) = wst[slot];
     };
 
     // prologue: weight slices 0 and 1 in LDS, slice 2 staged, activations 0..2 in flight
@@ -210,8 +227,8 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
         for (int u = 0; u < 4; ++u) {
             const int t = t0 + u;
             // this step's loads go out first and stay first: the weight slice
-            // stored into LDS at the end of the step was issued a whole step
-            // earlier, with this step's six loads behind it, so its wait does
+            // stored into LDS in the middle of the step was issued a step
+            // earlier, with this step's three loads behind it, so its wait does
             // not drain the activation prefetch
             load_w((u + 1) & 1, t + 3);
             load_x((u + 3) & 3, t + 3);
@@ -220,18 +237,17 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i][j] = mfma(wf[j], xr[u][i], acc[i][j]);
+                for (int i = 0; i < 2; ++i) acc[i][j] = mfma(wf[j], xr[u][i], acc[i][j]);
                 wf[j] = *reinterpret_cast<const v4i *>(&ldsw[nb][j * T_FRAG + lane * 16]);
                 if (j == 3) {
                     // the staged slice t+2 goes to LDS mid-step, pinned between
-                    // the reads of fragments 3 and 4 (it was loaded a step and a
-                    // half ago)
+                    // the reads of fragments 3 and 4
                     __builtin_amdgcn_sched_barrier(0);
                     store_w(u & 1, (u + 2) & 3);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            // Before the barrier only the two stores must be complete: LDS
+            // Before the barrier only the store must be complete: LDS
             // operations of a wave complete in order, so at most the 4 later
             // fragment reads may still be in flight (they read slice t+1,
             // which nobody overwrites before two more barriers).
@@ -244,37 +260,15 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
         }
     }
 
-    // epilogue.  Scales first, in one batch of loads.  fp16 output then goes
-    // through LDS (the weight buffers are free now): each wave converts its
-    // 64 x 128 block into a padded LDS tile and writes it back as rows of 256
-    // contiguous bytes, 16 bytes per lane.
-    float xsv[4];
-    float4 wsv[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = m0 + wave * 64 + i * 16 + (lane & 15);
-        xsv[i] = (F16OUT && m < M) ? xs[m] : 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int n = n0 + j * 16 + (lane >> 4) * 4;
-        wsv[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (F16OUT) {
-            if (n + 3 < N) {
-                wsv[j] = make_float4(ws[n], ws[n + 1], ws[n + 2], ws[n + 3]);
-            } else {
-                if (n < N) wsv[j].x = ws[n];
-                if (n + 1 < N) wsv[j].y = ws[n + 1];
-                if (n + 2 < N) wsv[j].z = ws[n + 2];
-            }
-        }
-    }
+    // epilogue.  fp16 output goes through LDS (the weight buffers are free
+    // now): each wave converts its 32 x 128 block into a padded LDS tile and
+    // writes it back as rows of 256 contiguous bytes, 16 bytes per lane.
     if (F16OUT && (vec_ok & 2)) {
         constexpr int PITCH = EPI_PITCH;
-        int8_t *tile = lds_raw + wave * EPI_WAVE;     // this wave's 17 KiB
+        int8_t *tile = lds_raw + wave * EPI_WAVE;     // this wave's 8.5 KiB
         __syncthreads();                              // every wave is done with the slices
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2; ++i) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const v4i &a = acc[i][j];
@@ -287,11 +281,11 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
             }
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0): this wave's LDS writes done
-        // 64 rows x 16 chunks of 16 bytes, 16 per lane; 4 rows per instruction
+        // 32 rows x 16 chunks of 16 bytes, 8 per lane; 4 rows per instruction
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
+        for (int c = 0; c < 8; ++c) {
             const int r = c * 4 + (lane >> 4);
-            const int m = m0 + wave * 64 + r;
+            const int m = m0 + wave * 32 + r;
             const int n = n0 + (lane & 15) * 8;
             const uint4 v = *reinterpret_cast<const uint4 *>(tile + r * PITCH + (lane & 15) * 16);
             if (m < M) {
@@ -310,8 +304,8 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = m0 + wave * 64 + i * 16 + (lane & 15);
+        for (int i = 0; i < 2; ++i) {
+            const int m = m0 + wave * 32 + i * 16 + (lane & 15);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 store4<F16OUT>(Y, ldy, (vec_ok & 1) != 0, m, n0 + j * 16 + (lane >> 4) * 4, M, N,
@@ -405,10 +399,10 @@ hipError_t launch_gemm(const int8_t *xq, const float *x_scale, const int8_t *wq,
         const int tiles_n = (n + T_BN - 1) / T_BN;
         const dim3 grid((unsigned)(tiles_m * tiles_n));
         if (f16)
-            k_gemm_tile<true><<<grid, dim3(256), 0, st>>>(xq, wq, x_scale, w_scale, m, n, k, y, ldy,
+            k_gemm_tile<true><<<grid, dim3(64 * T_WAVES), 0, st>>>(xq, wq, x_scale, w_scale, m, n, k, y, ldy,
                                                           tiles_m, tiles_n, vec_ok);
         else
-            k_gemm_tile<false><<<grid, dim3(256), 0, st>>>(xq, wq, x_scale, w_scale, m, n, k, y, ldy,
+            k_gemm_tile<false><<<grid, dim3(64 * T_WAVES), 0, st>>>(xq, wq, x_scale, w_scale, m, n, k, y, ldy,
                                                            tiles_m, tiles_n, vec_ok);
         return hipGetLastError();
     }

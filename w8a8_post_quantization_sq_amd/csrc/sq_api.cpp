@@ -146,7 +146,7 @@ SQ_API sq_status sq_smooth_fold_weights(const void *w_f16, int64_t K, int64_t N,
     if (e != hipSuccess) return SQ_ERR_HIP;
     e = hipEventRecord(g->ready, st);
     if (e != hipSuccess) {
-        hipStreamSynchronize(st);   // the copy must land before the buffer is reused
+        (void)hipStreamSynchronize(st);   // the copy must land before the buffer is reused
         return SQ_ERR_HIP;
     }
     if (N > 0) {
