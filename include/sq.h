@@ -145,8 +145,11 @@ sq_status sq_calibrate_absmax(const void *x_cal_f16, int64_t T, int64_t K, int64
  * a smooth_in entry) is NaN, infinite or negative; SQ_ERR_RANGE when a factor
  * or its reciprocal is zero, infinite or subnormal.  On a data error all four
  * outputs hold unspecified values (the kernels stay in bounds whatever the
- * values).  Per (thread, device) the library keeps a pinned host buffer of
- * 4*K bytes and an event for this check, made on first use.
+ * values).  Per (thread, device) the library keeps, from the first call on
+ * and grown as needed, a pinned host buffer of 4*K bytes for this check, a
+ * device scratch of 4*N bytes for the column maxima and an event; a call on
+ * another stream than the same thread's previous call first waits until the
+ * device is idle.
  */
 sq_status sq_smooth_fold_weights(const void *w_f16, int64_t K, int64_t N, int64_t ldw,
                                  const float *act_absmax, float alpha, const float *smooth_in,

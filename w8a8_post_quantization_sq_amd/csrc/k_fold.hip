@@ -9,15 +9,15 @@
 // key machinery, Eq. 4 at alpha = 1/2).
 //
 // Kernels, in launch order:
-//   k_row_smooth      aw_j = max_n |W[j][n]| (one wave per row), then s_j and
-//                     1/s_j in float; zeroes w_scale
-//   (a copy of s to the host, which checks s and 1/s while the rest runs)
-//   k_fold_colabsmax  amax_n = max_j |float(W[j][n]) * s_j|  (into w_scale, atomics)
+//   k_row_smooth      aw_j = max_n |W[j][n]| (four rows per wave), then s_j and
+//                     1/s_j in float, s also into a host buffer (the host checks
+//                     s and 1/s while the rest runs); zeroes the amax scratch
+//   k_fold_colabsmax  amax_n = max_j |float(W[j][n]) * s_j|  (atomics)
 //   k_fold_quant      Wq[n][j] = clamp(rint((W*s) * (127/amax_n)), +-127), transposed
 //                     through LDS and written as packed 16 x 64-byte fragments
 //                     (the operand order of the int8 matrix instruction), with
-//                     the padding rows and windows written as zero
-//   k_fold_finalize   w_scale[n] = amax_n / 127
+//                     the padding rows and windows written as zero; and
+//                     w_scale[n] = amax_n / 127
 #include <math.h>
 
 #include "sq_device.h"
@@ -33,8 +33,8 @@ namespace sq {
 // 0..RS_ROWS-1 then form the factors of the wave's rows side by side: a
 // statistic that is NaN, infinite or negative (or such a given factor) yields
 // s = NaN; range problems (s or 1/s zero, infinite, subnormal) are left as
-// they come.  The host checks both.  The workgroups also clear w_scale, the
-// column maxima's accumulator.
+// they come.  The host checks both, on the copy of s the kernel writes into a
+// host buffer.  The workgroups also clear the column maxima's accumulator.
 constexpr int RS_ROWS = 4;
 constexpr int RS_U = 4;
 
@@ -55,9 +55,10 @@ __device__ __forceinline__ double pow_ratio(float a, float aw, double alpha) {
 __global__ void __launch_bounds__(64)
 k_row_smooth(const uint16_t *__restrict__ w, int64_t K, int64_t N, int64_t ldw,
              const float *__restrict__ ax, const float *__restrict__ smooth_in, double alpha,
-             float *__restrict__ s_out, float *__restrict__ inv_out, float *__restrict__ w_scale) {
+             float *__restrict__ s_out, float *__restrict__ inv_out, float *__restrict__ s_host,
+             float *__restrict__ amax) {
     for (int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x; i < N; i += (int64_t)gridDim.x * 64)
-        w_scale[i] = 0.0f;
+        amax[i] = 0.0f;
     const int lane = threadIdx.x;
     const int64_t j0 = (int64_t)blockIdx.x * RS_ROWS;
     const int64_t nfull = N & ~(int64_t)7;          // columns in whole octets
@@ -128,13 +129,14 @@ k_row_smooth(const uint16_t *__restrict__ w, int64_t K, int64_t N, int64_t ldw,
     }
     s_out[j] = s;
     inv_out[j] = 1.0f / s;   // IEEE-correct float division
+    if (s_host) s_host[j] = s;   // for the host's check, without a copy kernel
 }
 
 hipError_t launch_row_smooth(const uint16_t *w, int64_t K, int64_t N, int64_t ldw,
                              const float *ax, const float *smooth_in, float alpha, float *s_out,
-                             float *inv_out, float *w_scale, hipStream_t st) {
+                             float *inv_out, float *s_host, float *amax, hipStream_t st) {
     k_row_smooth<<<dim3((unsigned)((K + RS_ROWS - 1) / RS_ROWS)), dim3(64), 0, st>>>(
-        w, K, N, ldw, ax, smooth_in, (double)alpha, s_out, inv_out, w_scale);
+        w, K, N, ldw, ax, smooth_in, (double)alpha, s_out, inv_out, s_host, amax);
     return hipGetLastError();
 }
 
@@ -257,7 +259,7 @@ __device__ __forceinline__ int fq_word(int row, int word) {   // word: 4-byte co
 __global__ void __launch_bounds__(256)
 k_fold_quant(const uint16_t *__restrict__ w, int64_t K, int64_t N, int64_t ldw,
              const float *__restrict__ s, const float *__restrict__ amax,
-             int8_t *__restrict__ wq) {
+             int8_t *__restrict__ wq, float *__restrict__ w_scale) {
     __shared__ __align__(16) uint32_t tile[FQ_TN * FQ_TK / 4];
     const int64_t n0 = (int64_t)blockIdx.x * FQ_TN;
     const int64_t k0 = (int64_t)blockIdx.y * FQ_TK;
@@ -284,6 +286,8 @@ k_fold_quant(const uint16_t *__restrict__ w, int64_t K, int64_t N, int64_t ldw,
     // the 8 quotients of its octet from the lanes that made them
     const float al = n0 + lane < N ? amax[n0 + lane] : 0.0f;
     const float rl = al > 0.0f ? 127.0f / al : 0.0f;
+    // the first tile row of each column block also writes the scales
+    if (blockIdx.y == 0 && threadIdx.x < 64 && n0 + lane < N) w_scale[n0 + lane] = al / 127.0f;
     float r[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) r[c] = __shfl(rl, oct * 8 + c, 64);
@@ -341,22 +345,9 @@ k_fold_quant(const uint16_t *__restrict__ w, int64_t K, int64_t N, int64_t ldw,
 }
 
 hipError_t launch_fold_quant(const uint16_t *w, int64_t K, int64_t N, int64_t ldw, const float *s,
-                             const float *amax, int8_t *wq, hipStream_t st) {
+                             const float *amax, int8_t *wq, float *w_scale, hipStream_t st) {
     const dim3 grid((unsigned)((N + FQ_TN - 1) / FQ_TN), (unsigned)((K + FQ_TK - 1) / FQ_TK));
-    k_fold_quant<<<grid, dim3(256), 0, st>>>(w, K, N, ldw, s, amax, wq);
-    return hipGetLastError();
-}
-
-// ---- w_scale[n] = amax_n / 127 -----------------------------------------------------
-
-__global__ void __launch_bounds__(256) k_fold_finalize(float *__restrict__ w_scale, int64_t N) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < N) w_scale[i] = w_scale[i] / 127.0f;
-}
-
-hipError_t launch_fold_finalize(float *w_scale, int64_t N, hipStream_t st) {
-    if (N <= 0) return hipSuccess;
-    k_fold_finalize<<<dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st>>>(w_scale, N);
+    k_fold_quant<<<grid, dim3(256), 0, st>>>(w, K, N, ldw, s, amax, wq, w_scale);
     return hipGetLastError();
 }
 

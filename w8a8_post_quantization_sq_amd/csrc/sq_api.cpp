@@ -2,7 +2,9 @@
 // the caller's stream.  Every check runs before the first HIP call, so a call
 // rejected for its arguments has no side effects.  The only host-side data
 // work is the fold's check of the smoothing factors it has just computed,
-// which overlaps the rest of the fold on the device.
+// which overlaps the rest of the fold on the device.  The fold keeps a little
+// state per (thread, device): a host buffer for the factors and a device
+// scratch for the column maxima.
 #include <math.h>
 #include <stdint.h>
 
@@ -26,23 +28,33 @@ inline sq_status hip_status(hipError_t e) { return e == hipSuccess ? SQ_OK : SQ_
 // K: 16 <= K <= SQ_MAX_K, K % 16 == 0 (int8 rows are whole 16-byte chunks).
 inline bool k_ok(int64_t K) { return K >= 16 && K <= SQ_MAX_K && (K % 16) == 0; }
 
-// Host side of the fold's factor check: a pinned buffer that receives s and
-// an event that marks its arrival, one pair per (thread, device), made on
-// first use and kept until the process ends.  A thread's calls wait for their
-// copy before returning, so the next call may reuse the buffer.  (The copy
-// stays in line on the caller's stream: on a side stream, the cross-stream
-// event costs more than the copy it would hide.)
+// Per (thread, device) state of the fold, made on first use and kept until
+// the process ends:
+//   host, host_dev  a pinned, host-coherent buffer of K floats that the
+//                   factor kernel writes s into directly (no copy kernel);
+//   ready           marks the end of that kernel on the caller's stream;
+//   amax            device scratch of N floats: the column maxima, which the
+//                   code kernel turns into w_scale;
+//   last            the stream of the previous fold: a fold on another stream
+//                   first waits (on the host) until the device is idle, as the
+//                   old stream's kernels may still use amax.  (An event per
+//                   fold for this costs more on the device than the rare wait.)
+// A thread's calls wait for `ready` before returning, so the next call may
+// reuse the host buffer.
 struct Staging {
     float *host = nullptr;
+    float *host_dev = nullptr;
     int64_t cap = 0;
-    hipEvent_t ready = nullptr;    // s on the host
+    float *amax = nullptr;
+    int64_t amax_cap = 0;
+    hipEvent_t ready = nullptr;
+    hipStream_t last = nullptr;
+    bool used = false;
 };
 
-hipError_t make_staging(Staging &g) {
-    return hipEventCreateWithFlags(&g.ready, hipEventDisableTiming);
-}
-
-hipError_t staging_for(hipStream_t st, int64_t K, Staging **out) {
+// Makes (or grows) the state of the stream's device; the buffers are
+// allocated with that device current.
+hipError_t staging_for(hipStream_t st, int64_t K, int64_t N, Staging **out) {
     static thread_local std::vector<Staging> per_device;
     int cur = 0, dev = 0;
     hipError_t e = hipGetDevice(&cur);
@@ -55,29 +67,47 @@ hipError_t staging_for(hipStream_t st, int64_t K, Staging **out) {
     if (dev < 0) return hipErrorInvalidDevice;
     if ((int)per_device.size() <= dev) per_device.resize((size_t)dev + 1);
     Staging &g = per_device[(size_t)dev];
+    const bool switch_dev = dev != cur;
+    if (switch_dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
     if (!g.ready) {
-        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
-        Staging fresh;
-        e = make_staging(fresh);
-        if (dev != cur) {
-            const hipError_t e2 = hipSetDevice(cur);
-            if (e == hipSuccess) e = e2;
-        }
-        if (e != hipSuccess) return e;   // (a partly made set is left to the process end)
-        fresh.host = g.host;
-        fresh.cap = g.cap;
-        g = fresh;
+        hipEvent_t ev = nullptr;
+        e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e == hipSuccess) g.ready = ev;
     }
-    if (g.cap < K) {
-        if (g.host && (e = hipHostFree(g.host)) != hipSuccess) return e;
-        g.host = nullptr;
+    if (e == hipSuccess && g.cap < K) {
+        if (g.host) e = hipHostFree(g.host);
+        g.host = g.host_dev = nullptr;
         g.cap = 0;
-        void *p = nullptr;
-        e = hipHostMalloc(&p, (size_t)K * sizeof(float), hipHostMallocDefault);
-        if (e != hipSuccess) return e;
-        g.host = static_cast<float *>(p);
-        g.cap = K;
+        void *p = nullptr, *pd = nullptr;
+        if (e == hipSuccess) e = hipHostMalloc(&p, (size_t)K * sizeof(float), hipHostMallocCoherent);
+        if (e == hipSuccess) e = hipHostGetDevicePointer(&pd, p, 0);
+        if (e == hipSuccess) {
+            g.host = static_cast<float *>(p);
+            g.host_dev = static_cast<float *>(pd);
+            g.cap = K;
+        }
     }
+    // a fold on another stream than this thread's previous one: wait until the
+    // device is done with the scratch (the old stream may be gone, so the
+    // wait is for the whole device; this is the rare case)
+    if (e == hipSuccess && g.used && g.last != st) e = hipDeviceSynchronize();
+    if (e == hipSuccess && g.amax_cap < N) {
+        // (hipFree waits for the device, so a previous fold is done with it)
+        if (g.amax) e = hipFree(g.amax);
+        g.amax = nullptr;
+        g.amax_cap = 0;
+        void *p = nullptr;
+        if (e == hipSuccess) e = hipMalloc(&p, (size_t)N * sizeof(float));
+        if (e == hipSuccess) {
+            g.amax = static_cast<float *>(p);
+            g.amax_cap = N;
+        }
+    }
+    if (switch_dev) {
+        const hipError_t e2 = hipSetDevice(cur);
+        if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
     *out = &g;
     return hipSuccess;
 }
@@ -134,26 +164,23 @@ SQ_API sq_status sq_smooth_fold_weights(const void *w_f16, int64_t K, int64_t N,
     const hipStream_t st = as_stream(stream);
     const uint16_t *w = static_cast<const uint16_t *>(w_f16);
     Staging *g = nullptr;
-    hipError_t e = staging_for(st, K, &g);
+    hipError_t e = staging_for(st, K, N, &g);
     if (e != hipSuccess) return SQ_ERR_HIP;
-    // Everything is queued before the one wait: s goes to the host right after
-    // it is formed, and the column maxima and the codes follow on the stream
-    // while the host waits for it.  With N == 0 no row is read (aw = 0).
+    // Everything is queued before the one wait: the factor kernel writes s
+    // straight to the host buffer, and the column maxima and the codes follow
+    // on the stream while the host waits for it.  With N == 0 no row is read
+    // (aw = 0).
     e = sq::launch_row_smooth(w, K, N, ldw, act_absmax, smooth_in, alpha, smooth_out,
-                              inv_smooth_out, w_scale, st);
-    if (e == hipSuccess)
-        e = hipMemcpyAsync(g->host, smooth_out, (size_t)K * sizeof(float), hipMemcpyDeviceToHost, st);
+                              inv_smooth_out, g->host_dev, g->amax, st);
+    if (e == hipSuccess) e = hipEventRecord(g->ready, st);
     if (e != hipSuccess) return SQ_ERR_HIP;
-    e = hipEventRecord(g->ready, st);
-    if (e != hipSuccess) {
-        (void)hipStreamSynchronize(st);   // the copy must land before the buffer is reused
-        return SQ_ERR_HIP;
-    }
     if (N > 0) {
-        e = sq::launch_fold_colabsmax(w, K, N, ldw, smooth_out, w_scale, st);
-        if (e == hipSuccess) e = sq::launch_fold_quant(w, K, N, ldw, smooth_out, w_scale, wq, st);
-        if (e == hipSuccess) e = sq::launch_fold_finalize(w_scale, N, st);
+        e = sq::launch_fold_colabsmax(w, K, N, ldw, smooth_out, g->amax, st);
+        if (e == hipSuccess)
+            e = sq::launch_fold_quant(w, K, N, ldw, smooth_out, g->amax, wq, w_scale, st);
     }
+    g->last = st;
+    g->used = true;
     const hipError_t ew = hipEventSynchronize(g->ready);
     if (e != hipSuccess || ew != hipSuccess) return SQ_ERR_HIP;
 

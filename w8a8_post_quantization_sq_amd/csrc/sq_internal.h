@@ -14,18 +14,20 @@ hipError_t launch_fill_f32(float *p, int64_t n, float v, hipStream_t st);
 hipError_t launch_calib_absmax(const uint16_t *x, int64_t T, int64_t K, int64_t ldx,
                                float *ax, int accumulate, hipStream_t st);
 
-// aw_j = max_n |W[j][n]| -> s_out[j] = s_j, inv_out[j] = 1/s_j; zeroes w_scale[0, N)
+// aw_j = max_n |W[j][n]| -> s_out[j] = s_j (also into s_host when not NULL,
+// a device-visible host buffer), inv_out[j] = 1/s_j; zeroes amax[0, N)
 hipError_t launch_row_smooth(const uint16_t *w, int64_t K, int64_t N, int64_t ldw,
                              const float *ax, const float *smooth_in, float alpha, float *s_out,
-                             float *inv_out, float *w_scale, hipStream_t st);
+                             float *inv_out, float *s_host, float *amax, hipStream_t st);
 
+// amax[n] = max(amax[n], max_j |float(W[j][n]) * s_j|)
 hipError_t launch_fold_colabsmax(const uint16_t *w, int64_t K, int64_t N, int64_t ldw,
                                  const float *s, float *amax, hipStream_t st);
 
+// packed codes of W * s against amax; w_scale[n] = amax[n] / 127
 hipError_t launch_fold_quant(const uint16_t *w, int64_t K, int64_t N, int64_t ldw,
-                             const float *s, const float *amax, int8_t *wq, hipStream_t st);
-
-hipError_t launch_fold_finalize(float *w_scale, int64_t N, hipStream_t st);
+                             const float *s, const float *amax, int8_t *wq, float *w_scale,
+                             hipStream_t st);
 
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                             const float *inv_s, int8_t *xq, float *x_scale, hipStream_t st);
