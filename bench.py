@@ -13,7 +13,7 @@ calibration on a separate 512-token draw.
 
 Printed: one JSON line with the whole-step throughput (2MNK per step / wall
 time), the product kernel against the int8 matrix-core roofline (its duration
-from HIP events around it on the library's stream, inside the timed steps),
+from HIP events around it on the library's stream, on every 10th timed step),
 the per-stage GPU times from a separate pass with events between the stages,
 the serving-time layer (A4 + A5/A6, the two calls a deployed layer makes per
 batch), and the CPU oracle timed on a bounded sample as a baseline.
@@ -103,11 +103,13 @@ def cpu_baseline(inp, wl, budget_s):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="qkv4096",
                     help="qkv4096 | down11008 | prefill8192x3 | tiny")
     ap.add_argument("--alpha", type=float, default=None)
+    ap.add_argument("--event-every", type=int, default=10,
+                    help="bracket the product kernel with HIP events on every n-th timed step")
     ap.add_argument("--stage-steps", type=int, default=20,
                     help="steps of the separate, untimed pass with an event between stages")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
@@ -188,18 +190,20 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
-    # Timed region: the only events in it bracket the product kernel (each
-    # event record adds a few microseconds of its own to the device timeline).
+    # Timed region: the only events in it bracket the product kernel, on every
+    # --event-every-th step (each event record adds ~3 us of its own to the
+    # device timeline, so bracketing every step would inflate the step time).
+    every = max(1, args.event_every)
     gemm_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-                   for _ in range(args.steps)]
+                   for _ in range(0, args.steps, every)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(gemm_ev=gemm_events[i])
+        step(gemm_ev=gemm_events[i // every] if i % every == 0 else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log(f"timed {args.steps} steps in {wall:.3f} s")
-    gemm_ms = sum(a.elapsed_time(b) for a, b in gemm_events) / args.steps
+    gemm_ms = sum(a.elapsed_time(b) for a, b in gemm_events) / len(gemm_events)
 
     # Per-stage breakdown, from a separate pass with an event between stages
     # (those events lengthen these steps a little; the headline is not taken here).
