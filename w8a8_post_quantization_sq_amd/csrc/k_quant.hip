@@ -20,13 +20,28 @@
 
 namespace sq {
 
-__device__ __forceinline__ void load8(const uint16_t *__restrict__ x, const float *__restrict__ inv_s,
-                                      int64_t c, float v[8], uint32_t &amax) {
-    const uint4 raw = *reinterpret_cast<const uint4 *>(x + c);
-    const float4 s0 = *reinterpret_cast<const float4 *>(inv_s + c);
-    const float4 s1 = *reinterpret_cast<const float4 *>(inv_s + c + 4);
-    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-    const uint32_t h[4] = {raw.x, raw.y, raw.z, raw.w};
+// One 8-channel chunk: the raw fp16 values and their 1/s factors, loaded
+// together; scale8 then forms x * inv_s and folds the magnitudes into amax.
+// Callers issue the loads of all their chunks before scaling any, so the
+// loads are in flight together (a load followed at once by its use makes
+// the compiler wait for each one in turn).
+struct Chunk {
+    uint4 raw;
+    float4 s0, s1;
+};
+
+__device__ __forceinline__ Chunk load8(const uint16_t *__restrict__ x,
+                                       const float *__restrict__ inv_s, int64_t c) {
+    Chunk ch;
+    ch.raw = *reinterpret_cast<const uint4 *>(x + c);
+    ch.s0 = *reinterpret_cast<const float4 *>(inv_s + c);
+    ch.s1 = *reinterpret_cast<const float4 *>(inv_s + c + 4);
+    return ch;
+}
+
+__device__ __forceinline__ void scale8(const Chunk &ch, float v[8], uint32_t &amax) {
+    const float sv[8] = {ch.s0.x, ch.s0.y, ch.s0.z, ch.s0.w, ch.s1.x, ch.s1.y, ch.s1.z, ch.s1.w};
+    const uint32_t h[4] = {ch.raw.x, ch.raw.y, ch.raw.z, ch.raw.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         v[2 * i] = h2f(h[i] & 0xffffu) * sv[2 * i];
@@ -100,10 +115,15 @@ k_quant_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
             const uint16_t *row = x + m * ldx;
             // 4 chunks per lane in flight at a time (the loop is latency-bound otherwise)
             for (int64_t c0 = (int64_t)lane * 8; c0 < K; c0 += 4 * 512) {
-                float v[4][8];
+                Chunk ch[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    if (c0 + u * 512 < K) load8(row, inv_s, c0 + u * 512, v[u], amax);
+                    if (c0 + u * 512 < K) ch[u] = load8(row, inv_s, c0 + u * 512);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    float v[8];
+                    if (c0 + u * 512 < K) scale8(ch[u], v, amax);
+                }
             }
         }
         amax = wave_max_u32(amax);
@@ -129,13 +149,23 @@ k_quant_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
     for (int64_t p0 = threadIdx.x; p0 < pieces; p0 += 4 * 512) {
         float v[4][16];
         uint32_t dummy = 0;
+        Chunk ch[4][2];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {   // all loads of 4 pieces first
             const int64_t p = p0 + u * 512;
             const int64_t k = (p >> 5) * 64 + ((p >> 3) & 3) * 16;
             if (!skip && p < pieces && k < K) {
-                load8(row, inv_s, k, &v[u][0], dummy);
-                load8(row, inv_s, k + 8, &v[u][8], dummy);
+                ch[u][0] = load8(row, inv_s, k);
+                ch[u][1] = load8(row, inv_s, k + 8);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t p = p0 + u * 512;
+            const int64_t k = (p >> 5) * 64 + ((p >> 3) & 3) * 16;
+            if (!skip && p < pieces && k < K) {
+                scale8(ch[u][0], &v[u][0], dummy);
+                scale8(ch[u][1], &v[u][8], dummy);
             }
         }
 #pragma unroll
@@ -182,10 +212,16 @@ k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t l
     const uint16_t *row = x + (real ? m : 0) * ldx;
     float v[CPL][8];
     uint32_t amax = 0;
+    Chunk ch[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {   // every load of the row first
+        const int64_t k = ((int64_t)(c * 2 + h) * 64 + lane) * 8;
+        if (real && k < K) ch[c] = load8(row, inv_s, k);
+    }
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
         const int64_t k = ((int64_t)(c * 2 + h) * 64 + lane) * 8;
-        if (real && k < K) load8(row, inv_s, k, v[c], amax);
+        if (real && k < K) scale8(ch[c], v[c], amax);
     }
     amax = wave_max_u32(amax);
     if (lane == 0) s_max[wave] = amax;
