@@ -316,7 +316,10 @@ def test_quant_ties_and_degenerate_rows(sq, dev, orc):
 
 # ---- A5 + A6 the product -----------------------------------------------------------------
 
-GEMM_SHAPES = [(1, 1, 16), (3, 5, 48), (17, 100, 80), (100, 200, 64), (128, 128, 4096),
+# token counts 1..64 run the decode kernel (1, 2, 3 or 4 activation row blocks;
+# non-temporal weight loads up to 2 of them), 65 and up the tile kernel
+GEMM_SHAPES = [(1, 1, 16), (3, 5, 48), (17, 100, 80), (40, 100, 320), (49, 1000, 1088),
+               (64, 70, 4096), (65, 33, 64), (100, 200, 64), (128, 128, 4096),
                (130, 129, 1040), (256, 384, 2048), (1, 28672, 128), (16, 300, 8192), (513, 77, 112)]
 
 
