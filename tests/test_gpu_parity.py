@@ -194,7 +194,7 @@ def test_fold_given_factors_and_consumer_slices(sq, dev, orc):
 
 
 @pytest.mark.parametrize("K,N,ldw", [(16, 1, 8), (48, 13, 16), (272, 100, 104), (528, 64, 64),
-                                     (1040, 520, 520)])
+                                     (1040, 520, 520), (272, 4093, 4096), (64, 4097, 4104)])
 def test_fold_ragged_and_strided(sq, dev, orc, K, N, ldw):
     w = W.random_f16(300 + N, K, ldw, 0.05)
     ax = orc.calibrate_absmax(W.random_f16(301, 20, K, 3.0))
@@ -206,6 +206,21 @@ def test_fold_ragged_and_strided(sq, dev, orc, K, N, ldw):
     g = H(f.wq)
     assert np.array_equal(unpack(g, N, K), wq) and bits_equal(H(f.w_scale), wsc)
     assert padding_is_zero(g, N, K)
+
+
+def test_fold_sequence_reuses_scratch(sq, dev, orc):
+    """Folds of different widths in a row (one pass over W up to 4096 output
+    channels, two beyond): the column-maxima scratch is reused, grown and
+    cleared between them, and every fold still matches the oracle."""
+    for i, (K, N) in enumerate([(272, 520), (272, 96), (1040, 1000), (64, 4200), (272, 3000),
+                                (272, 3000)]):
+        w = W.random_f16(1300 + i, K, N, 0.05)
+        ax = orc.calibrate_absmax(W.random_f16(1400 + i, 24, K, 3.0))
+        f = sq.fold(T(w, dev), T(ax, dev), 0.5)
+        s_, _, _ = orc.smoothing_factors(ax, orc.row_absmax(w), 0.5)
+        wq, wsc = orc.fold_quant_weights(w, s_)
+        assert np.array_equal(unpack(H(f.wq), N, K), wq), (K, N)
+        assert bits_equal(H(f.w_scale), wsc), (K, N)
 
 
 def test_fold_degenerate_channels(sq, dev, orc):
