@@ -1,0 +1,119 @@
+"""Quality measures of the smoothed W8A8 layer, for the alpha sweep.
+
+TEST INFRASTRUCTURE ONLY (like the rest of ``oracle``): the tests use these
+to score the layer; the product library never imports them.
+
+What is measured, and where the pages speak of it:
+  * layer error ||Y_q - XW||_F^2 / ||XW||_F^2 -- the layer-wise squared
+    Frobenius quantization error ([P4] core discovery);
+  * quantization difficulty -- the standard deviation of the channel
+    magnitudes ([P4] key machinery: the secondary device), taken for the
+    activations X S^-1 (magnitude of input channel j = max over tokens) and
+    for the weights S W (magnitude of input channel j = max over outputs),
+    the axis along which smoothing moves the difficulty ([P1] para. 2);
+  * weight reconstruction error ||S W - dequant(Wq)||_F^2 / ||S W||_F^2 of
+    the per-output-channel int8 weights;
+  * activation clipping under a static per-tensor scale fixed on the
+    calibration tokens: the share of entries of X S^-1 above the largest
+    calibration magnitude (the per-token dynamic scale never clips);
+  * in-sample versus held-out calibration ([P4] skeptic critique, concrete
+    test): the factors from the evaluated tokens themselves or from a
+    separate calibration draw.
+Readings: the magnitudes use the same float32 products as the quantizer
+(x * inv_s_j, W * s_j); the statistics are taken in float64; the standard
+deviation is the population one (divide by the channel count).
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+from . import (calibrate_absmax, dequant, fold_quant_weights, gemm_i32, matmul_fp64,
+               quant_act_per_token, row_absmax, smoothing_factors, to_f16)
+
+
+def scaled_activations(x: np.ndarray, inv_s: np.ndarray) -> np.ndarray:
+    """float32(x) * inv_s_j, one float32 product per entry (the quantizer's x~)."""
+    return x.astype(np.float32) * inv_s.astype(np.float32)[None, :]
+
+
+def scaled_weights(w: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """float32(W[j, n]) * s_j, one float32 product per entry (the fold's W~)."""
+    return w.astype(np.float32) * s.astype(np.float32)[:, None]
+
+
+def difficulty(magnitudes: np.ndarray) -> float:
+    """Population standard deviation of the channel magnitudes, in float64."""
+    m = np.asarray(magnitudes, np.float64)
+    return float(np.sqrt(np.mean((m - m.mean()) ** 2)))
+
+
+def activation_difficulty(x: np.ndarray, inv_s: np.ndarray) -> float:
+    return difficulty(np.abs(scaled_activations(x, inv_s)).max(axis=0))
+
+
+def weight_difficulty(w: np.ndarray, s: np.ndarray) -> float:
+    return difficulty(np.abs(scaled_weights(w, s)).max(axis=1))
+
+
+def weight_recon_error(w: np.ndarray, s: np.ndarray, wq: Optional[np.ndarray] = None,
+                       w_scale: Optional[np.ndarray] = None) -> float:
+    """||W~ - q * dw||_F^2 / ||W~||_F^2 with W~ = W * s, codes q[n][j] and
+    scales dw[n] (from the oracle's fold unless given)."""
+    if wq is None or w_scale is None:
+        wq, w_scale = fold_quant_weights(w, s)
+    wt = scaled_weights(w, s).astype(np.float64)
+    rec = (wq.astype(np.float64) * w_scale.astype(np.float64)[:, None]).T   # [K][N]
+    return float(np.sum((wt - rec) ** 2) / np.sum(wt ** 2))
+
+
+def static_clip_fraction(x: np.ndarray, x_cal: np.ndarray, inv_s: np.ndarray) -> float:
+    """Share of entries of x~ whose magnitude exceeds the largest magnitude of
+    the calibration tokens' x~ (one static scale for the whole tensor)."""
+    bound = np.abs(scaled_activations(x_cal, inv_s)).max()
+    return float(np.mean(np.abs(scaled_activations(x, inv_s)) > bound))
+
+
+def layer_error(y: np.ndarray, ref: np.ndarray) -> float:
+    """||y - ref||_F^2 / ||ref||_F^2 in float64."""
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.sum((y - ref) ** 2) / np.sum(ref ** 2))
+
+
+def factors(x_stat: np.ndarray, w: np.ndarray, alpha: Optional[float]):
+    """(s, inv_s) from the statistics of x_stat, or ones for alpha None (S = I)."""
+    K = w.shape[0]
+    if alpha is None:
+        one = np.ones(K, np.float32)
+        return one, one.copy()
+    s, inv, st = smoothing_factors(calibrate_absmax(x_stat), row_absmax(w), alpha)
+    assert st == 0
+    return s, inv
+
+
+def sweep(x: np.ndarray, x_cal: np.ndarray, w: np.ndarray, alphas: Sequence[Optional[float]],
+          rows: Optional[np.ndarray] = None) -> Dict[str, Dict[str, float]]:
+    """Every measure for each alpha (None: S = I), with held-out calibration
+    (x_cal) and in-sample calibration (x itself).  The layer error compares
+    the layer's fp16 output on the token rows `rows` (all if None) with the
+    float64 product XW."""
+    rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
+    ref = matmul_fp64(x[rows], w)
+    out: Dict[str, Dict[str, float]] = {}
+    for alpha in alphas:
+        for tag, stat in (("held_out", x_cal), ("in_sample", x)):
+            s, inv = factors(stat, w, alpha)
+            wq, wsc = fold_quant_weights(w, s)
+            xq, xsc = quant_act_per_token(x[rows], inv)
+            y = to_f16(dequant(gemm_i32(xq, wq), xsc, wsc))   # the layer's fp16 output
+            key = f"{'I' if alpha is None else alpha}/{tag}"
+            out[key] = {
+                "layer_error": layer_error(y, ref),
+                "weight_recon_error": weight_recon_error(w, s, wq, wsc),
+                "act_difficulty": activation_difficulty(x, inv),
+                "weight_difficulty": weight_difficulty(w, s),
+                "static_clip_fraction": static_clip_fraction(x, x_cal, inv),
+            }
+    return out
