@@ -39,6 +39,7 @@ _f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
 _i8p = np.ctypeslib.ndpointer(dtype=np.int8, flags="C_CONTIGUOUS")
 _i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
 _i64 = ctypes.c_int64
+_f16p1 = np.ctypeslib.ndpointer(dtype=np.uint16, ndim=1, flags="C_CONTIGUOUS")
 
 
 def lib():
@@ -65,6 +66,13 @@ def lib():
         L.oracle_gemm_i32.argtypes = [_i8p, _i8p, _i64, _i64, _i64, _i32p]
         L.oracle_dequant.restype = None
         L.oracle_dequant.argtypes = [_i32p, _f32p, _f32p, _i64, _i64, _f64p]
+        L.oracle_fold_norm_weight.restype = None
+        L.oracle_fold_norm_weight.argtypes = [_f16p1, _i64, _f32p, _f32p]
+        L.oracle_row_sum_squares.restype = ctypes.c_double
+        L.oracle_row_sum_squares.argtypes = [_f16p1, _i64]
+        L.oracle_rmsnorm_quant_per_token.restype = None
+        L.oracle_rmsnorm_quant_per_token.argtypes = [_f16p, _i64, _i64, _i64, _f32p,
+                                                     ctypes.c_float, _i8p, _f32p]
         L.oracle_layer.restype = None
         L.oracle_layer.argtypes = [_f16p, _i64, _i64, _i64, _f32p, _i8p, _f32p, _i64,
                                    _i8p, _f32p, _i32p, _f64p]
@@ -168,6 +176,35 @@ def layer_block(x: np.ndarray, inv_s: np.ndarray, wq: np.ndarray, w_scale: np.nd
     return y
 
 
+# ---- next row: S^-1 folded into the preceding RMS normalization (C) ---------
+
+def fold_norm_weight(gamma: np.ndarray, inv_s: np.ndarray) -> np.ndarray:
+    """g_j = float(gamma_j) * inv_s_j: the normalization's weight divided by the
+    smoothing factor, so that its output is already X S^-1 ([P1 para. 3])."""
+    gb = np.ascontiguousarray(np.asarray(gamma, np.float16)).view(np.uint16)
+    K = gb.shape[0]
+    g = np.empty(K, np.float32)
+    lib().oracle_fold_norm_weight(gb, K, np.ascontiguousarray(inv_s, np.float32), g)
+    return g
+
+
+def row_sum_squares(h_row: np.ndarray) -> float:
+    """sum_j h_j^2 of one fp16 row, exact and rounded once to double."""
+    hb = np.ascontiguousarray(np.asarray(h_row, np.float16)).view(np.uint16)
+    return float(lib().oracle_row_sum_squares(hb, hb.shape[0]))
+
+
+def rmsnorm_quant_per_token(h: np.ndarray, g: np.ndarray, eps: float):
+    """RMS normalization with the folded weight g and per-token int8
+    quantization in one step: Xq [M][K] int8 and x_scale [M]."""
+    M, K = h.shape
+    xq = np.empty((M, K), np.int8)
+    xs = np.empty(M, np.float32)
+    lib().oracle_rmsnorm_quant_per_token(_bits(h), M, K, K, np.ascontiguousarray(g, np.float32),
+                                         float(eps), xq, xs)
+    return xq, xs
+
+
 @dataclass
 class Chain:
     ax: np.ndarray
@@ -216,6 +253,14 @@ def smoothed_matmul_fp64(x: np.ndarray, w: np.ndarray, s: np.ndarray) -> np.ndar
     xs = np.asarray(x, np.float64) / s64[None, :]
     ws = np.asarray(w, np.float64) * s64[:, None]
     return xs @ ws
+
+
+def rmsnorm_fp64(h: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """The unfused normalization output h / sqrt(mean_j h^2 + eps) * gamma in
+    float64 (what the layer's X is before smoothing)."""
+    h64 = np.asarray(h, np.float64)
+    rstd = 1.0 / np.sqrt(np.mean(h64 * h64, axis=1) + float(eps))
+    return h64 * rstd[:, None] * np.asarray(gamma, np.float64)[None, :]
 
 
 def rel_fro(a: np.ndarray, b: np.ndarray) -> float:

@@ -257,3 +257,88 @@ void oracle_layer(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const fl
     oracle_gemm_i32(xq_tmp, wq, M, N, K, acc_tmp);
     oracle_dequant(acc_tmp, x_scale_tmp, w_scale, M, N, y);
 }
+
+/* ---- Next row: the division by s folded into the preceding RMS norm ----- */
+
+/* The normalization in front of the layer, root-mean-square form (no mean
+ * subtraction, no bias): for token m of the hidden state h,
+ *     xbar[m][j] = h[m][j] * rstd_m * gamma[j],
+ *     rstd_m     = 1 / sqrt((1/K) sum_j h[m][j]^2 + eps).
+ * [P1 para. 3] allows the inverse factors to be folded into the operation that
+ * precedes the layer, provided every consumer of its output receives the same
+ * compensation.  Here that fold is gamma_j -> gamma_j / s_j, applied as the
+ * float product g[j] = float(gamma[j]) * inv_s[j] (the same multiply by the
+ * stored reciprocal that A4 uses). */
+void oracle_fold_norm_weight(const uint16_t *gamma, int64_t K, const float *inv_s, float *g)
+{
+    for (int64_t j = 0; j < K; ++j)
+        g[j] = half_to_float(gamma[j]) * inv_s[j];
+}
+
+/* sum_j h[j]^2 over K fp16 values, computed exactly and rounded once to
+ * double.  |h| = i * 2^-24 for an integer i < 2^40 (i = m for subnormals,
+ * (1024 + m) * 2^(e-1) otherwise), so h^2 = i^2 * 2^-48 and the sum is an
+ * integer of at most 97 bits times 2^-48: it is summed in unsigned 128-bit
+ * integers, converted to double (round to nearest even) and scaled by 2^-48
+ * (exact).  A NaN element gives NaN, else an infinite one gives +inf. */
+double oracle_row_sum_squares(const uint16_t *h, int64_t K)
+{
+    unsigned __int128 acc = 0;
+    int nan = 0, inf = 0;
+    for (int64_t j = 0; j < K; ++j) {
+        int e = (h[j] >> 10) & 31;
+        int m = h[j] & 1023;
+        if (e == 31) {
+            if (m) nan = 1;
+            else inf = 1;
+            continue;
+        }
+        uint64_t i = e ? (uint64_t)(m + 1024) << (e - 1) : (uint64_t)m;
+        acc += (unsigned __int128)i * i;
+    }
+    if (nan) return NAN;
+    if (inf) return INFINITY;
+    return ldexp((double)acc, -48);
+}
+
+/* RMS normalization, the folded factors g = gamma / s and per-token int8
+ * quantization in one step.  For token m:
+ *     xt[j]      = float(h[m][j]) * g[j]            (float product)
+ *     a          = max_j |xt[j]|
+ *     Xq[m][j]   = clamp(rint(xt[j] * (127 / a)), -127, 127)
+ *     x_scale[m] = float(a * rstd_m / 127)          (double, rounded once)
+ * In exact arithmetic the codes of xbar / s = rstd_m * h * g do not depend on
+ * the positive per-token factor rstd_m (it scales the token's maximum by the
+ * same amount), so it enters the scale only.  rstd_m is taken in double from
+ * the exact sum of squares.  a == 0 gives scale 0 and codes 0; a row holding
+ * a non-finite xt gets scale NaN and codes 0 (as in A4). */
+void oracle_rmsnorm_quant_per_token(const uint16_t *h, int64_t M, int64_t K, int64_t ldh,
+                                    const float *g, float eps, int8_t *xq, float *x_scale)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *row = h + m * ldh;
+        float a = 0.0f;
+        int bad = 0;
+        for (int64_t j = 0; j < K; ++j) {
+            float xt = half_to_float(row[j]) * g[j];
+            if (!isfinite(xt)) { bad = 1; continue; }
+            if (fabsf(xt) > a) a = fabsf(xt);
+        }
+        if (bad || a == 0.0f) {
+            x_scale[m] = bad ? NAN : 0.0f;
+            for (int64_t j = 0; j < K; ++j) xq[m * K + j] = 0;
+            continue;
+        }
+        double ms = oracle_row_sum_squares(row, K) / (double)K;
+        double rstd = 1.0 / sqrt(ms + (double)eps);
+        x_scale[m] = (float)((double)a * rstd / 127.0);
+        float r = 127.0f / a;
+        for (int64_t j = 0; j < K; ++j) {
+            float xt = half_to_float(row[j]) * g[j];
+            float q = rintf(xt * r);
+            if (q > 127.0f) q = 127.0f;
+            if (q < -127.0f) q = -127.0f;
+            xq[m * K + j] = (int8_t)q;
+        }
+    }
+}

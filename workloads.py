@@ -167,3 +167,19 @@ def random_i8(seed: int, rows: int, cols: int, lo: int = -127, hi: int = 127) ->
 def random_scales(seed: int, n: int, lo: float = 1e-3, hi: float = 1e-1) -> np.ndarray:
     """Positive float32 scales, for direct GEMM epilogue tests."""
     return np.random.default_rng(seed).uniform(lo, hi, n).astype(np.float32)
+
+
+# ---- inputs of the normalization in front of the layer --------------------
+#
+# The fold of S^-1 into a preceding RMS normalization takes the hidden state h
+# (the normalization's input) instead of X.  Recipe: h is the workload's X
+# draw itself (same outlier channels and factors), the normalization weight
+# gamma is drawn from U(0.5, 1.5) by its own generator (seed + 1000, so the
+# draws above are unchanged) and rounded to float16; eps is the common 1e-5.
+NORM_EPS = 1e-5
+
+
+def norm_weight(wl: Workload) -> np.ndarray:
+    """float16 [K] weight of the normalization in front of workload wl."""
+    rng = np.random.default_rng(wl.seed + 1000)
+    return rng.uniform(0.5, 1.5, wl.K).astype(np.float16)
