@@ -16,7 +16,9 @@ time), the product kernel against the int8 matrix-core roofline (its duration
 from HIP events around it on the library's stream, on every 10th timed step),
 the per-stage GPU times from a separate pass with events between the stages,
 the serving-time layer (A4 + A5/A6, the two calls a deployed layer makes per
-batch), and the CPU oracle timed on a bounded sample as a baseline.
+batch), the fused RMS-norm + quantization that replaces A4 when 1/s is
+folded into the normalization in front of the layer (outside the step), and
+the CPU oracle timed on a bounded sample as a baseline.
 """
 import argparse
 import hashlib
@@ -112,6 +114,9 @@ def main():
                     help="bracket the product kernel with HIP events on every n-th timed step")
     ap.add_argument("--stage-steps", type=int, default=20,
                     help="steps of the separate, untimed pass with an event between stages")
+    ap.add_argument("--norm-launches", type=int, default=100,
+                    help="launches of the fused RMS-norm + quantization (and of the plain "
+                         "quantizer) timed between one pair of events (0: skip)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle layer work in the CPU baseline (0: skip)")
     ap.add_argument("--copy-kernel", type=int, default=0, metavar="MIB",
@@ -219,6 +224,47 @@ def main():
             per[n] += ev[j].elapsed_time(ev[j + 1])
     per = {n: v / max(1, args.stage_steps) for n, v in per.items()}    # ms per call
 
+    # The normalization in front of the layer with 1/s folded into its weight:
+    # the fused RMS-norm + quantization against the plain quantizer on the
+    # same batch, each timed as a run of launches between one event pair
+    # (the per-launch average includes the gaps between launches).
+    norm = None
+    if args.norm_launches > 0:
+        gamma = torch.from_numpy(workloads.norm_weight(wl)).to(dev)
+        g = torch.empty(K, dtype=torch.float32, device=dev)
+        if L.sq_fold_norm_weight(gamma.data_ptr(), K, p["inv"], g.data_ptr(), hs):
+            raise RuntimeError("sq_fold_norm_weight failed")
+        eps = workloads.NORM_EPS
+
+        def run(fused):
+            if fused:
+                return L.sq_rmsnorm_quant_per_token(p["x"], M, K, K, g.data_ptr(), eps, p["xq"],
+                                                    p["xsc"], hs)
+            return L.sq_quant_act_per_token(p["x"], M, K, K, p["inv"], p["xq"], p["xsc"], hs)
+
+        us = {}
+        for fused in (False, True, False, True):     # second round is the one kept
+            for _ in range(10):
+                run(fused)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.norm_launches):
+                if run(fused):
+                    raise RuntimeError("quantizer call failed")
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us[fused] = e0.elapsed_time(e1) * 1e3 / args.norm_launches
+        nbytes = 2 * M * K + M * K + 4 * M + 4 * K
+        gbs = nbytes / (us[True] * 1e-6) / 1e9
+        norm = {"what": "RMS norm with 1/s folded into its weight, fused with per-token quant "
+                        "(sq_rmsnorm_quant_per_token; replaces a separate norm pass)",
+                "us": round(us[True], 3), "plain_quant_us": round(us[False], 3),
+                "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4),
+                "per_launch": f"2MK (h) + MK (codes) + 4M + 4K = {nbytes} bytes",
+                "saved_bytes_per_batch": 4 * M * K}
+        log(f"fused norm + quant {us[True]:.2f} us, plain quant {us[False]:.2f} us")
+
     ops = 2.0 * M * N * K
     ms_step = wall * 1e3 / args.steps
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
@@ -255,6 +301,7 @@ def main():
                      "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                      "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": traffic,
                      "per_launch": f"2*M*N*K = {ops:.4g} int8 ops per launch"},
+        "norm_fold": norm,
         "cpu_baseline": None,
     }
     if args.cpu_budget > 0:

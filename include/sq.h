@@ -21,8 +21,8 @@
  *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
  *     Work is enqueued on that stream; only sq_smooth_fold_weights waits (for s).
  *   - Every argument is checked before any HIP call or any write: a call that
- *     returns an argument error (SQ_ERR_NULL, _SHAPE, _ALIGN, _ALPHA, _KIND)
- *     has no side effects.
+ *     returns an argument error (SQ_ERR_NULL, _SHAPE, _ALIGN, _ALPHA, _KIND,
+ *     _EPS) has no side effects.
  *   - Shape limits: sizes >= 0 (a zero token/output count is a no-op); K is a
  *     multiple of 16 with 16 <= K <= SQ_MAX_K, so that every int32 sum of K
  *     int8 products is exact; M, N, T < 2^31; ld >= the row length used.
@@ -65,7 +65,8 @@ typedef enum {
     SQ_ERR_RANGE = 6,      /* fold: a factor or its reciprocal is zero, infinite
                               or subnormal in float                              */
     SQ_ERR_HIP = 7,        /* the HIP runtime reported an error                   */
-    SQ_ERR_KIND = 8        /* unknown out_kind                                    */
+    SQ_ERR_KIND = 8,       /* unknown out_kind                                    */
+    SQ_ERR_EPS = 9         /* eps is negative, NaN or infinite                    */
 } sq_status;
 
 /* Output kinds of sq_w8a8_gemm. */
@@ -176,6 +177,53 @@ sq_status sq_smooth_fold_weights(const void *w_f16, int64_t K, int64_t N, int64_
 sq_status sq_quant_act_per_token(const void *x_f16, int64_t M, int64_t K, int64_t ldx,
                                  const float *inv_smooth, int8_t *xq, float *x_scale,
                                  void *stream);
+
+/*
+ * The division by s folded into the RMS normalization in front of the layer
+ * (offline part).  The inverse factors may be folded into the operation that
+ * produces the activation instead of being applied at run time ("Move
+ * activation scale ...", para. 3); for a root-mean-square normalization
+ *   xbar[m][j] = h[m][j] * rstd_m * gamma[j],  rstd_m = 1 / sqrt(mean_j h[m][j]^2 + eps)
+ * that means replacing its weight gamma by gamma / s:
+ *   gamma_out[j] = float(gamma[j]) * inv_smooth[j]
+ * Legal only when every consumer of the normalization's output is folded with
+ * this same s (same paragraph): fold them together as one K x (N1 + N2 + ...)
+ * matrix, or each with smooth_in = s.  A consumer that needs the unsmoothed
+ * activation cannot read the folded normalization's output.
+ *
+ *   gamma       fp16 [K], the normalization weight
+ *   inv_smooth  float [K] (inv_smooth_out of the fold)
+ *   gamma_out   float [K], written
+ * Asynchronous.
+ */
+sq_status sq_fold_norm_weight(const void *gamma_f16, int64_t K, const float *inv_smooth,
+                              float *gamma_out, void *stream);
+
+/*
+ * RMS normalization with the folded weight and per-token int8 quantization in
+ * one pass over the hidden state (serving time): the normalized activation
+ * X S^-1 is never written to memory.  Per token m, in float:
+ *   xt[j]      = float(h[m][j]) * gamma_folded[j]
+ *   xq[m][j]   = clamp(rint(xt[j] * (127 / max_j|xt[j]|)), -127, 127)
+ *   x_scale[m] = float(max_j|xt[j]| * rstd_m / 127), evaluated in double
+ * with rstd_m from the sum of squares of the row (summed in double; every
+ * square of an fp16 value is exact), so x_scale is within one float rounding
+ * of its value for the exact sum.  The codes do not depend on rstd_m (a
+ * positive per-token factor), so they are exactly sq_quant_act_per_token's
+ * codes of h with inv_smooth = gamma_folded.  An all-zero row gets scale 0
+ * and codes 0; a row with a non-finite xt gets scale NaN and codes 0.
+ *
+ *   h             fp16 [M][ldh], the normalization's input (hidden state)
+ *   gamma_folded  float [K] from sq_fold_norm_weight
+ *   eps           the normalization's epsilon, finite and >= 0 (else SQ_ERR_EPS)
+ *   xq            int8, packed (sq_packed_bytes(M, K) bytes), written, padding zero
+ *   x_scale       float [M], written
+ * The outputs go to sq_w8a8_gemm exactly as sq_quant_act_per_token's do.
+ * Asynchronous.
+ */
+sq_status sq_rmsnorm_quant_per_token(const void *h_f16, int64_t M, int64_t K, int64_t ldh,
+                                     const float *gamma_folded, float eps, int8_t *xq,
+                                     float *x_scale, void *stream);
 
 /*
  * The W8A8 product on int8 matrix cores with a fused dequantizing epilogue

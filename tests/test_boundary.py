@@ -52,11 +52,11 @@ def test_only_the_c_abi_is_exported(sq):
 
 
 def test_status_strings_and_version(sq):
-    for code in range(9):
+    for code in range(10):
         s = sq.status_str(code)
         assert s.startswith("SQ_")
     assert sq.status_str(99) == "unknown sq_status"
-    assert sq.lib().sq_version() == 10200
+    assert sq.lib().sq_version() == 10300
     assert sq.SQ_MAX_K * 128 * 128 < 2 ** 31 and sq.SQ_MAX_K % 16 == 0
 
 
@@ -64,7 +64,7 @@ def test_header_constants_match_binding(sq):
     text = open(HEADER).read()
     for name in ("SQ_OK", "SQ_ERR_NULL", "SQ_ERR_SHAPE", "SQ_ERR_ALIGN", "SQ_ERR_ALPHA",
                  "SQ_ERR_NONFINITE", "SQ_ERR_RANGE", "SQ_ERR_HIP", "SQ_ERR_KIND",
-                 "SQ_OUT_F16", "SQ_OUT_I32"):
+                 "SQ_ERR_EPS", "SQ_OUT_F16", "SQ_OUT_I32"):
         m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
         assert m and int(m.group(1)) == getattr(sq, name), name
     assert int(re.search(r"#define SQ_MAX_K (\d+)", text).group(1)) == sq.SQ_MAX_K
@@ -138,6 +138,52 @@ def test_fold_rejects(sq, kw, expect):
 ])
 def test_quant_rejects(sq, args, expect):
     assert sq.status_str(sq.lib().sq_quant_act_per_token(*args)).startswith(expect)
+
+
+# ---- normalization fold and fused normalization + quant ------------------------------
+
+@pytest.mark.parametrize("args,expect", [
+    ((None, 64, P, P, None), "SQ_ERR_NULL"),
+    ((P, 64, None, P, None), "SQ_ERR_NULL"),
+    ((P, 64, P, None, None), "SQ_ERR_NULL"),
+    ((P, 0, P, P, None), "SQ_ERR_SHAPE"),
+    ((P, 72, P, P, None), "SQ_ERR_SHAPE"),
+    ((P, 131072, P, P, None), "SQ_ERR_SHAPE"),
+    ((MIS, 64, P, P, None), "SQ_ERR_ALIGN"),
+    ((P, 64, MIS, P, None), "SQ_ERR_ALIGN"),
+    ((P, 64, P, MIS, None), "SQ_ERR_ALIGN"),
+])
+def test_fold_norm_weight_rejects(sq, args, expect):
+    assert sq.status_str(sq.lib().sq_fold_norm_weight(*args)).startswith(expect)
+
+
+def _nq(sq, h=P, M=4, K=64, ldh=64, g=P, eps=1e-5, xq=P, xs=P):
+    return sq.lib().sq_rmsnorm_quant_per_token(h, M, K, ldh, g, eps, xq, xs, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(g=None), "SQ_ERR_NULL"),
+    (dict(h=None), "SQ_ERR_NULL"),
+    (dict(xq=None), "SQ_ERR_NULL"),
+    (dict(xs=None), "SQ_ERR_NULL"),
+    (dict(M=-1), "SQ_ERR_SHAPE"),
+    (dict(K=24, ldh=24), "SQ_ERR_SHAPE"),
+    (dict(ldh=48), "SQ_ERR_SHAPE"),
+    (dict(eps=-1e-6), "SQ_ERR_EPS"),
+    (dict(eps=float("nan")), "SQ_ERR_EPS"),
+    (dict(eps=float("inf")), "SQ_ERR_EPS"),
+    (dict(h=MIS), "SQ_ERR_ALIGN"),
+    (dict(g=MIS), "SQ_ERR_ALIGN"),
+    (dict(xq=MIS), "SQ_ERR_ALIGN"),
+    (dict(ldh=68), "SQ_ERR_ALIGN"),
+])
+def test_rmsnorm_quant_rejects(sq, kw, expect):
+    assert sq.status_str(_nq(sq, **kw)).startswith(expect)
+
+
+def test_rmsnorm_quant_empty_is_noop(sq):
+    # M == 0 launches nothing (the fake pointers are never touched)
+    assert _nq(sq, M=0, h=None, xq=None, xs=None) == sq.SQ_OK
 
 
 # ---- gemm -------------------------------------------------------------------------

@@ -8,9 +8,11 @@ library, or without a GPU, the calls raise.
 
 Same-name calls (caller-allocated outputs, as in the C ABI):
     sq_calibrate_absmax, sq_smooth_fold_weights, sq_quant_act_per_token,
-    sq_w8a8_gemm, sq_packed_bytes, sq_pack_i8, sq_unpack_i8
+    sq_w8a8_gemm, sq_packed_bytes, sq_pack_i8, sq_unpack_i8,
+    sq_fold_norm_weight, sq_rmsnorm_quant_per_token
 Allocating helpers built on them:
-    calibrate, fold, quant, gemm, smoothed_linear, pack_i8, unpack_i8
+    calibrate, fold, quant, gemm, smoothed_linear, pack_i8, unpack_i8,
+    fold_norm_weight, rmsnorm_quant
 
 The int8 codes (xq, wq) travel as flat int8 tensors in the packed operand
 order the C ABI documents (16-row x 64-byte fragments of 1 KiB); their sizes
@@ -35,13 +37,14 @@ SQ_ERR_NONFINITE = 5
 SQ_ERR_RANGE = 6
 SQ_ERR_HIP = 7
 SQ_ERR_KIND = 8
+SQ_ERR_EPS = 9
 SQ_OUT_F16 = 0
 SQ_OUT_I32 = 1
 SQ_MAX_K = 131056
 
 EXPORTS = ("sq_status_str", "sq_version", "sq_packed_bytes", "sq_calibrate_absmax",
            "sq_smooth_fold_weights", "sq_quant_act_per_token", "sq_w8a8_gemm", "sq_pack_i8",
-           "sq_unpack_i8")
+           "sq_unpack_i8", "sq_fold_norm_weight", "sq_rmsnorm_quant_per_token")
 
 _LIB = None
 
@@ -80,6 +83,10 @@ def lib() -> ctypes.CDLL:
         L.sq_pack_i8.argtypes = [vp, i64, i64, i64, vp, vp]
         L.sq_unpack_i8.restype = ci
         L.sq_unpack_i8.argtypes = [vp, i64, i64, vp, i64, vp]
+        L.sq_fold_norm_weight.restype = ci
+        L.sq_fold_norm_weight.argtypes = [vp, i64, vp, vp, vp]
+        L.sq_rmsnorm_quant_per_token.restype = ci
+        L.sq_rmsnorm_quant_per_token.argtypes = [vp, i64, i64, i64, vp, f32, vp, vp, vp]
         _LIB = L
     return _LIB
 
@@ -211,6 +218,35 @@ def sq_w8a8_gemm(xq, x_scale, wq, w_scale, y, K: int, out_kind: int = SQ_OUT_F16
            "sq_w8a8_gemm")
 
 
+def sq_fold_norm_weight(gamma, inv_smooth, gamma_out, stream=None) -> None:
+    """gamma_out (float32 [K]) = float(gamma) * inv_smooth: the RMS
+    normalization's weight gamma (float16 [K]) with 1/s folded in."""
+    torch = _torch()
+    _need(gamma, torch.float16, "gamma", 1)
+    _need(inv_smooth, torch.float32, "inv_smooth", 1)
+    _need(gamma_out, torch.float32, "gamma_out", 1)
+    K = gamma.shape[0]
+    if inv_smooth.shape[0] < K or gamma_out.shape[0] < K:
+        raise ValueError("inv_smooth and gamma_out need K entries")
+    _check(lib().sq_fold_norm_weight(_ptr(gamma), K, _ptr(inv_smooth), _ptr(gamma_out),
+                                     _stream(stream, gamma.device)), "sq_fold_norm_weight")
+
+
+def sq_rmsnorm_quant_per_token(h, gamma_folded, eps: float, xq, x_scale, stream=None) -> None:
+    """xq (packed int8, packed_bytes(M, K)) and x_scale (float32 [M]) of the
+    RMS-normalized hidden state h (float16 [M][K]) with the folded weight."""
+    torch = _torch()
+    _need(h, torch.float16, "h", 2)
+    _need(gamma_folded, torch.float32, "gamma_folded", 1)
+    _need(x_scale, torch.float32, "x_scale", 1)
+    M, K = h.shape
+    _need_packed(xq, M, K, "xq")
+    _check(lib().sq_rmsnorm_quant_per_token(_ptr(h), M, K, _ld(h), _ptr(gamma_folded),
+                                            float(eps), _ptr(xq), _ptr(x_scale),
+                                            _stream(stream, h.device)),
+           "sq_rmsnorm_quant_per_token")
+
+
 def sq_pack_i8(src, dst, stream=None) -> None:
     """Row-major int8 codes src [rows][K] -> packed dst (padding zeroed)."""
     torch = _torch()
@@ -282,6 +318,24 @@ def gemm(xq, x_scale, wq, w_scale, M: int, N: int, K: int, out_kind: int = SQ_OU
     y = torch.empty((M, N), dtype=dt, device=xq.device)
     sq_w8a8_gemm(xq, x_scale, wq, w_scale, y, K, out_kind, stream=stream)
     return y
+
+
+def fold_norm_weight(gamma, inv_smooth, stream=None):
+    """Returns gamma / s as float32 [K]."""
+    torch = _torch()
+    out = torch.empty(gamma.shape[0], dtype=torch.float32, device=gamma.device)
+    sq_fold_norm_weight(gamma, inv_smooth, out, stream=stream)
+    return out
+
+
+def rmsnorm_quant(h, gamma_folded, eps: float, stream=None):
+    """Returns (packed xq, x_scale) of the normalized, smoothed hidden state."""
+    torch = _torch()
+    M, K = h.shape
+    xq = torch.empty(packed_bytes(M, K), dtype=torch.int8, device=h.device)
+    xs = torch.empty(M, dtype=torch.float32, device=h.device)
+    sq_rmsnorm_quant_per_token(h, gamma_folded, eps, xq, xs, stream=stream)
+    return xq, xs
 
 
 def pack_i8(codes, stream=None):

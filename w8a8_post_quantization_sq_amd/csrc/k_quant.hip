@@ -11,6 +11,18 @@
 // no fast-math), the products single float multiplies, so the codes are the
 // ones the plain definition gives.
 //
+// The same kernels also serve the normalization in front of the layer with
+// 1/s folded into its weight (the fold into the preceding operation that the
+// same paragraph allows): x is then the hidden state h, inv_s the folded
+// weight g = gamma / s, and the token's root-mean-square factor
+//   rstd = 1 / sqrt(sum_j h_j^2 / K + eps)
+// enters the scale only, scale = float(a * rstd / 127) in double: the codes of
+// rstd * h * g are those of h * g, since a positive per-token factor scales
+// the token's maximum alike.  Each lane sums the squares of its fp16 values,
+// which are exact in float (11-bit significands), in double; the row's sum is
+// reduced in double too, so it is within K * 2^-53 of the exact sum and the
+// scale within one float rounding of the exact-sum value.
+//
 // The codes are written in the packed operand order of the int8 matrix
 // instruction (16-row x 64-byte fragments of 1 KiB, lane order quarter-major,
 // row-minor), so 16 consecutive codes of a row are one 16-byte piece and the
@@ -39,13 +51,21 @@ __device__ __forceinline__ Chunk load8(const uint16_t *__restrict__ x,
     return ch;
 }
 
-__device__ __forceinline__ void scale8(const Chunk &ch, float v[8], uint32_t &amax) {
+// With NORM, also adds the chunk's squares (exact in float) to ss in double.
+template <bool NORM = false>
+__device__ __forceinline__ void scale8(const Chunk &ch, float v[8], uint32_t &amax,
+                                       double *ss = nullptr) {
     const float sv[8] = {ch.s0.x, ch.s0.y, ch.s0.z, ch.s0.w, ch.s1.x, ch.s1.y, ch.s1.z, ch.s1.w};
     const uint32_t h[4] = {ch.raw.x, ch.raw.y, ch.raw.z, ch.raw.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        v[2 * i] = h2f(h[i] & 0xffffu) * sv[2 * i];
-        v[2 * i + 1] = h2f(h[i] >> 16) * sv[2 * i + 1];
+        const float lo = h2f(h[i] & 0xffffu), hi = h2f(h[i] >> 16);
+        if (NORM) {
+            *ss += (double)(lo * lo);
+            *ss += (double)(hi * hi);
+        }
+        v[2 * i] = lo * sv[2 * i];
+        v[2 * i + 1] = hi * sv[2 * i + 1];
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -68,6 +88,12 @@ __device__ __forceinline__ uint2 quant8(const float v[8], float r, bool zero) {
     return make_uint2(lo, hi);
 }
 
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
 // Turns the row maximum into (scale, multiplier, all-zero-codes flag).
 __device__ __forceinline__ void row_params(uint32_t abits, float &scale, float &r, bool &zero) {
     if (abits >= 0x7f800000u) {          // a non-finite scaled value in the row
@@ -86,6 +112,15 @@ __device__ __forceinline__ void row_params(uint32_t abits, float &scale, float &
     }
 }
 
+// The normalized row's scale from its maximum and its sum of squares ss
+// (non-finite and zero maxima as in row_params).
+__device__ __forceinline__ float norm_scale(uint32_t abits, double ss, int64_t K, double eps) {
+    if (abits >= 0x7f800000u) return __builtin_nanf("");
+    if (abits == 0u) return 0.0f;
+    const double rstd = 1.0 / sqrt(ss / (double)K + eps);
+    return (float)((double)__uint_as_float(abits) * rstd / 127.0);
+}
+
 // Row-group kernel: a workgroup of 8 waves owns 8 consecutive token rows
 // (half a packed row block).
 //   pass 1: wave w streams row m0 + w once from HBM (16-byte loads) and
@@ -98,9 +133,10 @@ __device__ __forceinline__ void row_params(uint32_t abits, float &scale, float &
 // Rows past M and chunks past K are padding and get zero codes.
 constexpr int QR = 8;   // rows per workgroup
 
+template <bool NORM>
 __global__ void __launch_bounds__(512)
 k_quant_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
-             const float *__restrict__ inv_s, int8_t *__restrict__ xq,
+             const float *__restrict__ inv_s, double eps, int8_t *__restrict__ xq,
              float *__restrict__ x_scale) {
     __shared__ float s_r[QR];
     __shared__ int s_zero[QR];
@@ -111,6 +147,7 @@ k_quant_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
     {
         const int64_t m = m0 + wave;
         uint32_t amax = 0;
+        double ss = 0.0;
         if (m < M) {
             const uint16_t *row = x + m * ldx;
             // 4 chunks per lane in flight at a time (the loop is latency-bound otherwise)
@@ -122,14 +159,16 @@ k_quant_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     float v[8];
-                    if (c0 + u * 512 < K) scale8(ch[u], v, amax);
+                    if (c0 + u * 512 < K) scale8<NORM>(ch[u], v, amax, &ss);
                 }
             }
         }
         amax = wave_max_u32(amax);
+        if (NORM) ss = wave_sum_f64(ss);
         float scale, r;
         bool zero;
         row_params(amax, scale, r, zero);
+        if (NORM) scale = norm_scale(amax, ss, K, eps);
         if (lane == 0) {
             if (m < M) x_scale[m] = scale;
             s_r[wave] = r;
@@ -193,13 +232,14 @@ k_quant_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
 // shuffles, then the 2 waves of a row through LDS), quantizes, and writes its
 // codes into an LDS copy of the 8 rows; the group then leaves LDS as packed
 // 16-byte pieces, consecutive lanes on consecutive rows (128-byte runs).
-template <int CPL>
+template <int CPL, bool NORM>
 __global__ void __launch_bounds__(1024)
 k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
-                 const float *__restrict__ inv_s, int8_t *__restrict__ xq,
+                 const float *__restrict__ inv_s, double eps, int8_t *__restrict__ xq,
                  float *__restrict__ x_scale) {
     extern __shared__ __align__(16) int8_t codes[];     // [8][KW * 64]
     __shared__ uint32_t s_max[16];
+    __shared__ double s_ss[16];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;                   // 0..15
     const int r = wave >> 1;                             // row of the group
@@ -212,25 +252,38 @@ k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t l
     const uint16_t *row = x + (real ? m : 0) * ldx;
     float v[CPL][8];
     uint32_t amax = 0;
-    Chunk ch[CPL];
+    double ss = 0.0;
+    // Every load of the row first; with the sum of squares at 8 chunks per
+    // lane that needs more than the 128 registers a lane has here, so there
+    // the loads go in two rounds of 4.
+    constexpr int ROUND = (NORM && CPL == 8) ? 4 : CPL;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {   // every load of the row first
-        const int64_t k = ((int64_t)(c * 2 + h) * 64 + lane) * 8;
-        if (real && k < K) ch[c] = load8(row, inv_s, k);
-    }
+    for (int c0 = 0; c0 < CPL; c0 += ROUND) {
+        Chunk ch[ROUND];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        const int64_t k = ((int64_t)(c * 2 + h) * 64 + lane) * 8;
-        if (real && k < K) scale8(ch[c], v[c], amax);
+        for (int c = 0; c < ROUND; ++c) {
+            const int64_t k = ((int64_t)((c0 + c) * 2 + h) * 64 + lane) * 8;
+            if (real && k < K) ch[c] = load8(row, inv_s, k);
+        }
+#pragma unroll
+        for (int c = 0; c < ROUND; ++c) {
+            const int64_t k = ((int64_t)((c0 + c) * 2 + h) * 64 + lane) * 8;
+            if (real && k < K) scale8<NORM>(ch[c], v[c0 + c], amax, &ss);
+        }
     }
     amax = wave_max_u32(amax);
-    if (lane == 0) s_max[wave] = amax;
+    if (NORM) ss = wave_sum_f64(ss);
+    if (lane == 0) {
+        s_max[wave] = amax;
+        if (NORM) s_ss[wave] = ss;
+    }
     __syncthreads();
     const uint32_t a0 = s_max[2 * r], a1 = s_max[2 * r + 1];
+    const uint32_t arow = a0 > a1 ? a0 : a1;
     float scale, rr;
     bool zero;
-    row_params(a0 > a1 ? a0 : a1, scale, rr, zero);
-    if (real && h == 0 && lane == 0) x_scale[m] = scale;
+    row_params(arow, scale, rr, zero);
+    if (!NORM && real && h == 0 && lane == 0) x_scale[m] = scale;
     zero = zero || !real;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
@@ -239,6 +292,9 @@ k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t l
             *reinterpret_cast<uint2 *>(codes + r * pitch + k) =
                 (k < K) ? quant8(v[c], rr, zero) : make_uint2(0u, 0u);
     }
+    // the normalized scale once the row's values are no longer held
+    if (NORM && real && h == 0 && lane == 0)
+        x_scale[m] = norm_scale(arow, s_ss[2 * r] + s_ss[2 * r + 1], K, eps);
     __syncthreads();
     const int64_t rb = m0 >> 4;
     const int half = (int)(m0 & 15);
@@ -255,21 +311,64 @@ k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t l
     }
 }
 
-hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
-                            const float *inv_s, int8_t *xq, float *x_scale, hipStream_t st) {
+template <bool NORM>
+hipError_t launch_rows(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const float *inv_s,
+                       double eps, int8_t *xq, float *x_scale, hipStream_t st) {
     if (M <= 0) return hipSuccess;
     // every row of the padded row blocks, 8 rows per workgroup
     const int64_t groups = (M + 15) / 16 * 2;
     const int64_t cpl = (K + 1023) / 1024;        // chunks of 8 per lane, 2 waves per row
     const size_t lds = (size_t)QR * ((K + 63) / 64) * 64;
     const dim3 g((unsigned)groups);
-#define SQ_QR(C) k_quant_rows_reg<C><<<g, dim3(1024), lds, st>>>(x, M, K, ldx, inv_s, xq, x_scale)
+#define SQ_QR(C) \
+    k_quant_rows_reg<C, NORM><<<g, dim3(1024), lds, st>>>(x, M, K, ldx, inv_s, eps, xq, x_scale)
     if (cpl <= 1) SQ_QR(1);
     else if (cpl <= 2) SQ_QR(2);
     else if (cpl <= 4) SQ_QR(4);
-    else if (cpl <= 8) SQ_QR(8);     // up to 8192 channels: 100 VGPRs, 64 KiB LDS
-    else k_quant_rows<<<g, dim3(512), 0, st>>>(x, M, K, ldx, inv_s, xq, x_scale);
+    else if (cpl <= 8) SQ_QR(8);     // up to 8192 channels: 64 KiB LDS
+    else k_quant_rows<NORM><<<g, dim3(512), 0, st>>>(x, M, K, ldx, inv_s, eps, xq, x_scale);
 #undef SQ_QR
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                            const float *inv_s, int8_t *xq, float *x_scale, hipStream_t st) {
+    return launch_rows<false>(x, M, K, ldx, inv_s, 0.0, xq, x_scale, st);
+}
+
+hipError_t launch_rmsnorm_quant(const uint16_t *h, int64_t M, int64_t K, int64_t ldh,
+                                const float *g, float eps, int8_t *xq, float *x_scale,
+                                hipStream_t st) {
+    return launch_rows<true>(h, M, K, ldh, g, (double)eps, xq, x_scale, st);
+}
+
+// g[j] = float(gamma[j]) * inv_s[j], 8 channels per thread (K % 16 == 0).
+__global__ void __launch_bounds__(256)
+k_fold_norm_weight(const uint16_t *__restrict__ gamma, int64_t K, const float *__restrict__ inv_s,
+                   float *__restrict__ g) {
+    const int64_t c = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (c >= K) return;
+    const uint4 raw = *reinterpret_cast<const uint4 *>(gamma + c);
+    const float4 s0 = *reinterpret_cast<const float4 *>(inv_s + c);
+    const float4 s1 = *reinterpret_cast<const float4 *>(inv_s + c + 4);
+    float4 o0, o1;
+    o0.x = h2f(raw.x & 0xffffu) * s0.x;
+    o0.y = h2f(raw.x >> 16) * s0.y;
+    o0.z = h2f(raw.y & 0xffffu) * s0.z;
+    o0.w = h2f(raw.y >> 16) * s0.w;
+    o1.x = h2f(raw.z & 0xffffu) * s1.x;
+    o1.y = h2f(raw.z >> 16) * s1.y;
+    o1.z = h2f(raw.w & 0xffffu) * s1.z;
+    o1.w = h2f(raw.w >> 16) * s1.w;
+    *reinterpret_cast<float4 *>(g + c) = o0;
+    *reinterpret_cast<float4 *>(g + c + 4) = o1;
+}
+
+hipError_t launch_fold_norm_weight(const uint16_t *gamma, int64_t K, const float *inv_s, float *g,
+                                   hipStream_t st) {
+    const int64_t threads = K / 8;
+    k_fold_norm_weight<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st>>>(gamma, K,
+                                                                                      inv_s, g);
     return hipGetLastError();
 }
 

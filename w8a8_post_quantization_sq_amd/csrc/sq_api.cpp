@@ -125,11 +125,12 @@ SQ_API const char *sq_status_str(int status) {
         case SQ_ERR_RANGE: return "SQ_ERR_RANGE: a factor or its reciprocal is zero, infinite or subnormal";
         case SQ_ERR_HIP: return "SQ_ERR_HIP: the HIP runtime reported an error";
         case SQ_ERR_KIND: return "SQ_ERR_KIND: unknown out_kind";
+        case SQ_ERR_EPS: return "SQ_ERR_EPS: eps must be finite and >= 0";
         default: return "unknown sq_status";
     }
 }
 
-SQ_API int sq_version(void) { return 10200; }
+SQ_API int sq_version(void) { return 10300; }
 
 SQ_API int64_t sq_packed_bytes(int64_t rows, int64_t K) {
     if (rows < 0 || rows >= kMaxDim || !k_ok(K)) return 0;
@@ -206,6 +207,27 @@ SQ_API sq_status sq_quant_act_per_token(const void *x_f16, int64_t M, int64_t K,
     if (M > 0 && (!aligned16(x_f16) || !aligned16(xq) || !aligned16(x_scale))) return SQ_ERR_ALIGN;
     return hip_status(sq::launch_quant_act(static_cast<const uint16_t *>(x_f16), M, K, ldx,
                                            inv_smooth, xq, x_scale, as_stream(stream)));
+}
+
+SQ_API sq_status sq_fold_norm_weight(const void *gamma_f16, int64_t K, const float *inv_smooth,
+                                     float *gamma_out, void *stream) {
+    if (!gamma_f16 || !inv_smooth || !gamma_out) return SQ_ERR_NULL;
+    if (!k_ok(K)) return SQ_ERR_SHAPE;
+    if (!aligned16(gamma_f16) || !aligned16(inv_smooth) || !aligned16(gamma_out)) return SQ_ERR_ALIGN;
+    return hip_status(sq::launch_fold_norm_weight(static_cast<const uint16_t *>(gamma_f16), K,
+                                                  inv_smooth, gamma_out, as_stream(stream)));
+}
+
+SQ_API sq_status sq_rmsnorm_quant_per_token(const void *h_f16, int64_t M, int64_t K, int64_t ldh,
+                                            const float *gamma_folded, float eps, int8_t *xq,
+                                            float *x_scale, void *stream) {
+    if (!gamma_folded || (M > 0 && (!h_f16 || !xq || !x_scale))) return SQ_ERR_NULL;
+    if (M < 0 || M >= kMaxDim || !k_ok(K) || ldh < K) return SQ_ERR_SHAPE;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return SQ_ERR_EPS;
+    if (!aligned16(gamma_folded) || (ldh % 8) != 0) return SQ_ERR_ALIGN;
+    if (M > 0 && (!aligned16(h_f16) || !aligned16(xq) || !aligned16(x_scale))) return SQ_ERR_ALIGN;
+    return hip_status(sq::launch_rmsnorm_quant(static_cast<const uint16_t *>(h_f16), M, K, ldh,
+                                               gamma_folded, eps, xq, x_scale, as_stream(stream)));
 }
 
 SQ_API sq_status sq_w8a8_gemm(const int8_t *xq, const float *x_scale, const int8_t *wq,

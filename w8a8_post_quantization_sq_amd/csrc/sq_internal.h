@@ -32,6 +32,16 @@ hipError_t launch_fold_quant(const uint16_t *w, int64_t K, int64_t N, int64_t ld
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                             const float *inv_s, int8_t *xq, float *x_scale, hipStream_t st);
 
+// the same quantizer on the hidden state h with the folded norm weight g:
+// the scale takes the token's rstd = 1 / sqrt(sum h^2 / K + eps)
+hipError_t launch_rmsnorm_quant(const uint16_t *h, int64_t M, int64_t K, int64_t ldh,
+                                const float *g, float eps, int8_t *xq, float *x_scale,
+                                hipStream_t st);
+
+// g[j] = float(gamma[j]) * inv_s[j]
+hipError_t launch_fold_norm_weight(const uint16_t *gamma, int64_t K, const float *inv_s, float *g,
+                                   hipStream_t st);
+
 hipError_t launch_pack_i8(const int8_t *src, int64_t rows, int64_t K, int64_t ld, int8_t *dst,
                           hipStream_t st);
 
