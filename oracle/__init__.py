@@ -73,6 +73,11 @@ def lib():
         L.oracle_rmsnorm_quant_per_token.restype = None
         L.oracle_rmsnorm_quant_per_token.argtypes = [_f16p, _i64, _i64, _i64, _f32p,
                                                      ctypes.c_float, _i8p, _f32p]
+        L.oracle_fwht_f32.restype = None
+        L.oracle_fwht_f32.argtypes = [_f32p, _i64]
+        L.oracle_quant4_rows.restype = None
+        L.oracle_quant4_rows.argtypes = [_f16p, _i64, _i64, _i64, _f32p, ctypes.c_int,
+                                         ctypes.c_float, _i8p, _f32p, _f32p]
         L.oracle_layer.restype = None
         L.oracle_layer.argtypes = [_f16p, _i64, _i64, _i64, _f32p, _i8p, _f32p, _i64,
                                    _i8p, _f32p, _i32p, _f64p]
@@ -203,6 +208,56 @@ def rmsnorm_quant_per_token(h: np.ndarray, g: np.ndarray, eps: float):
     lib().oracle_rmsnorm_quant_per_token(_bits(h), M, K, K, np.ascontiguousarray(g, np.float32),
                                          float(eps), xq, xs)
     return xq, xs
+
+
+# ---- next row: Smooth Rotation at 4 bits ([P4]) (C) ---------------------------
+
+def fwht_f32(v: np.ndarray) -> np.ndarray:
+    """v H_d (unnormalized Sylvester Hadamard) by the fast transform in float,
+    strides 1, 2, 4, ... in that order; returns a new float32 vector."""
+    out = np.array(v, np.float32, copy=True)
+    d = out.shape[0]
+    assert d & (d - 1) == 0, "d must be a power of two"
+    lib().oracle_fwht_f32(out, d)
+    return out
+
+
+def quant4_rows(x: np.ndarray, mult: np.ndarray, rotate: bool, post: float = 1.0):
+    """4-bit symmetric round-to-nearest quantization of the rows of x (fp16)
+    times mult, rotated by H first when asked: (codes int8 [M][K], scale [M])."""
+    M, K = x.shape
+    if rotate:
+        assert K & (K - 1) == 0
+    q = np.empty((M, K), np.int8)
+    sc = np.empty(M, np.float32)
+    work = np.empty(K, np.float32)
+    lib().oracle_quant4_rows(_bits(x), M, K, K, np.ascontiguousarray(mult, np.float32),
+                             1 if rotate else 0, float(post), q, sc, work)
+    return q, sc
+
+
+def quant4_act_per_token(x: np.ndarray, inv_s: np.ndarray, rotate: bool):
+    """A4 at 4 bits: per-token codes in [-7, 7] of (x * inv_s) H (or of x * inv_s)."""
+    return quant4_rows(x, inv_s, rotate, 1.0)
+
+
+def fold4_weights(w: np.ndarray, s: np.ndarray, rotate: bool):
+    """A3 at 4 bits: per-output-channel codes [N][K] in [-7, 7] of H (s * W)
+    (or of s * W); with the rotation the scale carries the 1/d of the two
+    unnormalized transforms."""
+    K = w.shape[0]
+    return quant4_rows(np.ascontiguousarray(w.T), s, rotate, 1.0 / K if rotate else 1.0)
+
+
+def hadamard_fp64(d: int) -> np.ndarray:
+    """Sylvester H_d in float64, H[i][j] = (-1)^popcount(i & j)."""
+    i = np.arange(d)
+    bits = np.bitwise_and(i[:, None], i[None, :])
+    pop = np.zeros_like(bits)
+    while bits.any():
+        pop += bits & 1
+        bits >>= 1
+    return np.where(pop % 2 == 0, 1.0, -1.0)
 
 
 @dataclass

@@ -117,3 +117,50 @@ def sweep(x: np.ndarray, x_cal: np.ndarray, w: np.ndarray, alphas: Sequence[Opti
                 "static_clip_fraction": static_clip_fraction(x, x_cal, inv),
             }
     return out
+
+
+# ---- Smooth Rotation at 4 bits: the comparison of [P4] core discovery ---------
+
+W4A4_METHODS = {            # name: (smoothing strength or None for S = I, rotate)
+    "original": (None, False),
+    "smooth": (0.5, False),
+    "rotate": (None, True),
+    "smooth_rotate": (0.5, True),
+}
+
+
+def w4a4_layer(x: np.ndarray, w: np.ndarray, s: np.ndarray, inv_s: np.ndarray, rotate: bool,
+               rows: np.ndarray):
+    """The 4-bit layer on token rows `rows`: per-token codes of (x / s) [H],
+    per-output-channel codes of [H] (s W), int32 product, fp16 output.
+    Returns (y16 as float64, activation scales)."""
+    from . import fold4_weights, quant4_act_per_token
+    xq, xs = quant4_act_per_token(x[rows], inv_s, rotate)
+    wq, ws = fold4_weights(w, s, rotate)
+    y = to_f16(dequant(gemm_i32(xq, wq), xs, ws)).astype(np.float64)
+    return y, xs
+
+
+def w4a4_compare(x: np.ndarray, x_cal: np.ndarray, w: np.ndarray,
+                 rows: Optional[np.ndarray] = None) -> Dict[str, Dict[str, float]]:
+    """Original, smoothing alone (alpha 1/2), rotation alone and smoothing then
+    rotation, each at 4 bits on both operands, with held-out (x_cal) and
+    in-sample (x) smoothing statistics ([P4] core discovery; skeptic's
+    concrete test).  Measures: layer error of the fp16 output against the
+    float64 XW, and the mean activation step size in the orthonormal
+    convention (scale / sqrt(d) when rotated, since the transform here is
+    unnormalized)."""
+    rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
+    ref = matmul_fp64(x[rows], w)
+    d = x.shape[1]
+    out: Dict[str, Dict[str, float]] = {}
+    for name, (alpha, rot) in W4A4_METHODS.items():
+        for tag, stat in (("held_out", x_cal), ("in_sample", x)):
+            if alpha is None and tag == "in_sample":
+                continue        # no statistics involved
+            s, inv = factors(stat, w, alpha)
+            y, xs = w4a4_layer(x, w, s, inv, rot, rows)
+            step = xs.astype(np.float64) / (np.sqrt(d) if rot else 1.0)
+            out[f"{name}/{tag}"] = {"layer_error": layer_error(y, ref),
+                                    "act_step": float(np.mean(step))}
+    return out

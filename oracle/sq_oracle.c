@@ -342,3 +342,72 @@ void oracle_rmsnorm_quant_per_token(const uint16_t *h, int64_t M, int64_t K, int
         }
     }
 }
+
+/* ---- Next row: Smooth Rotation, 4-bit ([P4]) ------------------------------ */
+
+/* [P4] key machinery: after the diagonal scale, activations and weights are
+ * multiplied by the same Hadamard matrix R with entries +-1/sqrt(d), which
+ * leaves the product unchanged (R is orthogonal and symmetric), and both
+ * tensors are quantized to 4 bits symmetrically with round-to-nearest ([P4]
+ * core discovery).
+ *
+ * Rotation.  The Sylvester Hadamard matrix H_d, H[i][j] = (-1)^popcount(i & j)
+ * for d a power of two, applied to a vector v as v H (its symmetric, so also
+ * H v) by the fast Walsh-Hadamard transform: for h = 1, 2, 4, ..., d/2 in this
+ * order, every pair (i, i + h) with (i & h) == 0 becomes (v_i + v_{i+h},
+ * v_i - v_{i+h}).  In float, one IEEE add or subtract per butterfly.  The
+ * transform is unnormalized (it computes v H, not v H / sqrt(d)): the two
+ * factors 1/sqrt(d) of activation and weight multiply to 1/d, a power of two,
+ * applied exactly in the weight scale below. */
+void oracle_fwht_f32(float *v, int64_t d)
+{
+    for (int64_t h = 1; h < d; h <<= 1)
+        for (int64_t i = 0; i < d; ++i)
+            if ((i & h) == 0) {
+                float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+}
+
+/* 4-bit symmetric round-to-nearest quantization of rows, optionally rotated.
+ * For each of the M rows of x (fp16, row stride ldx):
+ *   v[j]     = float(x[m][j]) * mult[j]          (float product)
+ *   v        = v H   if rotate                  (oracle_fwht_f32)
+ *   a        = max_j |v[j]|
+ *   q[m][j]  = clamp(rint(v[j] * (7 / a)), -7, 7)
+ *   scale[m] = (a / 7) * post                    (post a power of two: exact)
+ * a == 0 gives scale 0 and codes 0; a non-finite v gives scale NaN and codes
+ * 0.  Activations use mult = 1/s and post = 1 (one row per token); weights
+ * use the rows of W transposed (one per output channel), mult = s and
+ * post = 1/d when rotated (1 otherwise). */
+void oracle_quant4_rows(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                        const float *mult, int rotate, float post, int8_t *q, float *scale,
+                        float *work /* K floats */)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t j = 0; j < K; ++j)
+            work[j] = half_to_float(x[m * ldx + j]) * mult[j];
+        if (rotate)
+            oracle_fwht_f32(work, K);
+        float a = 0.0f;
+        int bad = 0;
+        for (int64_t j = 0; j < K; ++j) {
+            if (!isfinite(work[j])) { bad = 1; continue; }
+            if (fabsf(work[j]) > a) a = fabsf(work[j]);
+        }
+        if (bad || a == 0.0f) {
+            scale[m] = bad ? NAN : 0.0f;
+            for (int64_t j = 0; j < K; ++j) q[m * K + j] = 0;
+            continue;
+        }
+        float r = 7.0f / a;
+        scale[m] = (a / 7.0f) * post;
+        for (int64_t j = 0; j < K; ++j) {
+            float c = rintf(work[j] * r);
+            if (c > 7.0f) c = 7.0f;
+            if (c < -7.0f) c = -7.0f;
+            q[m * K + j] = (int8_t)c;
+        }
+    }
+}
