@@ -158,6 +158,17 @@ sq_status sq_smooth_fold_weights(const void *w_f16, int64_t K, int64_t N, int64_
                                  int8_t *wq, float *w_scale, void *stream);
 
 /*
+ * The smoothing factors alone, without the 8-bit fold: s and 1/s exactly as
+ * sq_smooth_fold_weights computes them (same formula, same checks, same
+ * per (thread, device) host buffer and one wait), for a caller that folds S
+ * into W in another form (the 4-bit calls below).  N == 0 takes every weight
+ * statistic as 0 (s_j = 1).  Data errors as in sq_smooth_fold_weights.
+ */
+sq_status sq_smoothing_factors(const void *w_f16, int64_t K, int64_t N, int64_t ldw,
+                               const float *act_absmax, float alpha, float *smooth_out,
+                               float *inv_smooth_out, void *stream);
+
+/*
  * Per-token dynamic activation quantization with the 1/s scaling fused in,
  * instead of a separate runtime scaling kernel ("Move activation scale ...",
  * para. 3).  Per token m, in float:
@@ -224,6 +235,60 @@ sq_status sq_fold_norm_weight(const void *gamma_f16, int64_t K, const float *inv
 sq_status sq_rmsnorm_quant_per_token(const void *h_f16, int64_t M, int64_t K, int64_t ldh,
                                      const float *gamma_folded, float eps, int8_t *xq,
                                      float *x_scale, void *stream);
+
+/*
+ * Smooth Rotation at 4 bits (Pith review of arXiv 2506.01967: key machinery,
+ * scale the channels and then multiply activations and weights by the same
+ * Hadamard matrix; core discovery, 4-bit symmetric round-to-nearest on both).
+ * The rotation R = H / sqrt(K) uses the Sylvester matrix
+ * H[i][j] = (-1)^popcount(i & j), so (X S^-1 R)(R S W) = X W.  The calls apply
+ * the unnormalized H by the fast transform in float (strides 1, 2, 4, ...,
+ * K/2 in that order, each butterfly (a + b, a - b)), and the two factors
+ * 1/sqrt(K) go into the weight scale as one exact 1/K.  With rotate == 0 the
+ * same calls quantize to 4 bits without the transform (smoothing alone, or
+ * S = I with smooth = ones: the other columns of the paper's comparison).
+ * Codes are 4-bit values in [-7, 7] stored one per byte in the packed int8
+ * layout, so sq_w8a8_gemm multiplies them unchanged (int32 sums exact).
+ * Shapes: 16 <= K <= 8192, K % 16 == 0, and K a power of two when rotated
+ * (SQ_ERR_SHAPE otherwise).
+ */
+
+/* Bytes of workspace sq_w4_fold_weights needs: 2 * K * N (0 when out of range). */
+int64_t sq_w4_workspace_bytes(int64_t K, int64_t N);
+
+/*
+ * Offline: per output channel n, v = H (s * W[:, n]) (or s * W[:, n]), then
+ *   w_scale[n] = (max_j |v_j| / 7) * (rotate ? 1/K : 1)
+ *   wq[n][j]   = clamp(rint(v_j * (7 / max_j |v_j|)), -7, 7)
+ * (products float(W) * s in float; a zero channel gets scale 0 and codes 0, a
+ * non-finite value scale NaN and codes 0).
+ *   w          fp16 [K][ldw]
+ *   smooth     float [K] (s from sq_smoothing_factors, or ones for S = I)
+ *   wq         packed int8, sq_packed_bytes(N, K) bytes, written, padding zero
+ *   w_scale    float [N], written
+ *   workspace  device buffer of sq_w4_workspace_bytes(K, N) bytes, 16-byte
+ *              aligned, caller-owned: W is transposed into it first; its
+ *              contents afterwards are unspecified
+ * Asynchronous.
+ */
+sq_status sq_w4_fold_weights(const void *w_f16, int64_t K, int64_t N, int64_t ldw,
+                             const float *smooth, int rotate, int8_t *wq, float *w_scale,
+                             void *workspace, void *stream);
+
+/*
+ * Serving time: per token m, v = (float(x[m][j]) * inv_smooth[j]) H (or
+ * without H), then
+ *   x_scale[m] = max_j |v_j| / 7
+ *   xq[m][j]   = clamp(rint(v_j * (7 / max_j |v_j|)), -7, 7)
+ * (all-zero token: scale 0, codes 0; a non-finite value: scale NaN, codes 0).
+ *   x        fp16 [M][ldx]
+ *   xq       packed int8, sq_packed_bytes(M, K) bytes, written, padding zero
+ *   x_scale  float [M], written
+ * Asynchronous.
+ */
+sq_status sq_a4_quant_per_token(const void *x_f16, int64_t M, int64_t K, int64_t ldx,
+                                const float *inv_smooth, int rotate, int8_t *xq, float *x_scale,
+                                void *stream);
 
 /*
  * The W8A8 product on int8 matrix cores with a fused dequantizing epilogue

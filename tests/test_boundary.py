@@ -56,7 +56,7 @@ def test_status_strings_and_version(sq):
         s = sq.status_str(code)
         assert s.startswith("SQ_")
     assert sq.status_str(99) == "unknown sq_status"
-    assert sq.lib().sq_version() == 10300
+    assert sq.lib().sq_version() == 10400
     assert sq.SQ_MAX_K * 128 * 128 < 2 ** 31 and sq.SQ_MAX_K % 16 == 0
 
 
@@ -184,6 +184,76 @@ def test_rmsnorm_quant_rejects(sq, kw, expect):
 def test_rmsnorm_quant_empty_is_noop(sq):
     # M == 0 launches nothing (the fake pointers are never touched)
     assert _nq(sq, M=0, h=None, xq=None, xs=None) == sq.SQ_OK
+
+
+# ---- 4-bit calls and the factors alone ---------------------------------------------
+
+def _a4(sq, x=P, M=4, K=64, ldx=64, inv=P, rot=1, xq=P, xs=P):
+    return sq.lib().sq_a4_quant_per_token(x, M, K, ldx, inv, rot, xq, xs, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(inv=None), "SQ_ERR_NULL"),
+    (dict(x=None), "SQ_ERR_NULL"),
+    (dict(xq=None), "SQ_ERR_NULL"),
+    (dict(K=48, ldx=48), "SQ_ERR_SHAPE"),            # rotated: K must be a power of two
+    (dict(K=16384, ldx=16384), "SQ_ERR_SHAPE"),      # above the register-resident 8192
+    (dict(K=8, ldx=8), "SQ_ERR_SHAPE"),
+    (dict(ldx=32), "SQ_ERR_SHAPE"),
+    (dict(M=-1), "SQ_ERR_SHAPE"),
+    (dict(x=MIS), "SQ_ERR_ALIGN"),
+    (dict(inv=MIS), "SQ_ERR_ALIGN"),
+    (dict(xs=MIS), "SQ_ERR_ALIGN"),
+    (dict(ldx=68), "SQ_ERR_ALIGN"),
+])
+def test_a4_quant_rejects(sq, kw, expect):
+    assert sq.status_str(_a4(sq, **kw)).startswith(expect)
+
+
+def test_a4_unrotated_takes_any_k_and_empty_is_noop(sq):
+    # unrotated, K = 48 passes the shape checks (it then fails on the alignment of MIS)
+    assert sq.status_str(_a4(sq, K=48, ldx=48, rot=0, x=MIS)).startswith("SQ_ERR_ALIGN")
+    assert _a4(sq, M=0, x=None, xq=None, xs=None) == sq.SQ_OK
+
+
+def _w4(sq, w=P, K=64, N=32, ldw=32, s=P, rot=1, wq=P, ws=P, work=Q):
+    return sq.lib().sq_w4_fold_weights(w, K, N, ldw, s, rot, wq, ws, work, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(s=None), "SQ_ERR_NULL"),
+    (dict(work=None), "SQ_ERR_NULL"),
+    (dict(wq=None), "SQ_ERR_NULL"),
+    (dict(K=96), "SQ_ERR_SHAPE"),
+    (dict(K=16384), "SQ_ERR_SHAPE"),
+    (dict(ldw=16), "SQ_ERR_SHAPE"),
+    (dict(N=-2), "SQ_ERR_SHAPE"),
+    (dict(work=MIS), "SQ_ERR_ALIGN"),
+    (dict(w=MIS), "SQ_ERR_ALIGN"),
+    (dict(ldw=36), "SQ_ERR_ALIGN"),
+])
+def test_w4_fold_rejects(sq, kw, expect):
+    assert sq.status_str(_w4(sq, **kw)).startswith(expect)
+
+
+def test_w4_workspace_bytes(sq):
+    assert sq.sq_w4_workspace_bytes(4096, 4096) == 2 * 4096 * 4096
+    assert sq.sq_w4_workspace_bytes(64, 0) == 0
+    assert sq.sq_w4_workspace_bytes(40, 8) == 0 and sq.sq_w4_workspace_bytes(64, -1) == 0
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((P, 64, 32, 32, None, 0.5, P, P, None), "SQ_ERR_NULL"),
+    ((P, 64, 32, 32, P, 0.5, None, P, None), "SQ_ERR_NULL"),
+    ((P, 64, 32, 16, P, 0.5, P, P, None), "SQ_ERR_SHAPE"),
+    ((P, 72, 32, 32, P, 0.5, P, P, None), "SQ_ERR_SHAPE"),
+    ((P, 64, 32, 32, P, 1.5, P, P, None), "SQ_ERR_ALPHA"),
+    ((P, 64, 32, 32, P, float("nan"), P, P, None), "SQ_ERR_ALPHA"),
+    ((MIS, 64, 32, 32, P, 0.5, P, P, None), "SQ_ERR_ALIGN"),
+    ((P, 64, 32, 32, MIS, 0.5, P, P, None), "SQ_ERR_ALIGN"),
+])
+def test_smoothing_factors_rejects(sq, args, expect):
+    assert sq.status_str(sq.lib().sq_smoothing_factors(*args)).startswith(expect)
 
 
 # ---- gemm -------------------------------------------------------------------------

@@ -9,10 +9,11 @@ library, or without a GPU, the calls raise.
 Same-name calls (caller-allocated outputs, as in the C ABI):
     sq_calibrate_absmax, sq_smooth_fold_weights, sq_quant_act_per_token,
     sq_w8a8_gemm, sq_packed_bytes, sq_pack_i8, sq_unpack_i8,
-    sq_fold_norm_weight, sq_rmsnorm_quant_per_token
+    sq_fold_norm_weight, sq_rmsnorm_quant_per_token, sq_smoothing_factors,
+    sq_w4_workspace_bytes, sq_w4_fold_weights, sq_a4_quant_per_token
 Allocating helpers built on them:
     calibrate, fold, quant, gemm, smoothed_linear, pack_i8, unpack_i8,
-    fold_norm_weight, rmsnorm_quant
+    fold_norm_weight, rmsnorm_quant, smoothing_factors, fold4, quant4
 
 The int8 codes (xq, wq) travel as flat int8 tensors in the packed operand
 order the C ABI documents (16-row x 64-byte fragments of 1 KiB); their sizes
@@ -44,7 +45,9 @@ SQ_MAX_K = 131056
 
 EXPORTS = ("sq_status_str", "sq_version", "sq_packed_bytes", "sq_calibrate_absmax",
            "sq_smooth_fold_weights", "sq_quant_act_per_token", "sq_w8a8_gemm", "sq_pack_i8",
-           "sq_unpack_i8", "sq_fold_norm_weight", "sq_rmsnorm_quant_per_token")
+           "sq_unpack_i8", "sq_fold_norm_weight", "sq_rmsnorm_quant_per_token",
+           "sq_smoothing_factors", "sq_w4_workspace_bytes", "sq_w4_fold_weights",
+           "sq_a4_quant_per_token")
 
 _LIB = None
 
@@ -87,6 +90,14 @@ def lib() -> ctypes.CDLL:
         L.sq_fold_norm_weight.argtypes = [vp, i64, vp, vp, vp]
         L.sq_rmsnorm_quant_per_token.restype = ci
         L.sq_rmsnorm_quant_per_token.argtypes = [vp, i64, i64, i64, vp, f32, vp, vp, vp]
+        L.sq_smoothing_factors.restype = ci
+        L.sq_smoothing_factors.argtypes = [vp, i64, i64, i64, vp, f32, vp, vp, vp]
+        L.sq_w4_workspace_bytes.restype = i64
+        L.sq_w4_workspace_bytes.argtypes = [i64, i64]
+        L.sq_w4_fold_weights.restype = ci
+        L.sq_w4_fold_weights.argtypes = [vp, i64, i64, i64, vp, ci, vp, vp, vp, vp]
+        L.sq_a4_quant_per_token.restype = ci
+        L.sq_a4_quant_per_token.argtypes = [vp, i64, i64, i64, vp, ci, vp, vp, vp]
         _LIB = L
     return _LIB
 
@@ -247,6 +258,56 @@ def sq_rmsnorm_quant_per_token(h, gamma_folded, eps: float, xq, x_scale, stream=
            "sq_rmsnorm_quant_per_token")
 
 
+def sq_smoothing_factors(w, act_absmax, alpha: float, smooth_out, inv_smooth_out,
+                         stream=None) -> None:
+    """s and 1/s (float32 [K]) from the statistics and w (float16 [K][N])."""
+    torch = _torch()
+    _need(w, torch.float16, "w", 2)
+    _need(act_absmax, torch.float32, "act_absmax", 1)
+    _need(smooth_out, torch.float32, "smooth_out", 1)
+    _need(inv_smooth_out, torch.float32, "inv_smooth_out", 1)
+    K, N = w.shape
+    _check(lib().sq_smoothing_factors(_ptr(w), K, N, _ld(w), _ptr(act_absmax), float(alpha),
+                                      _ptr(smooth_out), _ptr(inv_smooth_out),
+                                      _stream(stream, w.device)), "sq_smoothing_factors")
+
+
+def sq_w4_workspace_bytes(K: int, N: int) -> int:
+    return int(lib().sq_w4_workspace_bytes(int(K), int(N)))
+
+
+def sq_w4_fold_weights(w, smooth, rotate: bool, wq, w_scale, workspace, stream=None) -> None:
+    """4-bit codes (packed int8) and scales of H (s W) per output channel, or
+    of s W with rotate False; workspace: uint8/int8 device buffer of
+    sq_w4_workspace_bytes(K, N) bytes."""
+    torch = _torch()
+    _need(w, torch.float16, "w", 2)
+    _need(smooth, torch.float32, "smooth", 1)
+    _need(w_scale, torch.float32, "w_scale", 1)
+    K, N = w.shape
+    _need_packed(wq, N, K, "wq")
+    if not workspace.is_cuda or workspace.numel() * workspace.element_size() < \
+            sq_w4_workspace_bytes(K, N):
+        raise ValueError("workspace: expected a GPU buffer of sq_w4_workspace_bytes(K, N) bytes")
+    _check(lib().sq_w4_fold_weights(_ptr(w), K, N, _ld(w), _ptr(smooth), 1 if rotate else 0,
+                                    _ptr(wq), _ptr(w_scale), _ptr(workspace),
+                                    _stream(stream, w.device)), "sq_w4_fold_weights")
+
+
+def sq_a4_quant_per_token(x, inv_smooth, rotate: bool, xq, x_scale, stream=None) -> None:
+    """4-bit per-token codes (packed int8) and scales of (x / s) H, or of
+    x / s with rotate False."""
+    torch = _torch()
+    _need(x, torch.float16, "x", 2)
+    _need(inv_smooth, torch.float32, "inv_smooth", 1)
+    _need(x_scale, torch.float32, "x_scale", 1)
+    M, K = x.shape
+    _need_packed(xq, M, K, "xq")
+    _check(lib().sq_a4_quant_per_token(_ptr(x), M, K, _ld(x), _ptr(inv_smooth),
+                                       1 if rotate else 0, _ptr(xq), _ptr(x_scale),
+                                       _stream(stream, x.device)), "sq_a4_quant_per_token")
+
+
 def sq_pack_i8(src, dst, stream=None) -> None:
     """Row-major int8 codes src [rows][K] -> packed dst (padding zeroed)."""
     torch = _torch()
@@ -335,6 +396,39 @@ def rmsnorm_quant(h, gamma_folded, eps: float, stream=None):
     xq = torch.empty(packed_bytes(M, K), dtype=torch.int8, device=h.device)
     xs = torch.empty(M, dtype=torch.float32, device=h.device)
     sq_rmsnorm_quant_per_token(h, gamma_folded, eps, xq, xs, stream=stream)
+    return xq, xs
+
+
+def smoothing_factors(w, act_absmax, alpha: float, stream=None):
+    """Returns (s, 1/s) as float32 [K]."""
+    torch = _torch()
+    K = w.shape[0]
+    s = torch.empty(K, dtype=torch.float32, device=w.device)
+    inv = torch.empty(K, dtype=torch.float32, device=w.device)
+    sq_smoothing_factors(w, act_absmax, alpha, s, inv, stream=stream)
+    return s, inv
+
+
+def fold4(w, smooth, rotate: bool, stream=None):
+    """Returns (packed 4-bit codes of the N output channels, w_scale)."""
+    torch = _torch()
+    K, N = w.shape
+    wq = torch.empty(packed_bytes(N, K), dtype=torch.int8, device=w.device)
+    ws = torch.empty(N, dtype=torch.float32, device=w.device)
+    work = torch.empty(max(16, sq_w4_workspace_bytes(K, N)), dtype=torch.uint8, device=w.device)
+    sq_w4_fold_weights(w, smooth, rotate, wq, ws, work, stream=stream)
+    if hasattr(stream, "cuda_stream"):
+        work.record_stream(stream)      # freed only once that stream is past the call
+    return wq, ws
+
+
+def quant4(x, inv_smooth, rotate: bool, stream=None):
+    """Returns (packed 4-bit codes of the M tokens, x_scale)."""
+    torch = _torch()
+    M, K = x.shape
+    xq = torch.empty(packed_bytes(M, K), dtype=torch.int8, device=x.device)
+    xs = torch.empty(M, dtype=torch.float32, device=x.device)
+    sq_a4_quant_per_token(x, inv_smooth, rotate, xq, xs, stream=stream)
     return xq, xs
 
 

@@ -25,7 +25,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libsq.so")
 
-SOURCES = ["sq_api.cpp", "k_calib.hip", "k_fold.hip", "k_quant.hip", "k_gemm.hip", "k_pack.hip"]
+SOURCES = ["sq_api.cpp", "k_calib.hip", "k_fold.hip", "k_quant.hip", "k_gemm.hip", "k_pack.hip",
+           "k_rot.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -57,8 +57,9 @@ k_row_smooth(const uint16_t *__restrict__ w, int64_t K, int64_t N, int64_t ldw,
              const float *__restrict__ ax, const float *__restrict__ smooth_in, double alpha,
              float *__restrict__ s_out, float *__restrict__ inv_out, float *__restrict__ s_host,
              float *__restrict__ amax) {
-    for (int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x; i < N; i += (int64_t)gridDim.x * 64)
-        amax[i] = 0.0f;
+    if (amax)   // (the factors alone need no column maxima)
+        for (int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x; i < N; i += (int64_t)gridDim.x * 64)
+            amax[i] = 0.0f;
     const int lane = threadIdx.x;
     const int64_t j0 = (int64_t)blockIdx.x * RS_ROWS;
     const int64_t nfull = N & ~(int64_t)7;          // columns in whole octets

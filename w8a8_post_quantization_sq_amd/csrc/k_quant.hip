@@ -23,6 +23,10 @@
 // reduced in double too, so it is within K * 2^-53 of the exact sum and the
 // scale within one float rounding of the exact-sum value.
 //
+// With QMAX = 7 the same kernels quantize to 4 bits symmetrically ([-7, 7],
+// scale = a / 7), the unrotated 4-bit quantizer of the Smooth Rotation
+// comparison.
+//
 // The codes are written in the packed operand order of the int8 matrix
 // instruction (16-row x 64-byte fragments of 1 KiB, lane order quarter-major,
 // row-minor), so 16 consecutive codes of a row are one 16-byte piece and the
@@ -75,12 +79,13 @@ __device__ __forceinline__ void scale8(const Chunk &ch, float v[8], uint32_t &am
     }
 }
 
+template <int QMAX>
 __device__ __forceinline__ uint2 quant8(const float v[8], float r, bool zero) {
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         float q = __builtin_rintf(v[i] * r);
-        q = fminf(fmaxf(q, -127.0f), 127.0f);
+        q = fminf(fmaxf(q, -(float)QMAX), (float)QMAX);
         const uint32_t b = zero ? 0u : ((uint32_t)(int)q & 0xffu);
         if (i < 4) lo |= b << (8 * i);
         else hi |= b << (8 * (i - 4));
@@ -95,6 +100,7 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 }
 
 // Turns the row maximum into (scale, multiplier, all-zero-codes flag).
+template <int QMAX>
 __device__ __forceinline__ void row_params(uint32_t abits, float &scale, float &r, bool &zero) {
     if (abits >= 0x7f800000u) {          // a non-finite scaled value in the row
         scale = __builtin_nanf("");
@@ -106,8 +112,8 @@ __device__ __forceinline__ void row_params(uint32_t abits, float &scale, float &
         zero = true;
     } else {
         const float a = __uint_as_float(abits);
-        scale = a / 127.0f;
-        r = 127.0f / a;
+        scale = a / (float)QMAX;
+        r = (float)QMAX / a;
         zero = false;
     }
 }
@@ -133,7 +139,7 @@ __device__ __forceinline__ float norm_scale(uint32_t abits, double ss, int64_t K
 // Rows past M and chunks past K are padding and get zero codes.
 constexpr int QR = 8;   // rows per workgroup
 
-template <bool NORM>
+template <bool NORM, int QMAX>
 __global__ void __launch_bounds__(512)
 k_quant_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
              const float *__restrict__ inv_s, double eps, int8_t *__restrict__ xq,
@@ -167,7 +173,7 @@ k_quant_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
         if (NORM) ss = wave_sum_f64(ss);
         float scale, r;
         bool zero;
-        row_params(amax, scale, r, zero);
+        row_params<QMAX>(amax, scale, r, zero);
         if (NORM) scale = norm_scale(amax, ss, K, eps);
         if (lane == 0) {
             if (m < M) x_scale[m] = scale;
@@ -216,8 +222,8 @@ k_quant_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
             const int64_t k = kw * 64 + q * 16;
             uint4 out = make_uint4(0u, 0u, 0u, 0u);
             if (!skip && k < K) {
-                const uint2 a = quant8(&v[u][0], rr, false);
-                const uint2 b = quant8(&v[u][8], rr, false);
+                const uint2 a = quant8<QMAX>(&v[u][0], rr, false);
+                const uint2 b = quant8<QMAX>(&v[u][8], rr, false);
                 out = make_uint4(a.x, a.y, b.x, b.y);
             }
             // piece (window kw, quarter q, row half + r) of the packed row block
@@ -232,7 +238,7 @@ k_quant_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
 // shuffles, then the 2 waves of a row through LDS), quantizes, and writes its
 // codes into an LDS copy of the 8 rows; the group then leaves LDS as packed
 // 16-byte pieces, consecutive lanes on consecutive rows (128-byte runs).
-template <int CPL, bool NORM>
+template <int CPL, bool NORM, int QMAX>
 __global__ void __launch_bounds__(1024)
 k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
                  const float *__restrict__ inv_s, double eps, int8_t *__restrict__ xq,
@@ -282,7 +288,7 @@ k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t l
     const uint32_t arow = a0 > a1 ? a0 : a1;
     float scale, rr;
     bool zero;
-    row_params(arow, scale, rr, zero);
+    row_params<QMAX>(arow, scale, rr, zero);
     if (!NORM && real && h == 0 && lane == 0) x_scale[m] = scale;
     zero = zero || !real;
 #pragma unroll
@@ -290,7 +296,7 @@ k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t l
         const int64_t k = ((int64_t)(c * 2 + h) * 64 + lane) * 8;
         if (k < pitch)   // codes past K (padding) are zero
             *reinterpret_cast<uint2 *>(codes + r * pitch + k) =
-                (k < K) ? quant8(v[c], rr, zero) : make_uint2(0u, 0u);
+                (k < K) ? quant8<QMAX>(v[c], rr, zero) : make_uint2(0u, 0u);
     }
     // the normalized scale once the row's values are no longer held
     if (NORM && real && h == 0 && lane == 0)
@@ -311,7 +317,7 @@ k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t l
     }
 }
 
-template <bool NORM>
+template <bool NORM, int QMAX>
 hipError_t launch_rows(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const float *inv_s,
                        double eps, int8_t *xq, float *x_scale, hipStream_t st) {
     if (M <= 0) return hipSuccess;
@@ -321,25 +327,31 @@ hipError_t launch_rows(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, con
     const size_t lds = (size_t)QR * ((K + 63) / 64) * 64;
     const dim3 g((unsigned)groups);
 #define SQ_QR(C) \
-    k_quant_rows_reg<C, NORM><<<g, dim3(1024), lds, st>>>(x, M, K, ldx, inv_s, eps, xq, x_scale)
+    k_quant_rows_reg<C, NORM, QMAX><<<g, dim3(1024), lds, st>>>(x, M, K, ldx, inv_s, eps, xq, \
+                                                                 x_scale)
     if (cpl <= 1) SQ_QR(1);
     else if (cpl <= 2) SQ_QR(2);
     else if (cpl <= 4) SQ_QR(4);
     else if (cpl <= 8) SQ_QR(8);     // up to 8192 channels: 64 KiB LDS
-    else k_quant_rows<NORM><<<g, dim3(512), 0, st>>>(x, M, K, ldx, inv_s, eps, xq, x_scale);
+    else k_quant_rows<NORM, QMAX><<<g, dim3(512), 0, st>>>(x, M, K, ldx, inv_s, eps, xq, x_scale);
 #undef SQ_QR
     return hipGetLastError();
 }
 
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                             const float *inv_s, int8_t *xq, float *x_scale, hipStream_t st) {
-    return launch_rows<false>(x, M, K, ldx, inv_s, 0.0, xq, x_scale, st);
+    return launch_rows<false, 127>(x, M, K, ldx, inv_s, 0.0, xq, x_scale, st);
 }
 
 hipError_t launch_rmsnorm_quant(const uint16_t *h, int64_t M, int64_t K, int64_t ldh,
                                 const float *g, float eps, int8_t *xq, float *x_scale,
                                 hipStream_t st) {
-    return launch_rows<true>(h, M, K, ldh, g, (double)eps, xq, x_scale, st);
+    return launch_rows<true, 127>(h, M, K, ldh, g, (double)eps, xq, x_scale, st);
+}
+
+hipError_t launch_quant4_plain(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                               const float *mult, int8_t *q, float *scale, hipStream_t st) {
+    return launch_rows<false, 7>(x, M, K, ldx, mult, 0.0, q, scale, st);
 }
 
 // g[j] = float(gamma[j]) * inv_s[j], 8 channels per thread (K % 16 == 0).

@@ -1,0 +1,243 @@
+// 4-bit symmetric quantization of rows, optionally after the Hadamard rotation
+// of Smooth Rotation (Pith review of arXiv 2506.01967, key machinery: scale the
+// channels, then multiply activations and weights by the same Hadamard matrix;
+// core discovery: 4-bit symmetric round-to-nearest on both).
+//
+// Per row of M rows (fp16 x, row stride ldx) with a per-channel float factor
+// `mult` (1/s for activations, s for the rows of W transposed); the rotation
+// off, the 7-level form of the 8-bit per-token quantizer does the same without
+// the transform:
+//   v[j]     = float(x[j]) * mult[j]
+//   v        = v H           (rotation on: the unnormalized Sylvester matrix,
+//                             H[i][j] = (-1)^popcount(i & j), K a power of two)
+//   a        = max_j |v[j]|,  q[j] = clamp(rint(v[j] * (7 / a)), -7, 7)
+//   scale    = (a / 7) * post (post a power of two, so the product is exact)
+// The two factors 1/sqrt(K) of the orthonormal rotation multiply to 1/K, which
+// the weight side passes as `post`.  A zero row gets scale 0, a row with a
+// non-finite value scale NaN, both with zero codes.
+//
+// The transform is the fast one, with its stages in the order h = 1, 2, 4, ...,
+// K/2 and every butterfly (a + b, a - b) in float, a being the element at the
+// lower index; each stage only changes where the two operands live:
+//   element k = (u * 64 + lane) * 8 + e  of a row held by one wave, so
+//   h = 1, 2, 4    (bits 0-2: e)     pair within a lane's 8-element chunk,
+//   h = 8 .. 256   (bits 3-8: lane)  pair across lanes (a shuffle),
+//   h = 512 ..     (bits 9+:  u)     pair across a lane's chunks.
+// So every value is the same float that the plain in-order transform gives.
+//
+// Codes leave as int8 in the packed operand order of the int8 matrix
+// instruction (the 4-bit values widened to bytes), through an LDS copy of the
+// workgroup's 8 rows, as the 8-bit quantizer writes them.
+#include "sq_device.h"
+
+namespace sq {
+
+constexpr int R4 = 8;   // rows per workgroup, one wave each
+
+template <int U>
+__global__ void __launch_bounds__(512)
+k_quant4_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
+              const float *__restrict__ mult, float post, int8_t *__restrict__ q,
+              float *__restrict__ scale) {
+    extern __shared__ __align__(16) int8_t codes[];     // [8][KW * 64]
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;                   // the row of the group
+    const int64_t m0 = (int64_t)blockIdx.x * R4;
+    const int64_t m = m0 + wave;
+    const int64_t KW = (K + 63) >> 6;
+    const int64_t pitch = KW * 64;
+    const bool real = m < M;
+    const uint16_t *row = x + (real ? m : 0) * ldx;
+
+    float v[U][8];
+    // loads in rounds of 4 chunks (16 bytes of x and 32 of factors each)
+#pragma unroll
+    for (int u0 = 0; u0 < U; u0 += 4) {
+        uint4 raw[4];
+        float4 f0[4], f1[4];
+#pragma unroll
+        for (int i = 0; i < 4 && u0 + i < U; ++i) {
+            const int64_t k = ((int64_t)(u0 + i) * 64 + lane) * 8;
+            if (real && k < K) {
+                raw[i] = *reinterpret_cast<const uint4 *>(row + k);
+                f0[i] = *reinterpret_cast<const float4 *>(mult + k);
+                f1[i] = *reinterpret_cast<const float4 *>(mult + k + 4);
+            } else {
+                raw[i] = make_uint4(0u, 0u, 0u, 0u);
+                f0[i] = f1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4 && u0 + i < U; ++i) {
+            const uint32_t h[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+            const float f[8] = {f0[i].x, f0[i].y, f0[i].z, f0[i].w,
+                                f1[i].x, f1[i].y, f1[i].z, f1[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[u0 + i][2 * e] = h2f(h[e] & 0xffffu) * f[2 * e];
+                v[u0 + i][2 * e + 1] = h2f(h[e] >> 16) * f[2 * e + 1];
+            }
+        }
+    }
+
+    {
+        // h = 1, 2, 4: inside each chunk
+#pragma unroll
+        for (int hb = 1; hb < 8; hb <<= 1) {
+            if (hb >= K) break;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if ((e & hb) == 0) {
+                        const float a = v[u][e], b = v[u][e + hb];
+                        v[u][e] = a + b;
+                        v[u][e + hb] = a - b;
+                    }
+        }
+        // h = 8 .. 256: lane bit t pairs lane l with l ^ (1 << t); the lower
+        // lane keeps a + b, the upper one a - b
+#pragma unroll
+        for (int t = 0; t < 6; ++t) {
+            if ((8 << t) >= K) break;
+            const bool upper = (lane >> t) & 1;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float p = __shfl_xor(v[u][e], 1 << t, 64);
+                    v[u][e] = upper ? p - v[u][e] : v[u][e] + p;
+                }
+        }
+        // h = 512 ..: between chunks u and u + 2^t (U = K / 512 here)
+#pragma unroll
+        for (int hu = 1; hu < U; hu <<= 1)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if ((u & hu) == 0)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float a = v[u][e], b = v[u + hu][e];
+                        v[u][e] = a + b;
+                        v[u + hu][e] = a - b;
+                    }
+    }
+
+    // row maximum on the magnitude bits (NaN above +inf); elements past K are 0
+    uint32_t amax = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t b = __float_as_uint(v[u][e]) & 0x7fffffffu;
+            amax = amax > b ? amax : b;
+        }
+    amax = wave_max_u32(amax);
+    float r = 0.0f;
+    bool zero = true;
+    if (amax >= 0x7f800000u) {
+        if (real && lane == 0) scale[m] = __builtin_nanf("");
+    } else if (amax == 0u) {
+        if (real && lane == 0) scale[m] = 0.0f;
+    } else {
+        const float a = __uint_as_float(amax);
+        r = 7.0f / a;
+        zero = false;
+        if (real && lane == 0) scale[m] = (a / 7.0f) * post;
+    }
+    zero = zero || !real;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t k = ((int64_t)u * 64 + lane) * 8;
+        if (k < pitch) {
+            uint32_t lo = 0, hi = 0;
+            if (!zero && k < K) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float c = __builtin_rintf(v[u][e] * r);
+                    c = fminf(fmaxf(c, -7.0f), 7.0f);
+                    const uint32_t b = (uint32_t)(int)c & 0xffu;
+                    if (e < 4) lo |= b << (8 * e);
+                    else hi |= b << (8 * (e - 4));
+                }
+            }
+            *reinterpret_cast<uint2 *>(codes + wave * pitch + k) = make_uint2(lo, hi);
+        }
+    }
+    __syncthreads();
+    const int64_t rb = m0 >> 4;
+    const int half = (int)(m0 & 15);
+    int8_t *base = q + ((rb * KW) << 10);
+    const int64_t pieces = (int64_t)R4 * 4 * KW;
+    for (int64_t p = threadIdx.x; p < pieces; p += 512) {
+        const int pr = (int)(p & 7);
+        const int qq = (int)((p >> 3) & 3);
+        const int64_t kw = p >> 5;
+        __builtin_nontemporal_store(
+            *reinterpret_cast<const v4i *>(codes + pr * pitch + kw * 64 + qq * 16),
+            reinterpret_cast<v4i *>(base + ((kw * 64 + qq * 16 + half + pr) << 4)));
+    }
+}
+
+hipError_t launch_quant4_rows(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                              const float *mult, int rotate, float post, int8_t *q, float *scale,
+                              hipStream_t st) {
+    if (M <= 0) return hipSuccess;
+    // unrotated: the per-token quantizer at 7 levels (post is 1 there)
+    if (!rotate) return launch_quant4_plain(x, M, K, ldx, mult, q, scale, st);
+    const int64_t groups = (M + 15) / 16 * 2;       // every row of the padded row blocks
+    const int64_t chunks = (K + 511) / 512;          // chunks of 8 per lane
+    const size_t lds = (size_t)R4 * ((K + 63) / 64) * 64;
+    const dim3 g((unsigned)groups), b(512);
+#define SQ_Q4(U_) k_quant4_rows<U_><<<g, b, lds, st>>>(x, M, K, ldx, mult, post, q, scale)
+    if (chunks <= 1) SQ_Q4(1);
+    else if (chunks <= 2) SQ_Q4(2);
+    else if (chunks <= 4) SQ_Q4(4);
+    else if (chunks <= 8) SQ_Q4(8);
+    else SQ_Q4(16);                                  // K <= 8192
+#undef SQ_Q4
+    return hipGetLastError();
+}
+
+// W fp16 [K][ldw] -> W^T fp16 [N][K]: 64 x 64 tiles through LDS.
+__global__ void __launch_bounds__(256)
+k_transpose_f16(const uint16_t *__restrict__ w, int64_t K, int64_t N, int64_t ldw,
+                uint16_t *__restrict__ wt) {
+    __shared__ uint16_t tile[64][66];
+    const int64_t n0 = (int64_t)blockIdx.x * 64, k0 = (int64_t)blockIdx.y * 64;
+    const int c = threadIdx.x & 63, r0 = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {   // consecutive lanes on consecutive columns
+        const int r = r0 + 4 * i;
+        const int64_t k = k0 + r, n = n0 + c;
+        tile[r][c] = (k < K && n < N) ? w[k * ldw + n] : (uint16_t)0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {    // 16 bytes (8 consecutive k) of one output row each
+        const int idx = threadIdx.x + 256 * i;
+        const int nn = idx >> 3, kc = (idx & 7) * 8;
+        const int64_t n = n0 + nn, k = k0 + kc;
+        if (n < N && k < K) {
+            uint32_t p[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                p[j] = (uint32_t)tile[kc + 2 * j][nn] | ((uint32_t)tile[kc + 2 * j + 1][nn] << 16);
+            *reinterpret_cast<uint4 *>(wt + n * K + k) = make_uint4(p[0], p[1], p[2], p[3]);
+        }
+    }
+}
+
+hipError_t launch_fold4(const uint16_t *w, int64_t K, int64_t N, int64_t ldw, const float *s,
+                        int rotate, int8_t *wq, float *w_scale, uint16_t *wt, hipStream_t st) {
+    if (N <= 0) return hipSuccess;
+    k_transpose_f16<<<dim3((unsigned)((N + 63) / 64), (unsigned)((K + 63) / 64)), dim3(256), 0,
+                      st>>>(w, K, N, ldw, wt);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // with the rotation the weight scale carries the 1/K of the two transforms
+    return launch_quant4_rows(wt, N, K, K, s, rotate, rotate ? 1.0f / (float)K : 1.0f, wq,
+                              w_scale, st);
+}
+
+}  // namespace sq

@@ -112,6 +112,21 @@ hipError_t staging_for(hipStream_t st, int64_t K, int64_t N, Staging **out) {
     return hipSuccess;
 }
 
+// The fold's check of the factors it wrote to the host buffer.  1/s is the
+// IEEE float quotient on both sides, so the host recomputes it for the range
+// check instead of copying it back.
+sq_status check_factors(const float *host, int64_t K) {
+    bool nonfinite = false, range = false;
+    for (int64_t j = 0; j < K; ++j) {
+        const float sj = host[j];
+        if (isnan(sj)) nonfinite = true;
+        else if (!isnormal(sj) || !isnormal(1.0f / sj) || sj < 0.0f) range = true;
+    }
+    if (nonfinite) return SQ_ERR_NONFINITE;
+    if (range) return SQ_ERR_RANGE;
+    return SQ_OK;
+}
+
 }  // namespace
 
 SQ_API const char *sq_status_str(int status) {
@@ -130,7 +145,7 @@ SQ_API const char *sq_status_str(int status) {
     }
 }
 
-SQ_API int sq_version(void) { return 10300; }
+SQ_API int sq_version(void) { return 10400; }
 
 SQ_API int64_t sq_packed_bytes(int64_t rows, int64_t K) {
     if (rows < 0 || rows >= kMaxDim || !k_ok(K)) return 0;
@@ -185,17 +200,71 @@ SQ_API sq_status sq_smooth_fold_weights(const void *w_f16, int64_t K, int64_t N,
     const hipError_t ew = hipEventSynchronize(g->ready);
     if (e != hipSuccess || ew != hipSuccess) return SQ_ERR_HIP;
 
-    // 1/s is the IEEE float quotient on both sides, so the host recomputes it
-    // for the range check instead of copying it back.
-    bool nonfinite = false, range = false;
-    for (int64_t j = 0; j < K; ++j) {
-        const float sj = g->host[j];
-        if (isnan(sj)) nonfinite = true;
-        else if (!isnormal(sj) || !isnormal(1.0f / sj) || sj < 0.0f) range = true;
+    return check_factors(g->host, K);
+}
+
+SQ_API sq_status sq_smoothing_factors(const void *w_f16, int64_t K, int64_t N, int64_t ldw,
+                                      const float *act_absmax, float alpha, float *smooth_out,
+                                      float *inv_smooth_out, void *stream) {
+    if (!smooth_out || !inv_smooth_out || !act_absmax || (N > 0 && !w_f16)) return SQ_ERR_NULL;
+    if (N < 0 || N >= kMaxDim || !k_ok(K) || (N > 0 && ldw < N)) return SQ_ERR_SHAPE;
+    if (!aligned16(smooth_out) || !aligned16(inv_smooth_out) || !aligned16(act_absmax))
+        return SQ_ERR_ALIGN;
+    if (N > 0 && (!aligned16(w_f16) || (ldw % 8) != 0)) return SQ_ERR_ALIGN;
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_ALPHA;
+    const hipStream_t st = as_stream(stream);
+    Staging *g = nullptr;
+    if (staging_for(st, K, 0, &g) != hipSuccess) return SQ_ERR_HIP;
+    hipError_t e = sq::launch_row_smooth(static_cast<const uint16_t *>(w_f16), K, N, ldw,
+                                         act_absmax, nullptr, alpha, smooth_out, inv_smooth_out,
+                                         g->host_dev, nullptr, st);
+    if (e == hipSuccess) e = hipEventRecord(g->ready, st);
+    g->last = st;
+    g->used = true;
+    if (e != hipSuccess) {
+        (void)hipStreamSynchronize(st);
+        return SQ_ERR_HIP;
     }
-    if (nonfinite) return SQ_ERR_NONFINITE;
-    if (range) return SQ_ERR_RANGE;
-    return SQ_OK;
+    if (hipEventSynchronize(g->ready) != hipSuccess) return SQ_ERR_HIP;
+    return check_factors(g->host, K);
+}
+
+SQ_API int64_t sq_w4_workspace_bytes(int64_t K, int64_t N) {
+    if (N < 0 || N >= kMaxDim || !k_ok(K)) return 0;
+    return 2 * K * N;
+}
+
+// K for the 4-bit calls: a whole number of 16-code rows up to the register-
+// resident kernels' 8192, and a power of two when rotated (Sylvester matrix).
+static bool k4_ok(int64_t K, int rotate) {
+    if (!k_ok(K) || K > 8192) return false;
+    return !rotate || (K & (K - 1)) == 0;
+}
+
+SQ_API sq_status sq_a4_quant_per_token(const void *x_f16, int64_t M, int64_t K, int64_t ldx,
+                                       const float *inv_smooth, int rotate, int8_t *xq,
+                                       float *x_scale, void *stream) {
+    if (!inv_smooth || (M > 0 && (!x_f16 || !xq || !x_scale))) return SQ_ERR_NULL;
+    if (M < 0 || M >= kMaxDim || !k4_ok(K, rotate) || ldx < K) return SQ_ERR_SHAPE;
+    if (!aligned16(inv_smooth) || (ldx % 8) != 0) return SQ_ERR_ALIGN;
+    if (M > 0 && (!aligned16(x_f16) || !aligned16(xq) || !aligned16(x_scale))) return SQ_ERR_ALIGN;
+    return hip_status(sq::launch_quant4_rows(static_cast<const uint16_t *>(x_f16), M, K, ldx,
+                                             inv_smooth, rotate != 0, 1.0f, xq, x_scale,
+                                             as_stream(stream)));
+}
+
+SQ_API sq_status sq_w4_fold_weights(const void *w_f16, int64_t K, int64_t N, int64_t ldw,
+                                    const float *smooth, int rotate, int8_t *wq, float *w_scale,
+                                    void *workspace, void *stream) {
+    if (!smooth || (N > 0 && (!w_f16 || !wq || !w_scale || !workspace))) return SQ_ERR_NULL;
+    if (N < 0 || N >= kMaxDim || !k4_ok(K, rotate) || (N > 0 && ldw < N)) return SQ_ERR_SHAPE;
+    if (!aligned16(smooth)) return SQ_ERR_ALIGN;
+    if (N > 0 && (!aligned16(w_f16) || !aligned16(wq) || !aligned16(w_scale) ||
+                  !aligned16(workspace) || (ldw % 8) != 0))
+        return SQ_ERR_ALIGN;
+    return hip_status(sq::launch_fold4(static_cast<const uint16_t *>(w_f16), K, N, ldw, smooth,
+                                       rotate != 0, wq, w_scale,
+                                       static_cast<uint16_t *>(workspace), as_stream(stream)));
 }
 
 SQ_API sq_status sq_quant_act_per_token(const void *x_f16, int64_t M, int64_t K, int64_t ldx,

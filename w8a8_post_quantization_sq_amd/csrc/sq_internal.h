@@ -15,7 +15,8 @@ hipError_t launch_calib_absmax(const uint16_t *x, int64_t T, int64_t K, int64_t 
                                float *ax, int accumulate, hipStream_t st);
 
 // aw_j = max_n |W[j][n]| -> s_out[j] = s_j (also into s_host when not NULL,
-// a device-visible host buffer), inv_out[j] = 1/s_j; zeroes amax[0, N)
+// a device-visible host buffer), inv_out[j] = 1/s_j; zeroes amax[0, N) when
+// amax is not NULL
 hipError_t launch_row_smooth(const uint16_t *w, int64_t K, int64_t N, int64_t ldw,
                              const float *ax, const float *smooth_in, float alpha, float *s_out,
                              float *inv_out, float *s_host, float *amax, hipStream_t st);
@@ -41,6 +42,21 @@ hipError_t launch_rmsnorm_quant(const uint16_t *h, int64_t M, int64_t K, int64_t
 // g[j] = float(gamma[j]) * inv_s[j]
 hipError_t launch_fold_norm_weight(const uint16_t *gamma, int64_t K, const float *inv_s, float *g,
                                    hipStream_t st);
+
+// the per-token quantizer at 7 levels: 4-bit codes of x * mult, scale = max / 7
+hipError_t launch_quant4_plain(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                               const float *mult, int8_t *q, float *scale, hipStream_t st);
+
+// 4-bit quantization of rows (x * mult, rotated by the Sylvester Hadamard
+// matrix when rotate != 0), codes packed as int8, scale = (max / 7) * post
+hipError_t launch_quant4_rows(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                              const float *mult, int rotate, float post, int8_t *q, float *scale,
+                              hipStream_t st);
+
+// 4-bit weights: W transposed into wt (N x K fp16), then its rows quantized
+// with mult = s (and post = 1/K when rotated)
+hipError_t launch_fold4(const uint16_t *w, int64_t K, int64_t N, int64_t ldw, const float *s,
+                        int rotate, int8_t *wq, float *w_scale, uint16_t *wt, hipStream_t st);
 
 hipError_t launch_pack_i8(const int8_t *src, int64_t rows, int64_t K, int64_t ld, int8_t *dst,
                           hipStream_t st);

@@ -83,6 +83,11 @@ WORKLOADS = {
     "prefill8192x3": Workload("prefill8192x3", 8192, 8192, (8192, 8192, 8192), 0.5, 5, 0.015, 41,
                               (100.0, 100.0),
                               description="8192x8192 shared X feeding three 8192x8192 projections, 0.5% channels x100"),
+    # The Smooth Rotation study needs a power-of-two width (the Sylvester
+    # matrix); this is the down_proj outlier structure at d = 4096.
+    "massive4096": Workload("massive4096", 2048, 4096, (4096,), 0.5, 6, 0.02, 4, (1000.0, 1000.0),
+                            token_frac=0.02,
+                            description="down_proj-style 2048x4096x4096, 4 channels x1000 on 2% of tokens"),
 }
 
 
