@@ -18,7 +18,9 @@ the per-stage GPU times from a separate pass with events between the stages,
 the serving-time layer (A4 + A5/A6, the two calls a deployed layer makes per
 batch), the fused RMS-norm + quantization that replaces A4 when 1/s is
 folded into the normalization in front of the layer (outside the step), and
-the CPU oracle timed on a bounded sample as a baseline.
+the rotated 4-bit quantizer of Smooth Rotation against the unrotated one
+(outside the step), and the CPU oracle timed on a bounded sample as a
+baseline.
 """
 import argparse
 import hashlib
@@ -117,6 +119,9 @@ def main():
     ap.add_argument("--norm-launches", type=int, default=100,
                     help="launches of the fused RMS-norm + quantization (and of the plain "
                          "quantizer) timed between one pair of events (0: skip)")
+    ap.add_argument("--rot-launches", type=int, default=100,
+                    help="launches of the rotated 4-bit quantizer (and of the unrotated one) "
+                         "timed between one pair of events (0: skip)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle layer work in the CPU baseline (0: skip)")
     ap.add_argument("--copy-kernel", type=int, default=0, metavar="MIB",
@@ -265,6 +270,37 @@ def main():
                 "saved_bytes_per_batch": 4 * M * K}
         log(f"fused norm + quant {us[True]:.2f} us, plain quant {us[False]:.2f} us")
 
+    # Smooth Rotation at 4 bits (outside the step): the per-token quantizer
+    # with the Hadamard transform against the same quantizer without it, on
+    # the same batch and factors; the product takes their codes unchanged.
+    rot = None
+    if args.rot_launches > 0 and K & (K - 1) == 0 and K <= 8192:
+        us = {}
+        for rotate in (0, 1, 0, 1):                  # second round is the one kept
+            def run4():
+                return L.sq_a4_quant_per_token(p["x"], M, K, K, p["inv"], rotate, p["xq"],
+                                               p["xsc"], hs)
+            for _ in range(10):
+                run4()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.rot_launches):
+                if run4():
+                    raise RuntimeError("4-bit quantizer call failed")
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us[rotate] = e0.elapsed_time(e1) * 1e3 / args.rot_launches
+        nbytes = 2 * M * K + M * K + 4 * M + 4 * K
+        gbs = nbytes / (us[1] * 1e-6) / 1e9
+        rot = {"what": "Smooth Rotation 4-bit per-token quantizer: x/s, fast Walsh-Hadamard "
+                       "transform, 4-bit codes (sq_a4_quant_per_token, rotate=1)",
+               "us": round(us[1], 3), "unrotated_us": round(us[0], 3),
+               "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+               "frac": round(gbs / PEAK_HBM_GBS, 4),
+               "per_launch": f"2MK (x) + MK (codes, one per byte) + 4M + 4K = {nbytes} bytes",
+               "transform_flops": int(M * K * (K.bit_length() - 1))}
+        log(f"rotated 4-bit quant {us[1]:.2f} us, unrotated {us[0]:.2f} us")
+
     ops = 2.0 * M * N * K
     ms_step = wall * 1e3 / args.steps
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
@@ -302,6 +338,7 @@ def main():
                      "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": traffic,
                      "per_launch": f"2*M*N*K = {ops:.4g} int8 ops per launch"},
         "norm_fold": norm,
+        "rotation_w4": rot,
         "cpu_baseline": None,
     }
     if args.cpu_budget > 0:

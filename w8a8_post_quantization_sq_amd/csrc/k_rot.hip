@@ -18,7 +18,8 @@
 //
 // The transform is the fast one, with its stages in the order h = 1, 2, 4, ...,
 // K/2 and every butterfly (a + b, a - b) in float, a being the element at the
-// lower index; each stage only changes where the two operands live:
+// lower index.  Up to K = 2048 (k_quant4_rows) each stage only changes where
+// the two operands live:
 //   element k = (u * 64 + lane) * 8 + e  of a row held by one wave, so
 //   h = 1, 2, 4    (bits 0-2: e)     pair within a lane's 8-element chunk,
 //   h = 8 .. 256   (bits 3-8: lane)  pair across lanes (a shuffle),
@@ -179,12 +180,159 @@ k_quant4_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
     }
 }
 
+// Wide rows, K = 64 * V (4096 or 8192), one wave per row, 4 rows per group.
+// Lane l first holds the contiguous elements l*V .. l*V + V - 1, so the
+// stages h = 1 .. V/2 (the low log2(V) index bits) run in its registers; one
+// transpose through LDS then gives lane l' the elements h*V + l' + 64 j
+// (h = 0..63, j < V/64), the six high index bits in registers for the stages
+// h = V .. K/2.  No butterfly crosses lanes.  The transpose area, 64 rows of
+// 64 floats padded to 68 per wave (writes and reads free of bank conflicts),
+// is reused for the codes before they leave in packed order.
+constexpr int RT = 4;     // rows per workgroup
+constexpr int TP = 68;    // padded floats per transpose row
+
+template <int V>
+__global__ void __launch_bounds__(256)
+k_quant4_rot_t(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
+               const float *__restrict__ mult, float post, int8_t *__restrict__ q,
+               float *__restrict__ scale) {
+    extern __shared__ __align__(16) float tr_all[];     // [RT][64][TP]
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t m0 = (int64_t)blockIdx.x * RT;
+    const int64_t m = m0 + wave;
+    const bool real = m < M;
+    const uint16_t *row = x + (real ? m : 0) * ldx;
+    float *tr = tr_all + wave * 64 * TP;
+
+    float v[V];
+    const int64_t k0 = (int64_t)lane * V;
+#pragma unroll
+    for (int c0 = 0; c0 < V / 8; c0 += 4) {     // loads in rounds of 4 chunks of 8
+        uint4 raw[4];
+        float4 f0[4], f1[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t k = k0 + (c0 + i) * 8;
+            if (real) {
+                raw[i] = *reinterpret_cast<const uint4 *>(row + k);
+                f0[i] = *reinterpret_cast<const float4 *>(mult + k);
+                f1[i] = *reinterpret_cast<const float4 *>(mult + k + 4);
+            } else {
+                raw[i] = make_uint4(0u, 0u, 0u, 0u);
+                f0[i] = f1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t h[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+            const float f[8] = {f0[i].x, f0[i].y, f0[i].z, f0[i].w,
+                                f1[i].x, f1[i].y, f1[i].z, f1[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[(c0 + i) * 8 + 2 * e] = h2f(h[e] & 0xffffu) * f[2 * e];
+                v[(c0 + i) * 8 + 2 * e + 1] = h2f(h[e] >> 16) * f[2 * e + 1];
+            }
+        }
+    }
+    // stages h = 1 .. V/2: inside the lane's segment
+#pragma unroll
+    for (int hb = 1; hb < V; hb <<= 1)
+#pragma unroll
+        for (int r = 0; r < V; ++r)
+            if ((r & hb) == 0) {
+                const float a = v[r], b = v[r + hb];
+                v[r] = a + b;
+                v[r + hb] = a - b;
+            }
+    // transpose, one block of 64 segment positions at a time: lane l writes
+    // its positions 64 j .. 64 j + 63 as transpose row l; lane l' reads column
+    // l', i.e. element h*V + l' + 64 j for h = 0..63, into v[64 j + h]
+#pragma unroll
+    for (int j = 0; j < V / 64; ++j) {
+#pragma unroll
+        for (int r4 = 0; r4 < 64; r4 += 4)
+            *reinterpret_cast<float4 *>(tr + lane * TP + r4) =
+                make_float4(v[64 * j + r4], v[64 * j + r4 + 1], v[64 * j + r4 + 2],
+                            v[64 * j + r4 + 3]);
+        __syncthreads();
+#pragma unroll
+        for (int h = 0; h < 64; ++h) v[64 * j + h] = tr[h * TP + lane];
+        __syncthreads();
+    }
+    // stages h = V .. K/2: the six high index bits, now the register index h
+#pragma unroll
+    for (int j = 0; j < V / 64; ++j)
+#pragma unroll
+        for (int hb = 1; hb < 64; hb <<= 1)
+#pragma unroll
+            for (int h = 0; h < 64; ++h)
+                if ((h & hb) == 0) {
+                    const float a = v[64 * j + h], b = v[64 * j + h + hb];
+                    v[64 * j + h] = a + b;
+                    v[64 * j + h + hb] = a - b;
+                }
+
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const uint32_t b = __float_as_uint(v[i]) & 0x7fffffffu;
+        amax = amax > b ? amax : b;
+    }
+    amax = wave_max_u32(amax);
+    float r = 0.0f;
+    bool zero = true;
+    if (amax >= 0x7f800000u) {
+        if (real && lane == 0) scale[m] = __builtin_nanf("");
+    } else if (amax == 0u) {
+        if (real && lane == 0) scale[m] = 0.0f;
+    } else {
+        const float a = __uint_as_float(amax);
+        r = 7.0f / a;
+        zero = false;
+        if (real && lane == 0) scale[m] = (a / 7.0f) * post;
+    }
+    zero = zero || !real;
+    // codes into the (now free) transpose area, row-major per row
+    int8_t *codes = reinterpret_cast<int8_t *>(tr_all) + wave * K;
+#pragma unroll
+    for (int j = 0; j < V / 64; ++j)
+#pragma unroll
+        for (int h = 0; h < 64; ++h) {
+            float c = __builtin_rintf(v[64 * j + h] * r);
+            c = fminf(fmaxf(c, -7.0f), 7.0f);
+            codes[h * V + 64 * j + lane] = zero ? (int8_t)0 : (int8_t)(int)c;
+        }
+    __syncthreads();
+    const int64_t KW = K >> 6;
+    const int64_t rb = m0 >> 4;
+    const int quarter = (int)(m0 & 15);          // 0, 4, 8 or 12
+    int8_t *base = q + ((rb * KW) << 10);
+    const int8_t *cb = reinterpret_cast<const int8_t *>(tr_all);
+    const int64_t pieces = (int64_t)RT * 4 * KW;
+    for (int64_t p = threadIdx.x; p < pieces; p += 256) {
+        const int pr = (int)(p & 3);
+        const int qq = (int)((p >> 2) & 3);
+        const int64_t kw = p >> 4;
+        __builtin_nontemporal_store(
+            *reinterpret_cast<const v4i *>(cb + pr * K + kw * 64 + qq * 16),
+            reinterpret_cast<v4i *>(base + ((kw * 64 + qq * 16 + quarter + pr) << 4)));
+    }
+}
+
 hipError_t launch_quant4_rows(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                               const float *mult, int rotate, float post, int8_t *q, float *scale,
                               hipStream_t st) {
     if (M <= 0) return hipSuccess;
     // unrotated: the per-token quantizer at 7 levels (post is 1 there)
     if (!rotate) return launch_quant4_plain(x, M, K, ldx, mult, q, scale, st);
+    if (K == 4096 || K == 8192) {
+        const dim3 g((unsigned)((M + 15) / 16 * 4)), b(256);   // every row of the padded blocks
+        const size_t lds = (size_t)RT * 64 * TP * sizeof(float);
+        if (K == 4096) k_quant4_rot_t<64><<<g, b, lds, st>>>(x, M, K, ldx, mult, post, q, scale);
+        else k_quant4_rot_t<128><<<g, b, lds, st>>>(x, M, K, ldx, mult, post, q, scale);
+        return hipGetLastError();
+    }
     const int64_t groups = (M + 15) / 16 * 2;       // every row of the padded row blocks
     const int64_t chunks = (K + 511) / 512;          // chunks of 8 per lane
     const size_t lds = (size_t)R4 * ((K + 63) / 64) * 64;
@@ -192,9 +340,7 @@ hipError_t launch_quant4_rows(const uint16_t *x, int64_t M, int64_t K, int64_t l
 #define SQ_Q4(U_) k_quant4_rows<U_><<<g, b, lds, st>>>(x, M, K, ldx, mult, post, q, scale)
     if (chunks <= 1) SQ_Q4(1);
     else if (chunks <= 2) SQ_Q4(2);
-    else if (chunks <= 4) SQ_Q4(4);
-    else if (chunks <= 8) SQ_Q4(8);
-    else SQ_Q4(16);                                  // K <= 8192
+    else SQ_Q4(4);                                   // K <= 2048 (wider rows above)
 #undef SQ_Q4
     return hipGetLastError();
 }
