@@ -44,6 +44,14 @@
  *   bytes.  Padding bytes (rows >= `rows` of the last row block, k >= K of the
  *   last window) must be zero; the library's producers write them as zero.
  * sq_pack_i8 / sq_unpack_i8 convert between this layout and row-major codes.
+ *
+ * Packed 4-bit weights (sq_w4_fold_weights, sq_w4_gemm) use the same fragment
+ * order at half the size: codes in [-8, 7] as two's-complement nibbles, each
+ * fragment 512 bytes, the lane chunk of 16 codes (k % 64 / 16 = quarter,
+ * r % 16 = row, as above) 8 bytes at ((r / 16) * KW + k / 64) * 512 +
+ * ((k % 64) / 16) * 128 + (r % 16) * 8; code i = k % 16 of the chunk in byte
+ * (i % 4) + 4 * (i / 8), low nibble for i % 8 < 4, high nibble otherwise.
+ * sq_packed4_bytes(rows, K) = ceil(rows / 16) * KW * 512 bytes; padding zero.
  */
 #ifndef SQ_H
 #define SQ_H
@@ -247,13 +255,18 @@ sq_status sq_rmsnorm_quant_per_token(const void *h_f16, int64_t M, int64_t K, in
  * 1/sqrt(K) go into the weight scale as one exact 1/K.  With rotate == 0 the
  * same calls quantize to 4 bits without the transform (smoothing alone, or
  * S = I with smooth = ones: the other columns of the paper's comparison).
- * Codes are 4-bit values in [-7, 7] stored one per byte in the packed int8
- * layout, so sq_w8a8_gemm multiplies them unchanged (int32 sums exact).
+ * Activation codes are 4-bit values in [-7, 7] stored one per byte in the
+ * packed int8 layout; weight codes two per byte in the packed 4-bit layout,
+ * which sq_w4_gemm widens to int8 in registers (half the weight bytes).
  * Shapes: 16 <= K <= 8192, K % 16 == 0, and K a power of two when rotated
  * (SQ_ERR_SHAPE otherwise).
  */
 
-/* Bytes of workspace sq_w4_fold_weights needs: 2 * K * N (0 when out of range). */
+/* Bytes of a packed 4-bit operand (0 when an argument is out of range). */
+int64_t sq_packed4_bytes(int64_t rows, int64_t K);
+
+/* Bytes of workspace sq_w4_fold_weights needs: 2 * K * N + sq_packed_bytes(N, K)
+ * (0 when out of range). */
 int64_t sq_w4_workspace_bytes(int64_t K, int64_t N);
 
 /*
@@ -264,15 +277,15 @@ int64_t sq_w4_workspace_bytes(int64_t K, int64_t N);
  * non-finite value scale NaN and codes 0).
  *   w          fp16 [K][ldw]
  *   smooth     float [K] (s from sq_smoothing_factors, or ones for S = I)
- *   wq         packed int8, sq_packed_bytes(N, K) bytes, written, padding zero
+ *   wq4        packed 4-bit, sq_packed4_bytes(N, K) bytes, written, padding zero
  *   w_scale    float [N], written
  *   workspace  device buffer of sq_w4_workspace_bytes(K, N) bytes, 16-byte
- *              aligned, caller-owned: W is transposed into it first; its
- *              contents afterwards are unspecified
+ *              aligned, caller-owned: W transposed, then the codes one per
+ *              byte; its contents afterwards are unspecified
  * Asynchronous.
  */
 sq_status sq_w4_fold_weights(const void *w_f16, int64_t K, int64_t N, int64_t ldw,
-                             const float *smooth, int rotate, int8_t *wq, float *w_scale,
+                             const float *smooth, int rotate, uint8_t *wq4, float *w_scale,
                              void *workspace, void *stream);
 
 /*
@@ -289,6 +302,17 @@ sq_status sq_w4_fold_weights(const void *w_f16, int64_t K, int64_t N, int64_t ld
 sq_status sq_a4_quant_per_token(const void *x_f16, int64_t M, int64_t K, int64_t ldx,
                                 const float *inv_smooth, int rotate, int8_t *xq, float *x_scale,
                                 void *stream);
+
+/*
+ * The product with 4-bit weights: as sq_w8a8_gemm, with wq4 in the packed
+ * 4-bit layout (codes widened to int8 in registers before the int8 matrix
+ * instruction, so the sums and the epilogue are exactly sq_w8a8_gemm's for
+ * the same codes).  xq holds int8 codes (sq_a4_quant_per_token's 4-bit ones,
+ * or any int8).  Asynchronous.
+ */
+sq_status sq_w4_gemm(const int8_t *xq, const float *x_scale, const uint8_t *wq4,
+                     const float *w_scale, int64_t M, int64_t N, int64_t K, void *y,
+                     int64_t ldy, int out_kind, void *stream);
 
 /*
  * The W8A8 product on int8 matrix cores with a fused dequantizing epilogue

@@ -56,7 +56,7 @@ def test_status_strings_and_version(sq):
         s = sq.status_str(code)
         assert s.startswith("SQ_")
     assert sq.status_str(99) == "unknown sq_status"
-    assert sq.lib().sq_version() == 10400
+    assert sq.lib().sq_version() == 10500
     assert sq.SQ_MAX_K * 128 * 128 < 2 ** 31 and sq.SQ_MAX_K % 16 == 0
 
 
@@ -237,7 +237,7 @@ def test_w4_fold_rejects(sq, kw, expect):
 
 
 def test_w4_workspace_bytes(sq):
-    assert sq.sq_w4_workspace_bytes(4096, 4096) == 2 * 4096 * 4096
+    assert sq.sq_w4_workspace_bytes(4096, 4096) == 2 * 4096 * 4096 + 4096 * 4096
     assert sq.sq_w4_workspace_bytes(64, 0) == 0
     assert sq.sq_w4_workspace_bytes(40, 8) == 0 and sq.sq_w4_workspace_bytes(64, -1) == 0
 
@@ -358,3 +358,53 @@ def test_layout_helper_matches_header_formula():
                 seen[off] = True
         assert np.all(buf[~seen] == 0)
         assert np.array_equal(unpack(buf, rows, K), R)
+
+
+def test_layout4_helper_matches_header_formula():
+    """The packed 4-bit layout of tests/layout.py against the formula stated in
+    include/sq.h, nibble by nibble."""
+    import numpy as np
+    from layout import pack4, packed4_bytes, unpack4
+    text = open(HEADER).read()
+    assert "((r / 16) * KW + k / 64) * 512 +" in text and "((k % 64) / 16) * 128 + (r % 16) * 8" in text
+    for rows, K in [(1, 16), (17, 80), (35, 208)]:
+        R = np.random.default_rng(rows + 1).integers(-8, 8, (rows, K)).astype(np.int8)
+        buf = pack4(R)
+        KW = -(-K // 64)
+        assert buf.size == packed4_bytes(rows, K) == -(-rows // 16) * KW * 512
+        seen = np.zeros((buf.size, 2), bool)
+        for r in range(rows):
+            for k in range(K):
+                i = k % 16
+                off = ((r // 16) * KW + k // 64) * 512 + ((k % 64) // 16) * 128 + (r % 16) * 8 \
+                    + (i % 4) + 4 * (i // 8)
+                hi = (i % 8) >= 4
+                nib = (int(buf[off]) >> (4 if hi else 0)) & 0xF
+                assert (nib - 16 if nib >= 8 else nib) == R[r, k]
+                seen[off, int(hi)] = True
+        assert all(((int(b) >> (4 * h)) & 0xF) == 0
+                   for (o, h) in zip(*np.nonzero(~seen)) for b in [buf[o]])
+        assert np.array_equal(unpack4(buf, rows, K), R)
+
+
+def _g4(sq, xq=P, xs=P, wq=P, ws=P, M=32, N=32, K=64, y=P, ldy=32, kind=0):
+    return sq.lib().sq_w4_gemm(xq, xs, wq, ws, M, N, K, y, ldy, kind, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(kind=3), "SQ_ERR_KIND"),
+    (dict(wq=None), "SQ_ERR_NULL"),
+    (dict(xs=None), "SQ_ERR_NULL"),
+    (dict(K=100), "SQ_ERR_SHAPE"),
+    (dict(ldy=16), "SQ_ERR_SHAPE"),
+    (dict(wq=MIS), "SQ_ERR_ALIGN"),
+    (dict(y=P + 1), "SQ_ERR_ALIGN"),
+])
+def test_w4_gemm_rejects(sq, kw, expect):
+    assert sq.status_str(_g4(sq, **kw)).startswith(expect)
+
+
+def test_packed4_bytes(sq):
+    assert sq.packed4_bytes(16, 64) == 512 and sq.packed4_bytes(17, 80) == 2 * 2 * 512
+    assert sq.packed4_bytes(0, 64) == 0 and sq.packed4_bytes(4, 40) == 0
+    assert sq.sq_w4_workspace_bytes(4096, 4096) == 2 * 4096 * 4096 + sq.packed_bytes(4096, 4096)

@@ -3,8 +3,9 @@ key machinery, core discovery; referee major comment 1 on Eq. (8) and (9)).
 
 The activation and weight quantizers run the same float butterflies in the
 same order as the oracle, so their 4-bit codes and scales must be bit-exact,
-rotated or not; the W4A4 chain then goes through the unchanged int8 product
-(fp16 output within 2^-10).  The paper's comparison -- original, smoothing,
+rotated or not (weights packed two codes per byte, unpacked here by an
+independent numpy permutation); the product with 4-bit weights must give the
+oracle's int32 sums exactly and its fp16 outputs within 2^-10.  The paper's comparison -- original, smoothing,
 rotation, smoothing then rotation -- is measured from the GPU's outputs and
 must equal the oracle's measures; Eq. (8) and Eq. (9) are checked on the
 GPU's rotated maxima of massive-outlier tokens.
@@ -13,7 +14,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from layout import padding_is_zero, unpack
+from layout import pack, pack4, padding4_is_zero, padding_is_zero, unpack, unpack4
 
 pytestmark = pytest.mark.gpu
 
@@ -135,10 +136,38 @@ def test_w4_fold_matches_oracle(sq, dev, orc, name, K, N, ldw, rotate):
     wq, ws = sq.fold4(wv, T(s, dev), rotate)
     rq, rs = orc.fold4_weights(w, s, rotate)
     g = H(wq)
-    assert np.array_equal(unpack(g, N_, K_), rq)
-    assert padding_is_zero(g, N_, K_)
+    assert np.array_equal(unpack4(g, N_, K_), rq)
+    assert padding4_is_zero(g, N_, K_)
     assert same_bits(H(ws), rs)
     del torch
+
+
+# token counts 1..64 run the decode kernel, 65 and up the tile kernel (as for
+# the 8-bit product)
+GEMM4_SHAPES = [(1, 1, 16), (3, 5, 48), (17, 100, 80), (40, 100, 320), (64, 70, 4096),
+                (65, 33, 64), (128, 128, 4096), (130, 129, 1040), (256, 384, 2048),
+                (1, 28672, 128), (16, 300, 8192), (513, 77, 112)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM4_SHAPES)
+def test_w4_gemm_matches_oracle(sq, dev, orc, M, N, K):
+    """Full int8 activation codes against every 4-bit weight code (-8 .. 7):
+    the int32 sums exact, the fp16 epilogue within 2^-10."""
+    xq = W.random_i8(1700 + M, M, K, -128, 127)
+    wq = W.random_i8(1701 + N, N, K, -8, 7)
+    xs = W.random_scales(1702, M)
+    ws = W.random_scales(1703, N)
+    xg, wg = T(pack(xq), dev), T(pack4(wq), dev)
+    acc = H(sq.gemm4(xg, None, wg, None, M, N, K, out_kind=sq.SQ_OUT_I32))
+    ref = orc.gemm_i32(xq, wq)
+    assert np.array_equal(acc, ref)
+    y = H(sq.gemm4(xg, T(xs, dev), wg, T(ws, dev), M, N, K)).astype(np.float64)
+    want = orc.dequant(ref, xs, ws).astype(np.float16).astype(np.float64)
+    err = np.abs(y - want) / np.maximum(np.abs(want), FLOOR)
+    assert err.max() <= TOL
+    # and the same codes through the 8-bit product give the same sums
+    acc8 = H(sq.gemm(xg, None, T(pack(wq), dev), None, M, N, K, out_kind=sq.SQ_OUT_I32))
+    assert np.array_equal(acc8, acc)
 
 
 def test_smoothing_factors_equal_the_fold(sq, dev, orc):
@@ -165,7 +194,7 @@ def w4a4_gpu(sq, dev, x, w, xcal, alpha, rotate):
         s, inv = sq.smoothing_factors(wv, sq.calibrate(T(xcal, dev)), alpha)
     wq, ws = sq.fold4(wv, s, rotate)
     xq, xs = sq.quant4(T(x, dev), inv, rotate)
-    return H(sq.gemm(xq, xs, wq, ws, x.shape[0], N, K)).astype(np.float64), H(xs)
+    return H(sq.gemm4(xq, xs, wq, ws, x.shape[0], N, K)).astype(np.float64), H(xs)
 
 
 @pytest.mark.parametrize("name,nrows", [("tiny", None), ("qkv4096", 24), ("massive4096", 24)])

@@ -10,10 +10,11 @@ Same-name calls (caller-allocated outputs, as in the C ABI):
     sq_calibrate_absmax, sq_smooth_fold_weights, sq_quant_act_per_token,
     sq_w8a8_gemm, sq_packed_bytes, sq_pack_i8, sq_unpack_i8,
     sq_fold_norm_weight, sq_rmsnorm_quant_per_token, sq_smoothing_factors,
-    sq_w4_workspace_bytes, sq_w4_fold_weights, sq_a4_quant_per_token
+    sq_w4_workspace_bytes, sq_w4_fold_weights, sq_a4_quant_per_token,
+    sq_packed4_bytes, sq_w4_gemm
 Allocating helpers built on them:
     calibrate, fold, quant, gemm, smoothed_linear, pack_i8, unpack_i8,
-    fold_norm_weight, rmsnorm_quant, smoothing_factors, fold4, quant4
+    fold_norm_weight, rmsnorm_quant, smoothing_factors, fold4, quant4, gemm4
 
 The int8 codes (xq, wq) travel as flat int8 tensors in the packed operand
 order the C ABI documents (16-row x 64-byte fragments of 1 KiB); their sizes
@@ -47,7 +48,7 @@ EXPORTS = ("sq_status_str", "sq_version", "sq_packed_bytes", "sq_calibrate_absma
            "sq_smooth_fold_weights", "sq_quant_act_per_token", "sq_w8a8_gemm", "sq_pack_i8",
            "sq_unpack_i8", "sq_fold_norm_weight", "sq_rmsnorm_quant_per_token",
            "sq_smoothing_factors", "sq_w4_workspace_bytes", "sq_w4_fold_weights",
-           "sq_a4_quant_per_token")
+           "sq_a4_quant_per_token", "sq_packed4_bytes", "sq_w4_gemm")
 
 _LIB = None
 
@@ -96,6 +97,10 @@ def lib() -> ctypes.CDLL:
         L.sq_w4_workspace_bytes.argtypes = [i64, i64]
         L.sq_w4_fold_weights.restype = ci
         L.sq_w4_fold_weights.argtypes = [vp, i64, i64, i64, vp, ci, vp, vp, vp, vp]
+        L.sq_packed4_bytes.restype = i64
+        L.sq_packed4_bytes.argtypes = [i64, i64]
+        L.sq_w4_gemm.restype = ci
+        L.sq_w4_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i64, ci, vp]
         L.sq_a4_quant_per_token.restype = ci
         L.sq_a4_quant_per_token.argtypes = [vp, i64, i64, i64, vp, ci, vp, vp, vp]
         _LIB = L
@@ -109,6 +114,11 @@ def status_str(status: int) -> str:
 def packed_bytes(rows: int, K: int) -> int:
     """Bytes of a packed int8 operand of `rows` rows of K codes."""
     return int(lib().sq_packed_bytes(int(rows), int(K)))
+
+
+def packed4_bytes(rows: int, K: int) -> int:
+    """Bytes of a packed 4-bit operand of `rows` rows of K codes."""
+    return int(lib().sq_packed4_bytes(int(rows), int(K)))
 
 
 def _check(st: int, call: str) -> None:
@@ -276,22 +286,50 @@ def sq_w4_workspace_bytes(K: int, N: int) -> int:
     return int(lib().sq_w4_workspace_bytes(int(K), int(N)))
 
 
-def sq_w4_fold_weights(w, smooth, rotate: bool, wq, w_scale, workspace, stream=None) -> None:
-    """4-bit codes (packed int8) and scales of H (s W) per output channel, or
-    of s W with rotate False; workspace: uint8/int8 device buffer of
+def _need_packed4(t, rows, K, name):
+    torch = _torch()
+    _need(t, torch.uint8, name, 1)
+    if not t.is_contiguous() or t.numel() < packed4_bytes(rows, K):
+        raise ValueError(f"{name}: expected a contiguous uint8 buffer of "
+                         f"{packed4_bytes(rows, K)} bytes (packed 4-bit {rows} x {K} codes)")
+
+
+def sq_w4_fold_weights(w, smooth, rotate: bool, wq4, w_scale, workspace, stream=None) -> None:
+    """4-bit codes (packed two per byte, uint8) and scales of H (s W) per
+    output channel, or of s W with rotate False; workspace: a device buffer of
     sq_w4_workspace_bytes(K, N) bytes."""
     torch = _torch()
     _need(w, torch.float16, "w", 2)
     _need(smooth, torch.float32, "smooth", 1)
     _need(w_scale, torch.float32, "w_scale", 1)
     K, N = w.shape
-    _need_packed(wq, N, K, "wq")
+    _need_packed4(wq4, N, K, "wq4")
+    wq = wq4
     if not workspace.is_cuda or workspace.numel() * workspace.element_size() < \
             sq_w4_workspace_bytes(K, N):
         raise ValueError("workspace: expected a GPU buffer of sq_w4_workspace_bytes(K, N) bytes")
     _check(lib().sq_w4_fold_weights(_ptr(w), K, N, _ld(w), _ptr(smooth), 1 if rotate else 0,
                                     _ptr(wq), _ptr(w_scale), _ptr(workspace),
                                     _stream(stream, w.device)), "sq_w4_fold_weights")
+
+
+def sq_w4_gemm(xq, x_scale, wq4, w_scale, y, K: int, out_kind: int = SQ_OUT_F16,
+               stream=None) -> None:
+    """y [M][N] from packed int8 xq (M tokens) and packed 4-bit wq4 (N
+    channels) of K codes each."""
+    torch = _torch()
+    if out_kind == SQ_OUT_F16:
+        _need(x_scale, torch.float32, "x_scale", 1)
+        _need(w_scale, torch.float32, "w_scale", 1)
+        _need(y, torch.float16, "y", 2)
+    else:
+        _need(y, torch.int32, "y", 2)
+    M, N = y.shape
+    _need_packed(xq, M, K, "xq")
+    _need_packed4(wq4, N, K, "wq4")
+    _check(lib().sq_w4_gemm(_ptr(xq), _ptr(x_scale), _ptr(wq4), _ptr(w_scale), M, N, int(K),
+                            _ptr(y), _ld(y), int(out_kind), _stream(stream, xq.device)),
+           "sq_w4_gemm")
 
 
 def sq_a4_quant_per_token(x, inv_smooth, rotate: bool, xq, x_scale, stream=None) -> None:
@@ -410,16 +448,25 @@ def smoothing_factors(w, act_absmax, alpha: float, stream=None):
 
 
 def fold4(w, smooth, rotate: bool, stream=None):
-    """Returns (packed 4-bit codes of the N output channels, w_scale)."""
+    """Returns (packed 4-bit codes of the N output channels (uint8), w_scale)."""
     torch = _torch()
     K, N = w.shape
-    wq = torch.empty(packed_bytes(N, K), dtype=torch.int8, device=w.device)
+    wq = torch.empty(packed4_bytes(N, K), dtype=torch.uint8, device=w.device)
     ws = torch.empty(N, dtype=torch.float32, device=w.device)
     work = torch.empty(max(16, sq_w4_workspace_bytes(K, N)), dtype=torch.uint8, device=w.device)
     sq_w4_fold_weights(w, smooth, rotate, wq, ws, work, stream=stream)
     if hasattr(stream, "cuda_stream"):
         work.record_stream(stream)      # freed only once that stream is past the call
     return wq, ws
+
+
+def gemm4(xq, x_scale, wq4, w_scale, M: int, N: int, K: int, out_kind: int = SQ_OUT_F16,
+          stream=None):
+    torch = _torch()
+    dt = torch.float16 if out_kind == SQ_OUT_F16 else torch.int32
+    y = torch.empty((M, N), dtype=dt, device=xq.device)
+    sq_w4_gemm(xq, x_scale, wq4, w_scale, y, K, out_kind, stream=stream)
+    return y
 
 
 def quant4(x, inv_smooth, rotate: bool, stream=None):

@@ -39,7 +39,18 @@
 // k_gemm_skinny (M <= 64, decode): one workgroup per 16 output channels; its
 // 4 waves split the k windows, stream the weight fragments (the dominant HBM
 // traffic) with 8 1 KiB loads in flight each (non-temporal for up to 32
-// tokens), and combine their partial sums through LDS.
+// tokens), and combine their partial sums through LDS.  Activation lanes of
+// token rows past M load nothing.  k_gemm_skinny_w4 is its 4-bit-weight form.
+//
+// With W4 the weights are 4-bit codes, two per byte (the Smooth Rotation
+// variant's W4A4): each 16 x 64 fragment is 512 bytes in the same lane order,
+// a lane's 8 bytes holding its 16 codes as two's-complement nibbles (byte j
+// of each 4-byte half: code j in the low nibble, code j + 4 in the high one).
+// They are widened to the int8 operand in registers (unpack4), so the matrix
+// instruction, the sums and the epilogue are the 8-bit ones; the decode kernel
+// streams half the bytes, the tile kernel widens while staging into LDS.
+#include <type_traits>
+
 #include "sq_device.h"
 #include "sq.h"
 
@@ -57,6 +68,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 // 16-byte buffer load; offsets at or past the buffer's extent read as zero.
 __device__ __forceinline__ v4i bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// 8-byte buffer load; offsets at or past the buffer's extent read as zero.
+__device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+}
+
+// Four two's-complement nibbles (one per byte, high nibbles clear) to four
+// int8: with t = n ^ 8 = code + 8 in [0, 15], (t + 0x78) ^ 0x80 is t - 8 mod
+// 256 in every byte, and t + 0x78 <= 0x87 never carries into the next byte.
+__device__ __forceinline__ int sext4(uint32_t n) {
+    return (int)(((n ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u);
+}
+
+// A lane's 8 bytes of 4-bit codes to its 16-byte int8 operand.
+__device__ __forceinline__ v4i unpack4(uint2 p) {
+    constexpr uint32_t LO = 0x0F0F0F0Fu;
+    return v4i{sext4(p.x & LO), sext4((p.x >> 4) & LO), sext4(p.y & LO), sext4((p.y >> 4) & LO)};
 }
 
 __device__ __forceinline__ v4i mfma(const v4i &a, const v4i &b, const v4i &c) {
@@ -121,7 +151,7 @@ constexpr int T_FRAG = 1024;         // bytes per packed fragment
 constexpr int T_SLICE = 8 * T_FRAG;  // weight bytes per k-step
 constexpr int T_WAVES = 8;
 
-template <bool F16OUT>
+template <bool F16OUT, bool W4>
 __global__ void __launch_bounds__(64 * T_WAVES)
 k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
             const float *__restrict__ xs, const float *__restrict__ ws, int M, int N, int K,
@@ -146,8 +176,9 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
     const int nbw = min(8, rbw - (n0 >> 4));
     const __amdgpu_buffer_rsrc_t rx =
         make_rsrc(X + (int64_t)(m0 >> 4) * KW * T_FRAG, (int64_t)nbx * KW * T_FRAG);
+    constexpr int WF = W4 ? T_FRAG / 2 : T_FRAG;           // weight bytes per fragment
     const __amdgpu_buffer_rsrc_t rw =
-        make_rsrc(W + (int64_t)(n0 >> 4) * KW * T_FRAG, (int64_t)nbw * KW * T_FRAG);
+        make_rsrc(W + (int64_t)(n0 >> 4) * KW * WF, (int64_t)nbw * KW * WF);
 
     // the epilogue's scales are loaded now and wait in registers
     float xsv[2];
@@ -179,16 +210,18 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
         const int b = wave * 2 + i;
         xbase[i] = b < nbx ? (uint32_t)(b * KW * T_FRAG + lane * 16) : OOB_BASE;
     }
-    // weight slice: 512 chunks of 16 bytes, one per thread; chunk tid = fragment tid / 64, lane tid % 64
+    // weight slice: 512 chunks of 16 bytes (8 with W4), one per thread; chunk
+    // tid = fragment tid / 64, lane tid % 64
     uint32_t wbase;
     {
         const int b = tid >> 6;
-        wbase = b < nbw ? (uint32_t)(b * KW * T_FRAG + (tid & 63) * 16) : OOB_BASE;
+        wbase = b < nbw ? (uint32_t)(b * KW * WF + (tid & 63) * (WF / 64)) : OOB_BASE;
     }
     // Offset of k window t (uniform): windows past the last one get OOB_WIN, so
     // every lane's base + offset falls past the buffer and reads zero.  Bases
     // are < 2^25 or OOB_BASE, offsets < 2^21 or OOB_WIN, so sums never wrap.
     auto win = [&](int t) -> uint32_t { return t < KW ? (uint32_t)t * T_FRAG : OOB_WIN; };
+    auto winw = [&](int t) -> uint32_t { return t < KW ? (uint32_t)t * WF : OOB_WIN; };
 
     v4i acc[2][8];
 #pragma unroll
@@ -197,16 +230,22 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
         for (int j = 0; j < 8; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
     v4i xr[4][2];    // activation ring: steps t .. t+3
-    v4i wst[2];      // weight staging ring: steps t+2, t+3
+    // weight staging ring: steps t+2, t+3 (W4: the packed 8 bytes, widened on
+    // their way to LDS)
+    typename std::conditional<W4, uint2, v4i>::type wst[2];
     v4i wf[8];       // weight fragments of the current step
     auto load_x = [&](int slot, int t) {
         const uint32_t wo = win(t);
 #pragma unroll
         for (int i = 0; i < 2; ++i) xr[slot][i] = bload(rx, xbase[i] + wo);
     };
-    auto load_w = [&](int slot, int t) { wst[slot] = bload(rw, wbase + win(t)); };
+    auto load_w = [&](int slot, int t) {
+        if constexpr (W4) wst[slot] = bload8(rw, wbase + winw(t));
+        else wst[slot] = bload(rw, wbase + winw(t));
+    };
     auto store_w = [&](int slot, int buf) {
-        *reinterpret_cast<v4i *>(&ldsw[buf][tid * 16]) = wst[slot];
+        if constexpr (W4) *reinterpret_cast<v4i *>(&ldsw[buf][tid * 16]) = unpack4(wst[slot]);
+        else *reinterpret_cast<v4i *>(&ldsw[buf][tid * 16]) = wst[slot];
     };
 
     // prologue: weight slices 0 and 1 in LDS, slice 2 staged, activations 0..2 in flight
@@ -316,7 +355,8 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
 
 // ---- small token counts (decode) ---------------------------------------------------------
 
-constexpr int S_UNROLL = 8;   // k windows in flight per wave
+constexpr int S_UNROLL = 8;   // k windows in flight per wave (twice that with 4-bit weights,
+                              // so a lane keeps the same 128 bytes of weights in flight)
 
 template <int MB, bool F16OUT>
 __global__ void __launch_bounds__(256)
@@ -332,6 +372,12 @@ k_gemm_skinny(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
     const int rbx = (M + 15) >> 4;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (int64_t)rbx * KW * T_FRAG);
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (int64_t)nb * KW * T_FRAG, (int64_t)KW * T_FRAG);
+    // Up to 2 row blocks, lanes of token rows past M (zero padding) load no
+    // activations: at M = 1, 15 of 16 lanes.  (With more row blocks this
+    // kernel keeps its registers low instead, which measured faster.)
+    bool xrow[MB];
+#pragma unroll
+    for (int b = 0; b < MB; ++b) xrow[b] = MB > 2 || b * 16 + (lane & 15) < M;
 
     v4i acc[MB];
 #pragma unroll
@@ -353,7 +399,8 @@ k_gemm_skinny(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
                 wf[u] = bload(rw, t < KW ? (uint32_t)(t * T_FRAG + lane * 16) : OOB);
 #pragma unroll
             for (int b = 0; b < MB; ++b)
-                xf[u][b] = bload(rx, (t < KW && b < rbx) ? (uint32_t)((b * KW + t) * T_FRAG + lane * 16) : OOB);
+                xf[u][b] = bload(rx, (t < KW && b < rbx && xrow[b])
+                                         ? (uint32_t)((b * KW + t) * T_FRAG + lane * 16) : OOB);
         }
 #pragma unroll
         for (int u = 0; u < S_UNROLL; ++u)
@@ -382,9 +429,115 @@ k_gemm_skinny(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
     }
 }
 
-hipError_t launch_gemm(const int8_t *xq, const float *x_scale, const int8_t *wq,
-                       const float *w_scale, int64_t M, int64_t N, int64_t K, void *y,
-                       int64_t ldy, int out_kind, hipStream_t st) {
+// 4-bit weights (decode): a workgroup takes CB channel blocks, so each
+// activation fragment it loads feeds CB weight fragments (with 512-byte
+// weight fragments the activations would otherwise be most of a window's
+// bytes), keeps a window batch's loads ahead of its products, and widens the
+// codes just before the matrix instruction.
+template <int MB, bool F16OUT, int CB>
+__global__ void __launch_bounds__(256)
+k_gemm_skinny_w4(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
+              const float *__restrict__ xs, const float *__restrict__ ws, int M, int N, int K,
+              void *__restrict__ Y, int64_t ldy, int vec_ok) {
+    __shared__ __align__(16) v4i part[3][CB][MB][64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int nb0 = blockIdx.x * CB;             // first 16-channel block
+    const int KW = (K + 63) >> 6;
+    const int rbx = (M + 15) >> 4;
+    const int rbw = (N + 15) >> 4;
+    const int ncb = rbw - nb0 < CB ? rbw - nb0 : CB;   // blocks present
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (int64_t)rbx * KW * T_FRAG);
+    constexpr int WF = T_FRAG / 2;                          // weight bytes per fragment
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(W + (int64_t)nb0 * KW * WF, (int64_t)ncb * KW * WF);
+    // A lane feeds token row 16 b + lane % 16 of each activation fragment:
+    // rows past M are zero padding, so those lanes load nothing (at M = 1,
+    // 15 of 16 lanes), which keeps the activations' L2 traffic to the real rows.
+    bool xrow[MB];
+#pragma unroll
+    for (int b = 0; b < MB; ++b) xrow[b] = b * 16 + (lane & 15) < M;
+
+    v4i acc[CB][MB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+        for (int b = 0; b < MB; ++b) acc[c][b] = v4i{0, 0, 0, 0};
+    // wave w takes windows w, w + 4, w + 8, ...: the 4 waves stream adjacent KiB
+    constexpr int SU = MB >= 3 ? S_UNROLL / 2 : S_UNROLL;
+    for (int t0 = wave; t0 < KW; t0 += 4 * SU) {
+        v4i xf[SU][MB];
+        uint2 wp[SU][CB];   // the packed codes as loaded
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+            const int t = t0 + 4 * u;
+            // the weights are read exactly once (non-temporal up to 32 tokens)
+#pragma unroll
+            for (int c = 0; c < CB; ++c) {
+                const bool in = t < KW && c < ncb;
+                const int64_t goff = ((int64_t)(nb0 + c) * KW + t) * WF;
+                const uint32_t boff = in ? (uint32_t)((c * KW + t) * WF) : OOB;
+                if constexpr (MB <= 2) {
+                    typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+                    const v2u p = in ? __builtin_nontemporal_load(
+                                           reinterpret_cast<const v2u *>(W + goff + lane * 8))
+                                     : v2u{0u, 0u};
+                    wp[u][c] = make_uint2(p[0], p[1]);
+                } else {
+                    wp[u][c] = bload8(rw, boff == OOB ? OOB : boff + lane * 8);
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < MB; ++b)
+                xf[u][b] = bload(rx, (t < KW && b < rbx && xrow[b])
+                                         ? (uint32_t)((b * KW + t) * T_FRAG + lane * 16) : OOB);
+        }
+        // all of the batch's loads stay ahead of its products
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+#pragma unroll
+            for (int c = 0; c < CB; ++c) {
+                const v4i wf = unpack4(wp[u][c]);
+#pragma unroll
+                for (int b = 0; b < MB; ++b) acc[c][b] = mfma(wf, xf[u][b], acc[c][b]);
+            }
+        }
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+#pragma unroll
+            for (int b = 0; b < MB; ++b) part[wave - 1][c][b][lane] = acc[c][b];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+#pragma unroll
+            for (int w = 0; w < 3; ++w) {
+                const v4i p = part[w][c][b][lane];
+                acc[c][b][0] += p[0];
+                acc[c][b][1] += p[1];
+                acc[c][b][2] += p[2];
+                acc[c][b][3] += p[3];
+            }
+            if (c >= ncb) continue;
+            const int m = b * 16 + (lane & 15);
+            const float xsm = (F16OUT && m < M) ? xs[m] : 0.0f;
+            store4<F16OUT>(Y, ldy, (vec_ok & 1) != 0, m, (nb0 + c) * 16 + (lane >> 4) * 4, M, N,
+                           acc[c][b], xsm, ws);
+        }
+    }
+}
+
+template <bool W4>
+hipError_t launch_gemm_any(const int8_t *xq, const float *x_scale, const int8_t *wq,
+                           const float *w_scale, int64_t M, int64_t N, int64_t K, void *y,
+                           int64_t ldy, int out_kind, hipStream_t st) {
     if (M <= 0 || N <= 0) return hipSuccess;
     const bool f16 = out_kind == SQ_OUT_F16;
     // bit 0: stores of 4 elements (8-byte fp16 / 16-byte int32) line up with
@@ -399,19 +552,30 @@ hipError_t launch_gemm(const int8_t *xq, const float *x_scale, const int8_t *wq,
         const int tiles_n = (n + T_BN - 1) / T_BN;
         const dim3 grid((unsigned)(tiles_m * tiles_n));
         if (f16)
-            k_gemm_tile<true><<<grid, dim3(64 * T_WAVES), 0, st>>>(xq, wq, x_scale, w_scale, m, n, k, y, ldy,
-                                                          tiles_m, tiles_n, vec_ok);
+            k_gemm_tile<true, W4><<<grid, dim3(64 * T_WAVES), 0, st>>>(
+                xq, wq, x_scale, w_scale, m, n, k, y, ldy, tiles_m, tiles_n, vec_ok);
         else
-            k_gemm_tile<false><<<grid, dim3(64 * T_WAVES), 0, st>>>(xq, wq, x_scale, w_scale, m, n, k, y, ldy,
-                                                           tiles_m, tiles_n, vec_ok);
+            k_gemm_tile<false, W4><<<grid, dim3(64 * T_WAVES), 0, st>>>(
+                xq, wq, x_scale, w_scale, m, n, k, y, ldy, tiles_m, tiles_n, vec_ok);
         return hipGetLastError();
     }
-    const dim3 grid((unsigned)((n + 15) / 16));
-#define SQ_SK(MB)                                                                                  \
-    (f16 ? (k_gemm_skinny<MB, true><<<grid, dim3(256), 0, st>>>(xq, wq, x_scale, w_scale, m, n, k, \
-                                                                y, ldy, vec_ok), 0)                \
-         : (k_gemm_skinny<MB, false><<<grid, dim3(256), 0, st>>>(xq, wq, x_scale, w_scale, m, n,   \
-                                                                 k, y, ldy, vec_ok), 0))
+    constexpr int CB = 2;    // channel blocks per workgroup of the 4-bit decode kernel
+    const dim3 grid((unsigned)(W4 ? ((n + 15) / 16 + CB - 1) / CB : (n + 15) / 16));
+#define SQ_SK(MB)                                                                                \
+    do {                                                                                         \
+        if (W4 && f16)                                                                           \
+            k_gemm_skinny_w4<MB, true, CB><<<grid, dim3(256), 0, st>>>(                          \
+                xq, wq, x_scale, w_scale, m, n, k, y, ldy, vec_ok);                              \
+        else if (W4)                                                                             \
+            k_gemm_skinny_w4<MB, false, CB><<<grid, dim3(256), 0, st>>>(                         \
+                xq, wq, x_scale, w_scale, m, n, k, y, ldy, vec_ok);                              \
+        else if (f16)                                                                            \
+            k_gemm_skinny<MB, true><<<grid, dim3(256), 0, st>>>(xq, wq, x_scale, w_scale, m, n, \
+                                                                k, y, ldy, vec_ok);              \
+        else                                                                                     \
+            k_gemm_skinny<MB, false><<<grid, dim3(256), 0, st>>>(xq, wq, x_scale, w_scale, m, n, \
+                                                                 k, y, ldy, vec_ok);             \
+    } while (0)
     const int64_t mb = (M + 15) / 16;
     if (mb == 1) SQ_SK(1);
     else if (mb == 2) SQ_SK(2);
@@ -419,6 +583,19 @@ hipError_t launch_gemm(const int8_t *xq, const float *x_scale, const int8_t *wq,
     else SQ_SK(4);
 #undef SQ_SK
     return hipGetLastError();
+}
+
+hipError_t launch_gemm(const int8_t *xq, const float *x_scale, const int8_t *wq,
+                       const float *w_scale, int64_t M, int64_t N, int64_t K, void *y,
+                       int64_t ldy, int out_kind, hipStream_t st) {
+    return launch_gemm_any<false>(xq, x_scale, wq, w_scale, M, N, K, y, ldy, out_kind, st);
+}
+
+hipError_t launch_gemm_w4(const int8_t *xq, const float *x_scale, const uint8_t *wq4,
+                          const float *w_scale, int64_t M, int64_t N, int64_t K, void *y,
+                          int64_t ldy, int out_kind, hipStream_t st) {
+    return launch_gemm_any<true>(xq, x_scale, reinterpret_cast<const int8_t *>(wq4), w_scale, M,
+                                 N, K, y, ldy, out_kind, st);
 }
 
 }  // namespace sq

@@ -52,4 +52,26 @@ hipError_t launch_unpack_i8(const int8_t *src, int64_t rows, int64_t K, int8_t *
     return hipGetLastError();
 }
 
+// Packed int8 codes in [-8, 7] -> the packed 4-bit layout: every lane chunk
+// of 16 codes (16 bytes) becomes 8 bytes, byte j of each half holding code j
+// of that half's 8 in its low nibble and code j + 4 in its high nibble (two's
+// complement).  One thread per chunk; padding stays zero.
+__global__ void __launch_bounds__(256)
+k_pack4_from8(const int8_t *__restrict__ src, uint8_t *__restrict__ dst, int64_t chunks) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= chunks) return;
+    const uint4 v = *reinterpret_cast<const uint4 *>(src + c * 16);
+    constexpr uint32_t LO = 0x0F0F0F0Fu;
+    const uint2 o = make_uint2((v.x & LO) | ((v.y & LO) << 4), (v.z & LO) | ((v.w & LO) << 4));
+    *reinterpret_cast<uint2 *>(dst + c * 8) = o;
+}
+
+hipError_t launch_pack4_from8(const int8_t *src, int64_t rows, int64_t K, uint8_t *dst,
+                              hipStream_t st) {
+    const int64_t chunks = (rows + 15) / 16 * ((K + 63) / 64) * 64;
+    if (chunks <= 0) return hipSuccess;
+    k_pack4_from8<<<dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, st>>>(src, dst, chunks);
+    return hipGetLastError();
+}
+
 }  // namespace sq

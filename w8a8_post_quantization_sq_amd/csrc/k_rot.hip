@@ -375,15 +375,20 @@ k_transpose_f16(const uint16_t *__restrict__ w, int64_t K, int64_t N, int64_t ld
 }
 
 hipError_t launch_fold4(const uint16_t *w, int64_t K, int64_t N, int64_t ldw, const float *s,
-                        int rotate, int8_t *wq, float *w_scale, uint16_t *wt, hipStream_t st) {
+                        int rotate, uint8_t *wq4, float *w_scale, uint8_t *work, hipStream_t st) {
     if (N <= 0) return hipSuccess;
+    // workspace: W^T (N x K fp16), then the codes one per byte (packed int8 order)
+    uint16_t *wt = reinterpret_cast<uint16_t *>(work);
+    int8_t *q8 = reinterpret_cast<int8_t *>(work + 2 * K * N);
     k_transpose_f16<<<dim3((unsigned)((N + 63) / 64), (unsigned)((K + 63) / 64)), dim3(256), 0,
                       st>>>(w, K, N, ldw, wt);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     // with the rotation the weight scale carries the 1/K of the two transforms
-    return launch_quant4_rows(wt, N, K, K, s, rotate, rotate ? 1.0f / (float)K : 1.0f, wq,
-                              w_scale, st);
+    if (e == hipSuccess)
+        e = launch_quant4_rows(wt, N, K, K, s, rotate, rotate ? 1.0f / (float)K : 1.0f, q8,
+                               w_scale, st);
+    if (e == hipSuccess) e = launch_pack4_from8(q8, N, K, wq4, st);
+    return e;
 }
 
 }  // namespace sq

@@ -145,7 +145,7 @@ SQ_API const char *sq_status_str(int status) {
     }
 }
 
-SQ_API int sq_version(void) { return 10400; }
+SQ_API int sq_version(void) { return 10500; }
 
 SQ_API int64_t sq_packed_bytes(int64_t rows, int64_t K) {
     if (rows < 0 || rows >= kMaxDim || !k_ok(K)) return 0;
@@ -229,9 +229,14 @@ SQ_API sq_status sq_smoothing_factors(const void *w_f16, int64_t K, int64_t N, i
     return check_factors(g->host, K);
 }
 
+SQ_API int64_t sq_packed4_bytes(int64_t rows, int64_t K) {
+    if (rows < 0 || rows >= kMaxDim || !k_ok(K)) return 0;
+    return ((rows + 15) / 16) * ((K + 63) / 64) * 512;
+}
+
 SQ_API int64_t sq_w4_workspace_bytes(int64_t K, int64_t N) {
     if (N < 0 || N >= kMaxDim || !k_ok(K)) return 0;
-    return 2 * K * N;
+    return 2 * K * N + sq_packed_bytes(N, K);
 }
 
 // K for the 4-bit calls: a whole number of 16-code rows up to the register-
@@ -254,8 +259,9 @@ SQ_API sq_status sq_a4_quant_per_token(const void *x_f16, int64_t M, int64_t K, 
 }
 
 SQ_API sq_status sq_w4_fold_weights(const void *w_f16, int64_t K, int64_t N, int64_t ldw,
-                                    const float *smooth, int rotate, int8_t *wq, float *w_scale,
+                                    const float *smooth, int rotate, uint8_t *wq4, float *w_scale,
                                     void *workspace, void *stream) {
+    uint8_t *wq = wq4;
     if (!smooth || (N > 0 && (!w_f16 || !wq || !w_scale || !workspace))) return SQ_ERR_NULL;
     if (N < 0 || N >= kMaxDim || !k4_ok(K, rotate) || (N > 0 && ldw < N)) return SQ_ERR_SHAPE;
     if (!aligned16(smooth)) return SQ_ERR_ALIGN;
@@ -264,7 +270,27 @@ SQ_API sq_status sq_w4_fold_weights(const void *w_f16, int64_t K, int64_t N, int
         return SQ_ERR_ALIGN;
     return hip_status(sq::launch_fold4(static_cast<const uint16_t *>(w_f16), K, N, ldw, smooth,
                                        rotate != 0, wq, w_scale,
-                                       static_cast<uint16_t *>(workspace), as_stream(stream)));
+                                       static_cast<uint8_t *>(workspace), as_stream(stream)));
+}
+
+SQ_API sq_status sq_w4_gemm(const int8_t *xq, const float *x_scale, const uint8_t *wq4,
+                            const float *w_scale, int64_t M, int64_t N, int64_t K, void *y,
+                            int64_t ldy, int out_kind, void *stream) {
+    if (out_kind != SQ_OUT_F16 && out_kind != SQ_OUT_I32) return SQ_ERR_KIND;
+    const bool work = M > 0 && N > 0;
+    if (work && (!xq || !wq4 || !y)) return SQ_ERR_NULL;
+    if (work && out_kind == SQ_OUT_F16 && (!x_scale || !w_scale)) return SQ_ERR_NULL;
+    if (M < 0 || N < 0 || M >= kMaxDim || N >= kMaxDim || !k_ok(K)) return SQ_ERR_SHAPE;
+    if (work && ldy < N) return SQ_ERR_SHAPE;
+    if (work && ((M + 255) / 256) * ((N + 127) / 128) >= kMaxDim) return SQ_ERR_SHAPE;
+    if (work) {
+        if (!aligned16(xq) || !aligned16(wq4)) return SQ_ERR_ALIGN;
+        if (out_kind == SQ_OUT_F16 && (!aligned16(x_scale) || !aligned16(w_scale))) return SQ_ERR_ALIGN;
+        if (((uintptr_t)y % (out_kind == SQ_OUT_F16 ? 2u : 4u)) != 0) return SQ_ERR_ALIGN;
+    }
+    if (!work) return SQ_OK;
+    return hip_status(sq::launch_gemm_w4(xq, x_scale, wq4, w_scale, M, N, K, y, ldy, out_kind,
+                                         as_stream(stream)));
 }
 
 SQ_API sq_status sq_quant_act_per_token(const void *x_f16, int64_t M, int64_t K, int64_t ldx,

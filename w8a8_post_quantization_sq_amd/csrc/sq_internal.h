@@ -53,10 +53,21 @@ hipError_t launch_quant4_rows(const uint16_t *x, int64_t M, int64_t K, int64_t l
                               const float *mult, int rotate, float post, int8_t *q, float *scale,
                               hipStream_t st);
 
-// 4-bit weights: W transposed into wt (N x K fp16), then its rows quantized
-// with mult = s (and post = 1/K when rotated)
+// 4-bit weights: W transposed into the workspace (N x K fp16), its rows
+// quantized with mult = s (and post = 1/K when rotated) into the workspace's
+// second part (packed int8 order), then packed two codes per byte into wq4
 hipError_t launch_fold4(const uint16_t *w, int64_t K, int64_t N, int64_t ldw, const float *s,
-                        int rotate, int8_t *wq, float *w_scale, uint16_t *wt, hipStream_t st);
+                        int rotate, uint8_t *wq4, float *w_scale, uint8_t *work, hipStream_t st);
+
+// packed int8 codes in [-8, 7] -> packed 4-bit codes
+hipError_t launch_pack4_from8(const int8_t *src, int64_t rows, int64_t K, uint8_t *dst,
+                              hipStream_t st);
+
+// the product with 4-bit weights (packed two per byte), widened to int8 in
+// registers; everything else as launch_gemm
+hipError_t launch_gemm_w4(const int8_t *xq, const float *x_scale, const uint8_t *wq4,
+                          const float *w_scale, int64_t M, int64_t N, int64_t K, void *y,
+                          int64_t ldy, int out_kind, hipStream_t st);
 
 hipError_t launch_pack_i8(const int8_t *src, int64_t rows, int64_t K, int64_t ld, int8_t *dst,
                           hipStream_t st);
