@@ -16,11 +16,12 @@ time), the product kernel against the int8 matrix-core roofline (its duration
 from HIP events around it on the library's stream, on every 10th timed step),
 the per-stage GPU times from a separate pass with events between the stages,
 the serving-time layer (A4 + A5/A6, the two calls a deployed layer makes per
-batch), the fused RMS-norm + quantization that replaces A4 when 1/s is
-folded into the normalization in front of the layer (outside the step), and
-the rotated 4-bit quantizer of Smooth Rotation against the unrotated one
-(outside the step), and the CPU oracle timed on a bounded sample as a
-baseline.
+batch), and, outside the step: the decode-size layer (M = 1 and 16 tokens
+against an 8192 x 28672 layer, the metric's M <= 16 half, as GB/s of its
+weights), the fused RMS-norm + quantization that replaces A4 when 1/s is
+folded into the normalization in front of the layer, the rotated 4-bit
+quantizer of Smooth Rotation against the unrotated one, and the CPU oracle
+timed on a bounded sample as a baseline.
 """
 import argparse
 import hashlib
@@ -104,6 +105,68 @@ def cpu_baseline(inp, wl, budget_s):
     }
 
 
+def decode_leg(torch, workloads, sq, L, dev, stream, hs, launches):
+    """The serving-time layer at decode sizes, the metric's M <= 16 half: the
+    decode8192 workload (K 8192, N 28672) folded once, its codes copied 4 times
+    (940 MB, beyond the 256 MB Infinity Cache) and the copies taken in turn, so
+    every product streams its weights from HBM.  Per token count, the product
+    alone and quantization + product, each as `launches` launches between one
+    event pair; GB/s = the weights' bytes / time."""
+    wl = workloads.WORKLOADS["decode8192"]
+    inp = workloads.generate(wl)
+    K, N = wl.K, wl.N
+    w = torch.from_numpy(inp.w).to(dev)
+    ax = torch.empty(K, dtype=torch.float32, device=dev)
+    s = torch.empty(K, dtype=torch.float32, device=dev)
+    inv = torch.empty(K, dtype=torch.float32, device=dev)
+    wsc = torch.empty(N, dtype=torch.float32, device=dev)
+    wq0 = torch.empty(sq.packed_bytes(N, K), dtype=torch.int8, device=dev)
+    xcal = torch.from_numpy(inp.x_cal).to(dev)
+    st = L.sq_calibrate_absmax(xcal.data_ptr(), xcal.shape[0], K, K, ax.data_ptr(), 0, hs)
+    st |= L.sq_smooth_fold_weights(w.data_ptr(), K, N, N, ax.data_ptr(), float(wl.alpha), None,
+                                   s.data_ptr(), inv.data_ptr(), wq0.data_ptr(), wsc.data_ptr(), hs)
+    if st:
+        raise RuntimeError("decode fold failed")
+    del w
+    copies = [wq0] + [wq0.clone() for _ in range(3)]
+    out = {"workload": "decode8192: K 8192, N 28672, 4 weight copies taken in turn",
+           "weight_bytes": N * K, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    for m in (1, 16):
+        x = torch.from_numpy(inp.x[:m].copy()).to(dev)
+        xq = torch.empty(sq.packed_bytes(m, K), dtype=torch.int8, device=dev)
+        xs = torch.empty(m, dtype=torch.float32, device=dev)
+        y = torch.empty((m, N), dtype=torch.float16, device=dev)
+
+        def run(i, with_quant):
+            r = 0
+            if with_quant:
+                r |= L.sq_quant_act_per_token(x.data_ptr(), m, K, K, inv.data_ptr(), xq.data_ptr(),
+                                              xs.data_ptr(), hs)
+            r |= L.sq_w8a8_gemm(xq.data_ptr(), xs.data_ptr(), copies[i % 4].data_ptr(),
+                                wsc.data_ptr(), m, N, K, y.data_ptr(), N, sq.SQ_OUT_F16, hs)
+            return r
+        res = {}
+        for with_quant in (True, False, True, False):
+            for i in range(8):
+                if run(i, with_quant):
+                    raise RuntimeError("decode layer call failed")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(launches):
+                run(i, with_quant)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[with_quant] = e0.elapsed_time(e1) * 1e3 / launches
+        gb_layer = N * K / (res[True] * 1e-6) / 1e9
+        gb_gemm = N * K / (res[False] * 1e-6) / 1e9
+        out[f"M{m}"] = {"layer_us": round(res[True], 2), "gemm_us": round(res[False], 2),
+                        "layer_gbs": round(gb_layer, 1), "gemm_gbs": round(gb_gemm, 1),
+                        "layer_frac": round(gb_layer / PEAK_HBM_GBS, 4),
+                        "gemm_frac": round(gb_gemm / PEAK_HBM_GBS, 4)}
+        log(f"decode M={m}: layer {res[True]:.2f} us, product {res[False]:.2f} us")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +185,9 @@ def main():
     ap.add_argument("--rot-launches", type=int, default=100,
                     help="launches of the rotated 4-bit quantizer (and of the unrotated one) "
                          "timed between one pair of events (0: skip)")
+    ap.add_argument("--decode-launches", type=int, default=40,
+                    help="launches per token count of the decode layer (decode8192: K 8192, "
+                         "N 28672, M 1 and 16), timed over 4 rotated weight copies (0: skip)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle layer work in the CPU baseline (0: skip)")
     ap.add_argument("--copy-kernel", type=int, default=0, metavar="MIB",
@@ -301,6 +367,10 @@ def main():
                "transform_flops": int(M * K * (K.bit_length() - 1))}
         log(f"rotated 4-bit quant {us[1]:.2f} us, unrotated {us[0]:.2f} us")
 
+    decode = None
+    if args.decode_launches > 0:
+        decode = decode_leg(torch, workloads, sq, L, dev, stream, hs, args.decode_launches)
+
     ops = 2.0 * M * N * K
     ms_step = wall * 1e3 / args.steps
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
@@ -337,6 +407,7 @@ def main():
                      "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                      "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": traffic,
                      "per_launch": f"2*M*N*K = {ops:.4g} int8 ops per launch"},
+        "decode": decode,
         "norm_fold": norm,
         "rotation_w4": rot,
         "cpu_baseline": None,

@@ -298,7 +298,11 @@ def test_quant_matches_oracle(sq, dev, orc, name):
     assert padding_is_zero(g, inp.x.shape[0], wl.K)
 
 
+# up to 64 tokens and K <= 16384 the one-token-per-workgroup form runs (one or
+# two chunks per lane), beyond it the 8-row forms
 @pytest.mark.parametrize("M,K,ld", [(1, 16, 16), (3, 48, 56), (17, 2064, 2064), (2, 4112, 4128),
+                                    (4, 11008, 11024), (64, 16384, 16384), (33, 8192, 8192),
+                                    (65, 4096, 4096), (64, 16400, 16400),
                                     (5, 32784, 32784), (2, 40000, 40000), (1, 131056, 131056)])
 def test_quant_ragged_long_and_strided(sq, dev, orc, M, K, ld):
     x = W.random_f16(600 + K, M, ld, 2.0)
@@ -331,9 +335,11 @@ def test_quant_ties_and_degenerate_rows(sq, dev, orc):
 
 # ---- A5 + A6 the product -----------------------------------------------------------------
 
-# token counts 1..64 run the decode kernel (1, 2, 3 or 4 activation row blocks;
-# non-temporal weight loads up to 2 of them), 65 and up the tile kernel
+# token counts 1..64 run the decode kernels (1, 2, 3 or 4 activation row blocks;
+# non-temporal weight loads up to 2 of them; two channel blocks per workgroup at
+# 9..32 tokens, also with an odd block count), 65 and up the tile kernel
 GEMM_SHAPES = [(1, 1, 16), (3, 5, 48), (17, 100, 80), (40, 100, 320), (49, 1000, 1088),
+               (9, 64, 4096), (25, 33, 256), (32, 48, 1024),
                (64, 70, 4096), (65, 33, 64), (100, 200, 64), (128, 128, 4096),
                (130, 129, 1040), (256, 384, 2048), (1, 28672, 128), (16, 300, 8192), (513, 77, 112)]
 

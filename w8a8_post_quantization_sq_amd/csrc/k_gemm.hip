@@ -40,7 +40,8 @@
 // 4 waves split the k windows, stream the weight fragments (the dominant HBM
 // traffic) with 8 1 KiB loads in flight each (non-temporal for up to 32
 // tokens), and combine their partial sums through LDS.  Activation lanes of
-// token rows past M load nothing.  k_gemm_skinny_w4 is its 4-bit-weight form.
+// token rows past M load nothing.  k_gemm_skinny_cb takes two channel blocks
+// per workgroup (4-bit weights, and 8-bit ones at 9 to 32 tokens).
 //
 // With W4 the weights are 4-bit codes, two per byte (the Smooth Rotation
 // variant's W4A4): each 16 x 64 fragment is 512 bytes in the same lane order,
@@ -429,14 +430,15 @@ k_gemm_skinny(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
     }
 }
 
-// 4-bit weights (decode): a workgroup takes CB channel blocks, so each
-// activation fragment it loads feeds CB weight fragments (with 512-byte
-// weight fragments the activations would otherwise be most of a window's
-// bytes), keeps a window batch's loads ahead of its products, and widens the
-// codes just before the matrix instruction.
-template <int MB, bool F16OUT, int CB>
+// Decode with CB channel blocks per workgroup: each activation fragment a
+// wave loads feeds CB weight fragments, which halves the activations' share
+// of the L2 traffic (with 16 or more real token rows, and always with 4-bit
+// weights, whose 512-byte fragments would otherwise be outweighed by the
+// activations); a window batch's loads stay ahead of its products, and 4-bit
+// codes are widened just before the matrix instruction.
+template <int MB, bool F16OUT, bool W4, int CB>
 __global__ void __launch_bounds__(256)
-k_gemm_skinny_w4(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
+k_gemm_skinny_cb(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
               const float *__restrict__ xs, const float *__restrict__ ws, int M, int N, int K,
               void *__restrict__ Y, int64_t ldy, int vec_ok) {
     __shared__ __align__(16) v4i part[3][CB][MB][64];
@@ -449,7 +451,7 @@ k_gemm_skinny_w4(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
     const int rbw = (N + 15) >> 4;
     const int ncb = rbw - nb0 < CB ? rbw - nb0 : CB;   // blocks present
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (int64_t)rbx * KW * T_FRAG);
-    constexpr int WF = T_FRAG / 2;                          // weight bytes per fragment
+    constexpr int WF = W4 ? T_FRAG / 2 : T_FRAG;           // weight bytes per fragment
     const __amdgpu_buffer_rsrc_t rw =
         make_rsrc(W + (int64_t)nb0 * KW * WF, (int64_t)ncb * KW * WF);
     // A lane feeds token row 16 b + lane % 16 of each activation fragment:
@@ -467,8 +469,8 @@ k_gemm_skinny_w4(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
     // wave w takes windows w, w + 4, w + 8, ...: the 4 waves stream adjacent KiB
     constexpr int SU = MB >= 3 ? S_UNROLL / 2 : S_UNROLL;
     for (int t0 = wave; t0 < KW; t0 += 4 * SU) {
-        v4i xf[SU][MB];
-        uint2 wp[SU][CB];   // the packed codes as loaded
+        v4i xf[SU][MB], wf[SU][CB];
+        uint2 wp[SU][CB];   // 4-bit: the packed codes as loaded
 #pragma unroll
         for (int u = 0; u < SU; ++u) {
             const int t = t0 + 4 * u;
@@ -478,14 +480,22 @@ k_gemm_skinny_w4(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
                 const bool in = t < KW && c < ncb;
                 const int64_t goff = ((int64_t)(nb0 + c) * KW + t) * WF;
                 const uint32_t boff = in ? (uint32_t)((c * KW + t) * WF) : OOB;
-                if constexpr (MB <= 2) {
-                    typedef unsigned int v2u __attribute__((ext_vector_type(2)));
-                    const v2u p = in ? __builtin_nontemporal_load(
-                                           reinterpret_cast<const v2u *>(W + goff + lane * 8))
-                                     : v2u{0u, 0u};
-                    wp[u][c] = make_uint2(p[0], p[1]);
+                if constexpr (W4) {
+                    if constexpr (MB <= 2) {
+                        typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+                        const v2u p = in ? __builtin_nontemporal_load(
+                                               reinterpret_cast<const v2u *>(W + goff + lane * 8))
+                                         : v2u{0u, 0u};
+                        wp[u][c] = make_uint2(p[0], p[1]);
+                    } else {
+                        wp[u][c] = bload8(rw, boff == OOB ? OOB : boff + lane * 8);
+                    }
+                } else if constexpr (MB <= 2) {
+                    wf[u][c] = in ? __builtin_nontemporal_load(
+                                        reinterpret_cast<const v4i *>(W + goff + lane * 16))
+                                  : v4i{0, 0, 0, 0};
                 } else {
-                    wp[u][c] = bload8(rw, boff == OOB ? OOB : boff + lane * 8);
+                    wf[u][c] = bload(rw, boff == OOB ? OOB : boff + lane * 16);
                 }
             }
 #pragma unroll
@@ -499,9 +509,9 @@ k_gemm_skinny_w4(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
         for (int u = 0; u < SU; ++u) {
 #pragma unroll
             for (int c = 0; c < CB; ++c) {
-                const v4i wf = unpack4(wp[u][c]);
+                if constexpr (W4) wf[u][c] = unpack4(wp[u][c]);
 #pragma unroll
-                for (int b = 0; b < MB; ++b) acc[c][b] = mfma(wf, xf[u][b], acc[c][b]);
+                for (int b = 0; b < MB; ++b) acc[c][b] = mfma(wf[u][c], xf[u][b], acc[c][b]);
             }
         }
     }
@@ -559,15 +569,20 @@ hipError_t launch_gemm_any(const int8_t *xq, const float *x_scale, const int8_t 
                 xq, wq, x_scale, w_scale, m, n, k, y, ldy, tiles_m, tiles_n, vec_ok);
         return hipGetLastError();
     }
-    constexpr int CB = 2;    // channel blocks per workgroup of the 4-bit decode kernel
-    const dim3 grid((unsigned)(W4 ? ((n + 15) / 16 + CB - 1) / CB : (n + 15) / 16));
+    // The two-block form for 4-bit weights, and for 8-bit weights with more
+    // than 8 tokens in 1 or 2 row blocks; the one-block kernel otherwise (at
+    // M <= 8 its activation loads are mostly skipped, and with 3 or 4 row
+    // blocks its low register count measured faster).
+    const int64_t nblk = (n + 15) / 16;
+    const bool two = W4 || (M > 8 && M <= 32);
+    const dim3 grid((unsigned)(two ? (nblk + 1) / 2 : nblk));
 #define SQ_SK(MB)                                                                                \
     do {                                                                                         \
-        if (W4 && f16)                                                                           \
-            k_gemm_skinny_w4<MB, true, CB><<<grid, dim3(256), 0, st>>>(                          \
+        if (two && f16)                                                                          \
+            k_gemm_skinny_cb<MB, true, W4, 2><<<grid, dim3(256), 0, st>>>(                       \
                 xq, wq, x_scale, w_scale, m, n, k, y, ldy, vec_ok);                              \
-        else if (W4)                                                                             \
-            k_gemm_skinny_w4<MB, false, CB><<<grid, dim3(256), 0, st>>>(                         \
+        else if (two)                                                                            \
+            k_gemm_skinny_cb<MB, false, W4, 2><<<grid, dim3(256), 0, st>>>(                      \
                 xq, wq, x_scale, w_scale, m, n, k, y, ldy, vec_ok);                              \
         else if (f16)                                                                            \
             k_gemm_skinny<MB, true><<<grid, dim3(256), 0, st>>>(xq, wq, x_scale, w_scale, m, n, \

@@ -317,10 +317,83 @@ k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t l
     }
 }
 
+// Decode-size batches (M <= 64): one token per workgroup of 1024 threads, one
+// (K <= 8192) or two chunks of 8 channels per lane, so a token's loads all go
+// out at once over 16 waves and each reduction is one wave shuffle plus one
+// LDS round (every thread folds the 16 wave results in the same order, so the
+// double sum of squares is the same everywhere).  Each lane writes its 8 codes
+// straight into the packed layout (half of a 16-byte piece); rows of the last
+// 16-row block past M get zero codes.
+template <int CPL, bool NORM, int QMAX>
+__global__ void __launch_bounds__(1024)
+k_quant_row1(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
+             const float *__restrict__ inv_s, double eps, int8_t *__restrict__ xq,
+             float *__restrict__ x_scale) {
+    __shared__ uint32_t s_max[16];
+    __shared__ double s_ss[16];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t m = blockIdx.x;
+    const bool real = m < M;
+    const uint16_t *row = x + (real ? m : 0) * ldx;
+    float v[CPL][8];
+    uint32_t amax = 0;
+    double ss = 0.0;
+    Chunk ch[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int64_t k = ((int64_t)c * 1024 + threadIdx.x) * 8;
+        if (real && k < K) ch[c] = load8(row, inv_s, k);
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int64_t k = ((int64_t)c * 1024 + threadIdx.x) * 8;
+        if (real && k < K) scale8<NORM>(ch[c], v[c], amax, &ss);
+    }
+    amax = wave_max_u32(amax);
+    if (NORM) ss = wave_sum_f64(ss);
+    if (lane == 0) {
+        s_max[wave] = amax;
+        if (NORM) s_ss[wave] = ss;
+    }
+    __syncthreads();
+    uint32_t a = 0;
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        a = a > s_max[w] ? a : s_max[w];
+        if (NORM) t += s_ss[w];
+    }
+    float scale, r;
+    bool zero;
+    row_params<QMAX>(a, scale, r, zero);
+    if (NORM) scale = norm_scale(a, t, K, eps);
+    if (real && threadIdx.x == 0) x_scale[m] = scale;
+    zero = zero || !real;
+    const int64_t KW = (K + 63) >> 6;
+    int8_t *base = xq + (((m >> 4) * KW) << 10) + (m & 15) * 16;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int64_t k = ((int64_t)c * 1024 + threadIdx.x) * 8;
+        if (k < KW * 64) {   // codes past K (padding) are zero
+            const uint2 q = (k < K) ? quant8<QMAX>(v[c], r, zero) : make_uint2(0u, 0u);
+            *reinterpret_cast<uint2 *>(base + ((k >> 6) << 10) + (((k >> 4) & 3) << 8) + (k & 15)) = q;
+        }
+    }
+}
+
 template <bool NORM, int QMAX>
 hipError_t launch_rows(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const float *inv_s,
                        double eps, int8_t *xq, float *x_scale, hipStream_t st) {
     if (M <= 0) return hipSuccess;
+    if (M <= 64 && K <= 16384) {   // decode sizes: one token per workgroup
+        const dim3 g((unsigned)((M + 15) / 16 * 16));
+        if (K <= 8192)
+            k_quant_row1<1, NORM, QMAX><<<g, dim3(1024), 0, st>>>(x, M, K, ldx, inv_s, eps, xq, x_scale);
+        else
+            k_quant_row1<2, NORM, QMAX><<<g, dim3(1024), 0, st>>>(x, M, K, ldx, inv_s, eps, xq, x_scale);
+        return hipGetLastError();
+    }
     // every row of the padded row blocks, 8 rows per workgroup
     const int64_t groups = (M + 15) / 16 * 2;
     const int64_t cpl = (K + 1023) / 1024;        // chunks of 8 per lane, 2 waves per row
