@@ -16,7 +16,7 @@ time), the product kernel against the int8 matrix-core roofline (its duration
 from HIP events around it on the library's stream, on every 10th timed step),
 the per-stage GPU times from a separate pass with events between the stages,
 the serving-time layer (A4 + A5/A6, the two calls a deployed layer makes per
-batch), and, outside the step: the decode-size layer (M = 1 and 16 tokens
+batch), and, outside the step: the decode-size layer (M = 1, 4 and 16 tokens
 against an 8192 x 28672 layer, the metric's M <= 16 half, as GB/s of its
 weights), the fused RMS-norm + quantization that replaces A4 when 1/s is
 folded into the normalization in front of the layer, the rotated 4-bit
@@ -110,8 +110,8 @@ def decode_leg(torch, workloads, sq, L, dev, stream, hs, launches):
     decode8192 workload (K 8192, N 28672) folded once, its codes copied 4 times
     (940 MB, beyond the 256 MB Infinity Cache) and the copies taken in turn, so
     every product streams its weights from HBM.  Per token count, the product
-    alone and quantization + product, each as `launches` launches between one
-    event pair; GB/s = the weights' bytes / time."""
+    alone and quantization + product (M = 1, 4, 16), each as `launches`
+    launches between one event pair; GB/s = the weights' bytes / time."""
     wl = workloads.WORKLOADS["decode8192"]
     inp = workloads.generate(wl)
     K, N = wl.K, wl.N
@@ -131,7 +131,7 @@ def decode_leg(torch, workloads, sq, L, dev, stream, hs, launches):
     copies = [wq0] + [wq0.clone() for _ in range(3)]
     out = {"workload": "decode8192: K 8192, N 28672, 4 weight copies taken in turn",
            "weight_bytes": N * K, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    for m in (1, 16):
+    for m in (1, 4, 16):
         x = torch.from_numpy(inp.x[:m].copy()).to(dev)
         xq = torch.empty(sq.packed_bytes(m, K), dtype=torch.int8, device=dev)
         xs = torch.empty(m, dtype=torch.float32, device=dev)
@@ -187,7 +187,7 @@ def main():
                          "timed between one pair of events (0: skip)")
     ap.add_argument("--decode-launches", type=int, default=40,
                     help="launches per token count of the decode layer (decode8192: K 8192, "
-                         "N 28672, M 1 and 16), timed over 4 rotated weight copies (0: skip)")
+                         "N 28672, M 1, 4 and 16), timed over 4 rotated weight copies (0: skip)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle layer work in the CPU baseline (0: skip)")
     ap.add_argument("--copy-kernel", type=int, default=0, metavar="MIB",

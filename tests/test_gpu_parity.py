@@ -336,10 +336,12 @@ def test_quant_ties_and_degenerate_rows(sq, dev, orc):
 # ---- A5 + A6 the product -----------------------------------------------------------------
 
 # token counts 1..64 run the decode kernels (1, 2, 3 or 4 activation row blocks;
-# non-temporal weight loads up to 2 of them; two channel blocks per workgroup at
-# 9..32 tokens, also with an odd block count), 65 and up the tile kernel
+# non-temporal weight loads up to 2 of them; at 9..32 tokens with 512 or more
+# channel blocks, 2, 4 or 7 blocks per workgroup, also with a partial last
+# workgroup), 65 and up the tile kernel
 GEMM_SHAPES = [(1, 1, 16), (3, 5, 48), (17, 100, 80), (40, 100, 320), (49, 1000, 1088),
                (9, 64, 4096), (25, 33, 256), (32, 48, 1024),
+               (16, 28672, 128), (9, 28672, 64), (24, 8192, 64), (32, 12304, 64), (20, 8200, 64),
                (64, 70, 4096), (65, 33, 64), (100, 200, 64), (128, 128, 4096),
                (130, 129, 1040), (256, 384, 2048), (1, 28672, 128), (16, 300, 8192), (513, 77, 112)]
 

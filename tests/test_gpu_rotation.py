@@ -145,6 +145,7 @@ def test_w4_fold_matches_oracle(sq, dev, orc, name, K, N, ldw, rotate):
 # token counts 1..64 run the decode kernel, 65 and up the tile kernel (as for
 # the 8-bit product)
 GEMM4_SHAPES = [(1, 1, 16), (3, 5, 48), (17, 100, 80), (40, 100, 320), (64, 70, 4096),
+                (16, 28672, 64), (33, 8200, 64),
                 (65, 33, 64), (128, 128, 4096), (130, 129, 1040), (256, 384, 2048),
                 (1, 28672, 128), (16, 300, 8192), (513, 77, 112)]
 

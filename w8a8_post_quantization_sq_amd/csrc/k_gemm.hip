@@ -40,8 +40,8 @@
 // 4 waves split the k windows, stream the weight fragments (the dominant HBM
 // traffic) with 8 1 KiB loads in flight each (non-temporal for up to 32
 // tokens), and combine their partial sums through LDS.  Activation lanes of
-// token rows past M load nothing.  k_gemm_skinny_cb takes two channel blocks
-// per workgroup (4-bit weights, and 8-bit ones at 9 to 32 tokens).
+// token rows past M load nothing.  k_gemm_skinny_cb takes 2, 4 or 7 channel
+// blocks per workgroup (4-bit weights, and 8-bit ones at 9 to 32 tokens).
 //
 // With W4 the weights are 4-bit codes, two per byte (the Smooth Rotation
 // variant's W4A4): each 16 x 64 fragment is 512 bytes in the same lane order,
@@ -431,11 +431,11 @@ k_gemm_skinny(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
 }
 
 // Decode with CB channel blocks per workgroup: each activation fragment a
-// wave loads feeds CB weight fragments, which halves the activations' share
-// of the L2 traffic (with 16 or more real token rows, and always with 4-bit
-// weights, whose 512-byte fragments would otherwise be outweighed by the
-// activations); a window batch's loads stay ahead of its products, and 4-bit
-// codes are widened just before the matrix instruction.
+// wave loads feeds CB weight fragments, which divides the activations' share
+// of the L2 traffic by CB (it matters with 16 or more real token rows, and
+// always with 4-bit weights, whose 512-byte fragments would otherwise be
+// outweighed by the activations); a window batch's loads stay ahead of its
+// products, and 4-bit codes are widened just before the matrix instruction.
 template <int MB, bool F16OUT, bool W4, int CB>
 __global__ void __launch_bounds__(256)
 k_gemm_skinny_cb(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
@@ -544,6 +544,53 @@ k_gemm_skinny_cb(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
     }
 }
 
+// Channel blocks per decode workgroup.  8-bit weights: one (k_gemm_skinny) up
+// to 8 tokens, where the activation loads are mostly skipped, and from 3 row
+// blocks on, where its low register count measured best; at 9..32 tokens the
+// one of 2, 4, 7 whose workgroup count fills whole rounds of the 256 CUs best
+// (N = 28672: 7, one workgroup per CU), as long as at least 512 blocks exist.
+// 4-bit weights: 2 at one row block, 4 beyond (measured).
+inline int decode_blocks(bool w4, int M, int64_t nblk) {
+    if (w4) return M <= 16 ? 2 : 4;
+    if (M <= 8 || M > 32 || nblk < 512) return 1;
+    int best = 2;
+    double best_waste = 2.0;
+    for (int cb : {2, 4, 7}) {
+        const int64_t wg = (nblk + cb - 1) / cb;
+        const double waste = (double)((wg + 255) / 256 * 256) / (double)wg;
+        if (waste < best_waste - 1e-9) {
+            best = cb;
+            best_waste = waste;
+        }
+    }
+    return best;
+}
+
+template <int MB, bool F16OUT, bool W4>
+void launch_skinny(int cb, dim3 grid, hipStream_t st, const int8_t *xq, const int8_t *wq,
+                   const float *x_scale, const float *w_scale, int m, int n, int k, void *y,
+                   int64_t ldy, int vec_ok) {
+    const dim3 b(256);
+    if constexpr (!W4) {
+        if (cb == 1 || MB > 2) {
+            k_gemm_skinny<MB, F16OUT><<<grid, b, 0, st>>>(xq, wq, x_scale, w_scale, m, n, k, y,
+                                                          ldy, vec_ok);
+            return;
+        }
+    }
+    if constexpr (W4 || MB <= 2) {
+        if (cb == 2)
+            k_gemm_skinny_cb<MB, F16OUT, W4, 2><<<grid, b, 0, st>>>(xq, wq, x_scale, w_scale, m, n,
+                                                                   k, y, ldy, vec_ok);
+        else if (cb == 4)
+            k_gemm_skinny_cb<MB, F16OUT, W4, 4><<<grid, b, 0, st>>>(xq, wq, x_scale, w_scale, m, n,
+                                                                   k, y, ldy, vec_ok);
+        else if constexpr (!W4)
+            k_gemm_skinny_cb<MB, F16OUT, W4, 7><<<grid, b, 0, st>>>(xq, wq, x_scale, w_scale, m, n,
+                                                                   k, y, ldy, vec_ok);
+    }
+}
+
 template <bool W4>
 hipError_t launch_gemm_any(const int8_t *xq, const float *x_scale, const int8_t *wq,
                            const float *w_scale, int64_t M, int64_t N, int64_t K, void *y,
@@ -569,27 +616,15 @@ hipError_t launch_gemm_any(const int8_t *xq, const float *x_scale, const int8_t 
                 xq, wq, x_scale, w_scale, m, n, k, y, ldy, tiles_m, tiles_n, vec_ok);
         return hipGetLastError();
     }
-    // The two-block form for 4-bit weights, and for 8-bit weights with more
-    // than 8 tokens in 1 or 2 row blocks; the one-block kernel otherwise (at
-    // M <= 8 its activation loads are mostly skipped, and with 3 or 4 row
-    // blocks its low register count measured faster).
     const int64_t nblk = (n + 15) / 16;
-    const bool two = W4 || (M > 8 && M <= 32);
-    const dim3 grid((unsigned)(two ? (nblk + 1) / 2 : nblk));
-#define SQ_SK(MB)                                                                                \
-    do {                                                                                         \
-        if (two && f16)                                                                          \
-            k_gemm_skinny_cb<MB, true, W4, 2><<<grid, dim3(256), 0, st>>>(                       \
-                xq, wq, x_scale, w_scale, m, n, k, y, ldy, vec_ok);                              \
-        else if (two)                                                                            \
-            k_gemm_skinny_cb<MB, false, W4, 2><<<grid, dim3(256), 0, st>>>(                      \
-                xq, wq, x_scale, w_scale, m, n, k, y, ldy, vec_ok);                              \
-        else if (f16)                                                                            \
-            k_gemm_skinny<MB, true><<<grid, dim3(256), 0, st>>>(xq, wq, x_scale, w_scale, m, n, \
-                                                                k, y, ldy, vec_ok);              \
-        else                                                                                     \
-            k_gemm_skinny<MB, false><<<grid, dim3(256), 0, st>>>(xq, wq, x_scale, w_scale, m, n, \
-                                                                 k, y, ldy, vec_ok);             \
+    const int cb = decode_blocks(W4, m, nblk);
+    const dim3 grid((unsigned)((nblk + cb - 1) / cb));
+#define SQ_SK(MB)                                                                               \
+    do {                                                                                        \
+        if (f16) launch_skinny<MB, true, W4>(cb, grid, st, xq, wq, x_scale, w_scale, m, n, k, y, \
+                                             ldy, vec_ok);                                      \
+        else launch_skinny<MB, false, W4>(cb, grid, st, xq, wq, x_scale, w_scale, m, n, k, y,   \
+                                          ldy, vec_ok);                                         \
     } while (0)
     const int64_t mb = (M + 15) / 16;
     if (mb == 1) SQ_SK(1);
