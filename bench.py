@@ -164,6 +164,55 @@ def decode_leg(torch, workloads, sq, L, dev, stream, hs, launches):
                         "layer_frac": round(gb_layer / PEAK_HBM_GBS, 4),
                         "gemm_frac": round(gb_gemm / PEAK_HBM_GBS, 4)}
         log(f"decode M={m}: layer {res[True]:.2f} us, product {res[False]:.2f} us")
+
+    # The same layer as Smooth Rotation at 4 bits: factors, Hadamard-rotated
+    # 4-bit weights packed two per byte (half the bytes), rotated 4-bit tokens.
+    w = torch.from_numpy(inp.w).to(dev)
+    work = torch.empty(sq.sq_w4_workspace_bytes(K, N), dtype=torch.uint8, device=dev)
+    w4 = torch.empty(sq.packed4_bytes(N, K), dtype=torch.uint8, device=dev)
+    ws4 = torch.empty(N, dtype=torch.float32, device=dev)
+    st = L.sq_smoothing_factors(w.data_ptr(), K, N, N, ax.data_ptr(), float(wl.alpha),
+                                s.data_ptr(), inv.data_ptr(), hs)
+    st |= L.sq_w4_fold_weights(w.data_ptr(), K, N, N, s.data_ptr(), 1, w4.data_ptr(),
+                               ws4.data_ptr(), work.data_ptr(), hs)
+    torch.cuda.synchronize()
+    if st:
+        raise RuntimeError("4-bit decode fold failed")
+    del w, work
+    copies4 = [w4] + [w4.clone() for _ in range(3)]
+    w4a4 = {"what": "Smooth Rotation W4A4: rotated 4-bit tokens (sq_a4_quant_per_token, rotate=1) + "
+                    "product with 4-bit weights (sq_w4_gemm)", "weight_bytes": N * K // 2}
+    for m in (1, 16):
+        x = torch.from_numpy(inp.x[:m].copy()).to(dev)
+        xq = torch.empty(sq.packed_bytes(m, K), dtype=torch.int8, device=dev)
+        xs = torch.empty(m, dtype=torch.float32, device=dev)
+        y = torch.empty((m, N), dtype=torch.float16, device=dev)
+
+        def run4(i, with_quant):
+            r = 0
+            if with_quant:
+                r |= L.sq_a4_quant_per_token(x.data_ptr(), m, K, K, inv.data_ptr(), 1,
+                                             xq.data_ptr(), xs.data_ptr(), hs)
+            r |= L.sq_w4_gemm(xq.data_ptr(), xs.data_ptr(), copies4[i % 4].data_ptr(),
+                              ws4.data_ptr(), m, N, K, y.data_ptr(), N, sq.SQ_OUT_F16, hs)
+            return r
+        res = {}
+        for with_quant in (True, False, True, False):
+            for i in range(8):
+                if run4(i, with_quant):
+                    raise RuntimeError("4-bit decode layer call failed")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(launches):
+                run4(i, with_quant)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[with_quant] = e0.elapsed_time(e1) * 1e3 / launches
+        gb = N * K // 2 / (res[True] * 1e-6) / 1e9
+        w4a4[f"M{m}"] = {"layer_us": round(res[True], 2), "gemm_us": round(res[False], 2),
+                         "layer_gbs": round(gb, 1), "layer_frac": round(gb / PEAK_HBM_GBS, 4)}
+        log(f"decode W4A4 M={m}: layer {res[True]:.2f} us, product {res[False]:.2f} us")
+    out["w4a4"] = w4a4
     return out
 
 

@@ -78,8 +78,12 @@ def test_a4_matches_oracle(sq, dev, orc, name, m, rotate):
     check_a4(sq, dev, orc, inp.x, inv, rotate, f"{name} M={inp.x.shape[0]} rotate={rotate}")
 
 
+# up to 64 tokens at K = 4096 and 8192 the one-token-per-workgroup form runs,
+# beyond it the 4-rows-per-workgroup transposed form
 @pytest.mark.parametrize("M,K,ld", [(37, 16, 16), (5, 32, 40), (3, 256, 256), (9, 512, 512),
-                                    (33, 1024, 1032), (17, 2048, 2048), (2, 8192, 8200)])
+                                    (33, 1024, 1032), (17, 2048, 2048), (2, 8192, 8200),
+                                    (5, 4096, 4104), (64, 4096, 4096), (65, 4096, 4096),
+                                    (64, 8192, 8192), (66, 8192, 8192)])
 def test_a4_rotated_ragged_and_strided(sq, dev, orc, M, K, ld):
     x = W.random_f16(900 + K, M, ld, 3.0)
     inv = W.random_scales(901 + K, K, 0.05, 4.0)

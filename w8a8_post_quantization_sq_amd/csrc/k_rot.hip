@@ -320,12 +320,136 @@ k_quant4_rot_t(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx
     }
 }
 
+// Decode-size batches (M <= 64) with K = 4096 or 8192: one token per workgroup
+// of K / 8 threads (8 or 16 waves), each holding one chunk of 8 consecutive
+// elements, k = tid * 8 + e.  Stages h = 1, 2, 4 in registers, h = 8 .. 256
+// across the lanes of a wave (shuffles), then one LDS transpose: thread p <
+// 512 takes the elements p + 512 w of every wave w, so the wave bits are its
+// register index for the stages h = 512 .. K/2.  Same stage order and
+// butterflies as everywhere else.  The codes go to LDS in element order and
+// leave as packed 16-byte pieces.
+template <int WAVES>
+__global__ void __launch_bounds__(64 * WAVES)
+k_quant4_rot_row1(const uint16_t *__restrict__ x, int64_t M, int64_t ldx,
+                  const float *__restrict__ mult, float post, int8_t *__restrict__ q,
+                  float *__restrict__ scale) {
+    constexpr int K = 512 * WAVES;
+    __shared__ __align__(16) float tr[K];
+    __shared__ __align__(16) int8_t codes[K];
+    __shared__ uint32_t s_max[WAVES];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t m = blockIdx.x;
+    const bool real = m < M;
+    const uint16_t *row = x + (real ? m : 0) * ldx;
+    float v[8];
+    {
+        uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+        float4 f0 = make_float4(0.f, 0.f, 0.f, 0.f), f1 = f0;
+        if (real) {
+            raw = *reinterpret_cast<const uint4 *>(row + tid * 8);
+            f0 = *reinterpret_cast<const float4 *>(mult + tid * 8);
+            f1 = *reinterpret_cast<const float4 *>(mult + tid * 8 + 4);
+        }
+        const uint32_t h[4] = {raw.x, raw.y, raw.z, raw.w};
+        const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[2 * e] = h2f(h[e] & 0xffffu) * f[2 * e];
+            v[2 * e + 1] = h2f(h[e] >> 16) * f[2 * e + 1];
+        }
+    }
+#pragma unroll
+    for (int hb = 1; hb < 8; hb <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if ((e & hb) == 0) {
+                const float a = v[e], b = v[e + hb];
+                v[e] = a + b;
+                v[e + hb] = a - b;
+            }
+#pragma unroll
+    for (int t = 0; t < 6; ++t) {
+        const bool upper = (lane >> t) & 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float p = __shfl_xor(v[e], 1 << t, 64);
+            v[e] = upper ? p - v[e] : v[e] + p;
+        }
+    }
+    *reinterpret_cast<float4 *>(&tr[tid * 8]) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4 *>(&tr[tid * 8 + 4]) = make_float4(v[4], v[5], v[6], v[7]);
+    __syncthreads();
+    // thread p < 512: the elements p + 512 w, w = 0 .. WAVES-1 (the wave bits)
+    float u[WAVES];
+    uint32_t amax = 0;
+    if (tid < 512) {
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) u[w] = tr[tid + 512 * w];
+#pragma unroll
+        for (int hb = 1; hb < WAVES; hb <<= 1)
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w)
+                if ((w & hb) == 0) {
+                    const float a = u[w], b = u[w + hb];
+                    u[w] = a + b;
+                    u[w + hb] = a - b;
+                }
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            const uint32_t b = __float_as_uint(u[w]) & 0x7fffffffu;
+            amax = amax > b ? amax : b;
+        }
+    }
+    amax = wave_max_u32(amax);
+    if (lane == 0) s_max[wave] = amax;
+    __syncthreads();
+    uint32_t a = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) a = a > s_max[w] ? a : s_max[w];
+    float r = 0.0f;
+    bool zero = true;
+    if (a >= 0x7f800000u) {
+        if (real && tid == 0) scale[m] = __builtin_nanf("");
+    } else if (a == 0u) {
+        if (real && tid == 0) scale[m] = 0.0f;
+    } else {
+        const float af = __uint_as_float(a);
+        r = 7.0f / af;
+        zero = false;
+        if (real && tid == 0) scale[m] = (af / 7.0f) * post;
+    }
+    zero = zero || !real;
+    if (tid < 512) {
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            float c = __builtin_rintf(u[w] * r);
+            c = fminf(fmaxf(c, -7.0f), 7.0f);
+            codes[tid + 512 * w] = zero ? (int8_t)0 : (int8_t)(int)c;
+        }
+    }
+    __syncthreads();
+    // K / 16 pieces of 16 codes: piece j (k = 16 j ..) to window j / 4, quarter j % 4
+    constexpr int KW = K / 64;
+    int8_t *base = q + (((m >> 4) * KW) << 10) + (m & 15) * 16;
+    for (int j = tid; j < K / 16; j += 64 * WAVES)
+        *reinterpret_cast<v4i *>(base + ((j >> 2) << 10) + ((j & 3) << 8)) =
+            *reinterpret_cast<const v4i *>(&codes[j * 16]);
+}
+
 hipError_t launch_quant4_rows(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                               const float *mult, int rotate, float post, int8_t *q, float *scale,
                               hipStream_t st) {
     if (M <= 0) return hipSuccess;
     // unrotated: the per-token quantizer at 7 levels (post is 1 there)
     if (!rotate) return launch_quant4_plain(x, M, K, ldx, mult, q, scale, st);
+    if (M <= 64 && (K == 4096 || K == 8192)) {   // decode sizes: one token per workgroup
+        const dim3 g((unsigned)((M + 15) / 16 * 16));   // every row of the padded blocks
+        if (K == 4096) k_quant4_rot_row1<8><<<g, dim3(512), 0, st>>>(x, M, ldx, mult, post, q, scale);
+        else k_quant4_rot_row1<16><<<g, dim3(1024), 0, st>>>(x, M, ldx, mult, post, q, scale);
+        return hipGetLastError();
+    }
     if (K == 4096 || K == 8192) {
         const dim3 g((unsigned)((M + 15) / 16 * 4)), b(256);   // every row of the padded blocks
         const size_t lds = (size_t)RT * 64 * TP * sizeof(float);
