@@ -16,7 +16,9 @@ time), the product kernel against the int8 matrix-core roofline (its duration
 from HIP events around it on the library's stream, on every 10th timed step),
 the per-stage GPU times from a separate pass with events between the stages,
 the serving-time layer (A4 + A5/A6, the two calls a deployed layer makes per
-batch), and, outside the step: the decode-size layer (M = 1, 4 and 16 tokens
+batch), and, outside the step: the product at the other large-token
+configurations (down_proj 2048 x 11008 -> 4096, prefill 8192 x 8192 -> 3 x 8192),
+the decode-size layer (M = 1, 4 and 16 tokens
 against an 8192 x 28672 layer, the metric's M <= 16 half, as GB/s of its
 weights), the fused RMS-norm + quantization that replaces A4 when 1/s is
 folded into the normalization in front of the layer, the rotated 4-bit
@@ -103,6 +105,61 @@ def cpu_baseline(inp, wl, budget_s):
                    f"first {rows} of {wl.M} tokens ({t_layer:.2f} s), scaled to the batch: "
                    f"{t_step:.1f} s per step"),
     }
+
+
+def prefill_leg(torch, workloads, sq, L, dev, stream, hs, launches):
+    """The metric's M >= 2048 half beyond the step's workload: the product at
+    the down_proj-style (2048 x 11008 -> 4096, alpha 0.5) and the large-prefill
+    (8192 x 8192 -> 3 x 8192, one smoothed X for the three projections)
+    configurations, on their own calibrated, folded and quantized codes (the
+    matrix cores' power, and so their clock, depends on the codes), each as
+    `launches` launches between one event pair."""
+    out = {"peak": PEAK_INT8_TOPS, "unit": "TOP/s"}
+    for name in ("down11008", "prefill8192x3"):
+        wl = workloads.WORKLOADS[name]
+        inp = workloads.generate(wl)
+        M, K, N = wl.M, wl.K, wl.N
+        x = torch.from_numpy(inp.x).to(dev)
+        xcal = torch.from_numpy(inp.x_cal).to(dev)
+        w = torch.from_numpy(inp.w).to(dev)
+        del inp
+        ax = torch.empty(K, dtype=torch.float32, device=dev)
+        s = torch.empty(K, dtype=torch.float32, device=dev)
+        inv = torch.empty(K, dtype=torch.float32, device=dev)
+        wq = torch.empty(sq.packed_bytes(N, K), dtype=torch.int8, device=dev)
+        wsc = torch.empty(N, dtype=torch.float32, device=dev)
+        xq = torch.empty(sq.packed_bytes(M, K), dtype=torch.int8, device=dev)
+        xsc = torch.empty(M, dtype=torch.float32, device=dev)
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        st = L.sq_calibrate_absmax(xcal.data_ptr(), xcal.shape[0], K, K, ax.data_ptr(), 0, hs)
+        st |= L.sq_smooth_fold_weights(w.data_ptr(), K, N, N, ax.data_ptr(), float(wl.alpha), None,
+                                       s.data_ptr(), inv.data_ptr(), wq.data_ptr(), wsc.data_ptr(),
+                                       hs)
+        st |= L.sq_quant_act_per_token(x.data_ptr(), M, K, K, inv.data_ptr(), xq.data_ptr(),
+                                       xsc.data_ptr(), hs)
+        if st:
+            raise RuntimeError(f"{name}: preparing the product failed")
+        del w, x, xcal
+
+        def run():
+            return L.sq_w8a8_gemm(xq.data_ptr(), xsc.data_ptr(), wq.data_ptr(), wsc.data_ptr(), M,
+                                  N, K, y.data_ptr(), N, sq.SQ_OUT_F16, hs)
+        for _ in range(3):
+            if run():
+                raise RuntimeError(f"{name}: product failed")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(launches):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / launches
+        tops = 2.0 * M * N * K / (us * 1e-6) / 1e12
+        out[name] = {"M": M, "K": K, "N": N, "us": round(us, 2), "tops": round(tops, 1),
+                     "frac": round(tops / PEAK_INT8_TOPS, 4)}
+        log(f"product {name}: {us:.1f} us, {tops:.0f} TOP/s")
+        del xq, wq, y
+    return out
 
 
 def decode_leg(torch, workloads, sq, L, dev, stream, hs, launches):
@@ -237,6 +294,9 @@ def main():
     ap.add_argument("--decode-launches", type=int, default=40,
                     help="launches per token count of the decode layer (decode8192: K 8192, "
                          "N 28672, M 1, 4 and 16), timed over 4 rotated weight copies (0: skip)")
+    ap.add_argument("--prefill-launches", type=int, default=10,
+                    help="launches of the product at the other large-token configurations "
+                         "(down11008, prefill8192x3), on their folded codes (0: skip)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle layer work in the CPU baseline (0: skip)")
     ap.add_argument("--copy-kernel", type=int, default=0, metavar="MIB",
@@ -416,6 +476,10 @@ def main():
                "transform_flops": int(M * K * (K.bit_length() - 1))}
         log(f"rotated 4-bit quant {us[1]:.2f} us, unrotated {us[0]:.2f} us")
 
+    prefill = None
+    if args.prefill_launches > 0:
+        prefill = prefill_leg(torch, workloads, sq, L, dev, stream, hs, args.prefill_launches)
+
     decode = None
     if args.decode_launches > 0:
         decode = decode_leg(torch, workloads, sq, L, dev, stream, hs, args.decode_launches)
@@ -456,6 +520,7 @@ def main():
                      "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                      "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": traffic,
                      "per_launch": f"2*M*N*K = {ops:.4g} int8 ops per launch"},
+        "prefill": prefill,
         "decode": decode,
         "norm_fold": norm,
         "rotation_w4": rot,
