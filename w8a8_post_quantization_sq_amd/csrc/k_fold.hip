@@ -338,10 +338,11 @@ k_fold_quant(const uint16_t *__restrict__ w, int64_t K, int64_t N, int64_t ldw,
         const int64_t kw = (k0 >> 6) + kwl;
         const int rn = rbl * 16 + (l & 15);
         const int word = kwl * 16 + (l >> 4) * 4;     // first of 4 words (16 codes)
-        // non-temporal: the codes are not read again by this pass
+        // plain stores: where the product follows the fold, it finds the
+        // codes in the caches
         if (rb < RB && kw < KW)
-            __builtin_nontemporal_store(*reinterpret_cast<const v4i *>(tile + fq_word(rn, word)),
-                                        reinterpret_cast<v4i *>(wq + ((rb * KW + kw) << 10) + l * 16));
+            *reinterpret_cast<v4i *>(wq + ((rb * KW + kw) << 10) + l * 16) =
+                *reinterpret_cast<const v4i *>(tile + fq_word(rn, word));
     }
 }
 

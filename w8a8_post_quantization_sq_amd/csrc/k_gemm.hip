@@ -30,9 +30,10 @@
 //     order, so reads and writes are conflict-free);
 //   - the loop is software-pipelined: while the matrix cores work on step t,
 //     each wave already reads step t+1's weight fragments from LDS (one
-//     fragment after the 4 products that used its register), and stores step
-//     t+2's slice; one barrier per step, and no LDS wait sits in front of the
-//     first product of a step;
+//     fragment after the 2 products that used its register), stores step
+//     t+2's slice and issues step t+3's global loads, all spread over the
+//     step's products; one barrier per step, and no LDS wait sits in front of
+//     the first product of a step;
 //   - workgroups are numbered so that the 32 tiles one XCD (and its L2) runs
 //     form a 4 x 8 block of the tile grid, which shares activation and weight
 //     rows.
@@ -266,33 +267,47 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int t = t0 + u;
-            // this step's loads go out first and stay first: the weight slice
-            // stored into LDS in the middle of the step was issued a step
-            // earlier, with this step's three loads behind it, so its wait does
-            // not drain the activation prefetch
-            load_w((u + 1) & 1, t + 3);
-            load_x((u + 3) & 3, t + 3);
-            __builtin_amdgcn_sched_barrier(0);
             const int nb = (u + 1) & 3;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
 #pragma unroll
                 for (int i = 0; i < 2; ++i) acc[i][j] = mfma(wf[j], xr[u][i], acc[i][j]);
                 wf[j] = *reinterpret_cast<const v4i *>(&ldsw[nb][j * T_FRAG + lane * 16]);
-                if (j == 3) {
-                    // the staged slice t+2 goes to LDS mid-step, pinned between
-                    // the reads of fragments 3 and 4
+                // The step's three global loads (weight slice t+3, then the two
+                // activation fragments of t+3) and the LDS store of slice t+2
+                // are spread over its products, each pinned in place: issued
+                // together at the top of the step, the two waves of a SIMD
+                // queued all their loads at once and then waited on the
+                // address path with no products to issue.  The slice stored
+                // here was loaded a step earlier, so its wait leaves the later
+                // loads in flight.
+                if (j == 1) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_w((u + 1) & 1, t + 3);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (j == 4) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    xr[(u + 3) & 3][0] = bload(rx, xbase[0] + win(t + 3));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (j == 5) {
                     __builtin_amdgcn_sched_barrier(0);
                     store_w(u & 1, (u + 2) & 3);
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                if (j == 6) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    xr[(u + 3) & 3][1] = bload(rx, xbase[1] + win(t + 3));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
             // Before the barrier only the store must be complete: LDS
-            // operations of a wave complete in order, so at most the 4 later
-            // fragment reads may still be in flight (they read slice t+1,
-            // which nobody overwrites before two more barriers).
+            // operations of a wave complete in order, so at most the 2 later
+            // fragment reads (6 and 7) may still be in flight (they read slice
+            // t+1, which nobody overwrites before two more barriers).
             __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt(0xc07f | (4 << 8));   // lgkmcnt(4)
+            __builtin_amdgcn_s_waitcnt(0xc07f | (2 << 8));   // lgkmcnt(2)
             __builtin_amdgcn_s_barrier();
             // keep each step's products inside the step: hoisting them above
             // the barrier would put them right behind the LDS reads they use

@@ -310,10 +310,11 @@ k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t l
         const int pr = (int)(p & 7);
         const int q = (int)((p >> 3) & 3);
         const int64_t kw = p >> 5;
-        // non-temporal: the codes are read by the product, not by this pass
-        __builtin_nontemporal_store(
-            *reinterpret_cast<const v4i *>(codes + pr * pitch + kw * 64 + q * 16),
-            reinterpret_cast<v4i *>(base + ((kw * 64 + q * 16 + half + pr) << 4)));
+        // plain stores: the product reads the codes next, and finds them in
+        // the caches (non-temporal stores sent them to HBM, which cost the
+        // product ~2 us at 2048 x 4096)
+        *reinterpret_cast<v4i *>(base + ((kw * 64 + q * 16 + half + pr) << 4)) =
+            *reinterpret_cast<const v4i *>(codes + pr * pitch + kw * 64 + q * 16);
     }
 }
 

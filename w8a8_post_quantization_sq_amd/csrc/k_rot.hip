@@ -174,9 +174,9 @@ k_quant4_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
         const int pr = (int)(p & 7);
         const int qq = (int)((p >> 3) & 3);
         const int64_t kw = p >> 5;
-        __builtin_nontemporal_store(
-            *reinterpret_cast<const v4i *>(codes + pr * pitch + kw * 64 + qq * 16),
-            reinterpret_cast<v4i *>(base + ((kw * 64 + qq * 16 + half + pr) << 4)));
+        // plain stores: the product reads the codes next
+        *reinterpret_cast<v4i *>(base + ((kw * 64 + qq * 16 + half + pr) << 4)) =
+            *reinterpret_cast<const v4i *>(codes + pr * pitch + kw * 64 + qq * 16);
     }
 }
 
@@ -314,9 +314,9 @@ k_quant4_rot_t(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx
         const int pr = (int)(p & 3);
         const int qq = (int)((p >> 2) & 3);
         const int64_t kw = p >> 4;
-        __builtin_nontemporal_store(
-            *reinterpret_cast<const v4i *>(cb + pr * K + kw * 64 + qq * 16),
-            reinterpret_cast<v4i *>(base + ((kw * 64 + qq * 16 + quarter + pr) << 4)));
+        // plain stores: the product reads the codes next
+        *reinterpret_cast<v4i *>(base + ((kw * 64 + qq * 16 + quarter + pr) << 4)) =
+            *reinterpret_cast<const v4i *>(cb + pr * K + kw * 64 + qq * 16);
     }
 }
 
