@@ -22,8 +22,11 @@ the decode-size layer (M = 1, 4 and 16 tokens
 against an 8192 x 28672 layer, the metric's M <= 16 half, as GB/s of its
 weights), the fused RMS-norm + quantization that replaces A4 when 1/s is
 folded into the normalization in front of the layer, the rotated 4-bit
-quantizer of Smooth Rotation against the unrotated one, and the CPU oracle
-timed on a bounded sample as a baseline.
+quantizer of Smooth Rotation against the unrotated one, the matrix cores'
+and HBM's attainable rates measured on this GPU (a matrix-instruction loop
+with the product's register pattern on the workload's codes, a 1 GiB
+streaming read) beside the published peaks, and the CPU oracle timed on a
+bounded sample as a baseline.
 """
 import argparse
 import hashlib
@@ -273,6 +276,49 @@ def decode_leg(torch, workloads, sq, L, dev, stream, hs, launches):
     return out
 
 
+def attainable_leg(torch, sq, dev, stream, hs, wq, xq):
+    """Measured ceilings on this GPU, reported beside the published peaks
+    (libsq_probe.so): the int8 matrix cores' sustained rate with the product
+    kernel's register pattern (one workgroup of 8 waves per CU, 16 MFMAs per
+    k-step into 16 accumulators) on the workload's own weight and activation
+    codes, and a streaming read of 1 GiB (beyond the 256 MB Infinity Cache)."""
+    P = sq.probe_lib()
+    a = wq.view(-1)[:65536]
+    b = xq.view(-1)[:16384]
+    a = a.repeat((65536 + a.numel() - 1) // a.numel())[:65536].contiguous()
+    b = b.repeat((16384 + b.numel() - 1) // b.numel())[:16384].contiguous()
+    blocks, iters, reps = 256, 2000, 5
+    out = torch.empty(blocks * 512, dtype=torch.int32, device=dev)
+    if P.sqp_mfma_rate(a.data_ptr(), b.data_ptr(), 50, blocks, out.data_ptr(), hs):
+        raise RuntimeError("sqp_mfma_rate failed")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        P.sqp_mfma_rate(a.data_ptr(), b.data_ptr(), iters, blocks, out.data_ptr(), hs)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ops = blocks * 8 * iters * 16 * (2 * 16 * 16 * 64) * reps
+    mfma_tops = ops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    nbytes, rblocks = 1 << 30, 8192
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    rout = torch.empty(rblocks * 256, dtype=torch.int32, device=dev)
+    if P.sqp_stream_read(buf.data_ptr(), nbytes, rblocks, rout.data_ptr(), hs):
+        raise RuntimeError("sqp_stream_read failed")
+    e0.record(stream)
+    for _ in range(reps):
+        P.sqp_stream_read(buf.data_ptr(), nbytes, rblocks, rout.data_ptr(), hs)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    read_gbs = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+    log(f"attainable: matrix cores {mfma_tops:.0f} TOP/s on the workload's codes, "
+        f"streaming read {read_gbs:.0f} GB/s")
+    return {"what": "measured on this GPU (libsq_probe.so): int8 MFMA rate with the product's "
+                    "register pattern on the workload's codes, 2 waves per SIMD; streaming "
+                    "read of 1 GiB with 16-byte non-temporal loads",
+            "mfma_int8_tops": round(mfma_tops, 1), "hbm_read_gbs": round(read_gbs, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -297,6 +343,9 @@ def main():
     ap.add_argument("--prefill-launches", type=int, default=10,
                     help="launches of the product at the other large-token configurations "
                          "(down11008, prefill8192x3), on their folded codes (0: skip)")
+    ap.add_argument("--attainable", type=int, default=1,
+                    help="measure the matrix cores' and HBM's attainable rates on this GPU "
+                         "(libsq_probe.so) and report them beside the published peaks (0: skip)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle layer work in the CPU baseline (0: skip)")
     ap.add_argument("--copy-kernel", type=int, default=0, metavar="MIB",
@@ -388,7 +437,11 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log(f"timed {args.steps} steps in {wall:.3f} s")
-    gemm_ms = sum(a.elapsed_time(b) for a, b in gemm_events) / len(gemm_events)
+    gemm_samples = sorted(a.elapsed_time(b) for a, b in gemm_events)
+    gemm_ms = sum(gemm_samples) / len(gemm_samples)
+
+    def pct(q):
+        return gemm_samples[min(len(gemm_samples) - 1, int(q * len(gemm_samples)))] * 1e3
 
     # Per-stage breakdown, from a separate pass with an event between stages
     # (those events lengthen these steps a little; the headline is not taken here).
@@ -519,6 +572,9 @@ def main():
         "roofline": {"kernel": "k_gemm_w8a8 (sq_w8a8_gemm)", "bound": "mfma",
                      "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                      "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": traffic,
+                     "launch_us": {"mean": round(gemm_ms * 1e3, 2), "p10": round(pct(0.1), 2),
+                                   "p50": round(pct(0.5), 2), "p90": round(pct(0.9), 2),
+                                   "samples": len(gemm_samples)},
                      "per_launch": f"2*M*N*K = {ops:.4g} int8 ops per launch"},
         "prefill": prefill,
         "decode": decode,
@@ -526,6 +582,14 @@ def main():
         "rotation_w4": rot,
         "cpu_baseline": None,
     }
+    if args.attainable:
+        att = attainable_leg(torch, sq, dev, stream, hs, wq, xq)
+        att["product_frac_of_mfma"] = round(gemm_tops / att["mfma_int8_tops"], 4)
+        if decode:
+            att["decode_layer_frac_of_read"] = {
+                k: round(v["layer_gbs"] / att["hbm_read_gbs"], 4)
+                for k, v in decode.items() if k in ("M1", "M4", "M16")}
+        out["attainable"] = att
     if args.cpu_budget > 0:
         log("timing the CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_budget)

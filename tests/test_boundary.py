@@ -408,3 +408,35 @@ def test_packed4_bytes(sq):
     assert sq.packed4_bytes(16, 64) == 512 and sq.packed4_bytes(17, 80) == 2 * 2 * 512
     assert sq.packed4_bytes(0, 64) == 0 and sq.packed4_bytes(4, 40) == 0
     assert sq.sq_w4_workspace_bytes(4096, 4096) == 2 * 4096 * 4096 + sq.packed_bytes(4096, 4096)
+
+
+# ---- the benchmark's probe library (include/sq_probe.h) ---------------------------------
+
+PROBE_HEADER = os.path.join(ROOT, "include", "sq_probe.h")
+
+
+@pytest.fixture(scope="module")
+def probe(sq):
+    if not os.path.exists(sq.PROBE_PATH):
+        from w8a8_post_quantization_sq_amd import build
+        build.build()
+    return sq.probe_lib()
+
+
+def test_probe_exports_exactly_its_header(sq, probe):
+    import subprocess
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    decl = set(re.findall(r"\b(sqp_[a-z0-9_]+)\s*\(", text))
+    assert decl == set(sq.PROBE_EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", sq.PROBE_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert {l.split()[-1] for l in out.splitlines() if " T " in l} == decl
+
+
+def test_probe_rejects_bad_arguments_before_launching(probe):
+    assert probe.sqp_mfma_rate(None, Q, 10, 256, P, None) == 1
+    assert probe.sqp_mfma_rate(P, Q, 0, 256, P, None) == 1
+    assert probe.sqp_mfma_rate(P, Q, 10, 0, P, None) == 1
+    assert probe.sqp_stream_read(P, 1000, 64, Q, None) == 1     # not a multiple of 16
+    assert probe.sqp_stream_read(None, 1024, 64, Q, None) == 1
+    assert probe.sqp_stream_read(P, 1024, 0, Q, None) == 1

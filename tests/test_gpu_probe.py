@@ -1,0 +1,45 @@
+"""The benchmark's probe library on the GPU: both ceilings run, write their
+outputs, and the matrix loop's sums are what the instruction computes.
+
+With every activation operand byte 1 and every weight operand byte equal to
+c, each 16 x 16 x 64 product adds 64 c to every accumulator entry, so after
+`iters` iterations a lane's 16 accumulators of 4 entries sum to
+16 * 4 * iters * 64 * c.
+"""
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import w8a8_post_quantization_sq_amd as sq
+    return torch, sq.probe_lib(), torch.device("cuda:0")
+
+
+def test_mfma_rate_sums(env):
+    torch, P, dev = env
+    c, iters, blocks = 3, 7, 4
+    a = torch.full((65536,), c, dtype=torch.int8, device=dev)
+    b = torch.ones(16384, dtype=torch.int8, device=dev)
+    out = torch.zeros(blocks * 512, dtype=torch.int32, device=dev)
+    hs = torch.cuda.current_stream(dev).cuda_stream
+    assert P.sqp_mfma_rate(a.data_ptr(), b.data_ptr(), iters, blocks, out.data_ptr(), hs) == 0
+    torch.cuda.synchronize()
+    assert torch.all(out == 16 * 4 * iters * 64 * c)
+
+
+def test_stream_read_xor(env):
+    torch, P, dev = env
+    blocks = 2
+    n = blocks * 256 * 16 * 3          # three 16-byte vectors per thread
+    buf = torch.zeros(n, dtype=torch.uint8, device=dev)
+    buf[0] = 0x5a                       # first vector of thread 0, word 0
+    out = torch.full((blocks * 256,), -1, dtype=torch.int32, device=dev)
+    hs = torch.cuda.current_stream(dev).cuda_stream
+    assert P.sqp_stream_read(buf.data_ptr(), n, blocks, out.data_ptr(), hs) == 0
+    torch.cuda.synchronize()
+    o = out.cpu()
+    assert o[0].item() == 0x5a and torch.all(o[1:] == 0)

@@ -107,6 +107,29 @@ def lib() -> ctypes.CDLL:
     return _LIB
 
 
+PROBE_PATH = os.path.join(HERE, "libsq_probe.so")
+PROBE_EXPORTS = ("sqp_mfma_rate", "sqp_stream_read")
+_PROBE = None
+
+
+def probe_lib() -> ctypes.CDLL:
+    """libsq_probe.so, the benchmark's measured ceilings (include/sq_probe.h):
+    not part of the layer.  Raises if it has not been built."""
+    global _PROBE
+    if _PROBE is None:
+        if not os.path.exists(PROBE_PATH):
+            raise ImportError(f"{PROBE_PATH} is missing: build it with "
+                              "`python -m w8a8_post_quantization_sq_amd.build`")
+        P = ctypes.CDLL(PROBE_PATH)
+        vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        P.sqp_mfma_rate.restype = ci
+        P.sqp_mfma_rate.argtypes = [vp, vp, ci, ci, vp, vp]
+        P.sqp_stream_read.restype = ci
+        P.sqp_stream_read.argtypes = [vp, i64, ci, vp, vp]
+        _PROBE = P
+    return _PROBE
+
+
 def status_str(status: int) -> str:
     return lib().sq_status_str(int(status)).decode()
 

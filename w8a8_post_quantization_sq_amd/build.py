@@ -1,4 +1,5 @@
-"""Builds libsq.so (the HIP library behind include/sq.h) in-tree for gfx950.
+"""Builds libsq.so (the HIP library behind include/sq.h) and libsq_probe.so (the
+benchmark's measured ceilings, include/sq_probe.h) in-tree for gfx950.
 
 Flags:
   --offload-arch=gfx950                  CDNA4 / MI355X only
@@ -25,6 +26,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libsq.so")
 
+PROBE_PATH = os.path.join(HERE, "libsq_probe.so")
+PROBE_SOURCES = ["probe.hip"]
+
 SOURCES = ["sq_api.cpp", "k_calib.hip", "k_fold.hip", "k_quant.hip", "k_gemm.hip", "k_pack.hip",
            "k_rot.hip"]
 
@@ -44,13 +48,13 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the gfx950 library cannot be built")
 
 
-def build(verbose: bool = False) -> str:
+def _compile(sources, out: str, verbose: bool) -> str:
     srcs = []
-    for s in SOURCES:
+    for s in sources:
         p = os.path.join(CSRC, s)
         # .cpp sources are host code; .hip sources carry the kernels
         srcs += (["-x", "hip", p, "-x", "none"] if s.endswith(".hip") else [p])
-    tmp = LIB_PATH + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd))
@@ -61,8 +65,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Builds libsq.so (the layer) and libsq_probe.so (the benchmark's
+    measured ceilings); returns the path of libsq.so."""
+    _compile(PROBE_SOURCES, PROBE_PATH, verbose)
+    return _compile(SOURCES, LIB_PATH, verbose)
 
 
 if __name__ == "__main__":
