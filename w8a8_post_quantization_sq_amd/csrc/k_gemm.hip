@@ -25,15 +25,15 @@
 // wave w owns tokens [32w, 32w + 32) and all 128 channels.
 //   - activation fragments are private to a wave and go straight from global
 //     memory into a register ring, 3 k-steps ahead;
-//   - the 8 KiB weight slice of a k-step is shared by the 8 waves: staged
-//     through registers into a ring of 4 LDS buffers (copied as is, in lane
-//     order, so reads and writes are conflict-free);
+//   - the 8 KiB weight slice of a k-step is shared by the 8 waves: loaded
+//     straight into a ring of 8 LDS buffers, 4 steps ahead (4-bit weights:
+//     staged through registers and widened into a ring of 4), in lane order,
+//     so reads are conflict-free;
 //   - the loop is software-pipelined: while the matrix cores work on step t,
 //     each wave already reads step t+1's weight fragments from LDS (one
-//     fragment after the 2 products that used its register), stores step
-//     t+2's slice and issues step t+3's global loads, all spread over the
-//     step's products; one barrier per step, and no LDS wait sits in front of
-//     the first product of a step;
+//     fragment after the 2 products that used its register) and issues the
+//     step's global loads, spread over its products; one barrier per step,
+//     and no LDS wait sits in front of the first product of a step;
 //   - workgroups are numbered so that the 32 tiles one XCD (and its L2) runs
 //     form a 4 x 8 block of the tile grid, which shares activation and weight
 //     rows.
@@ -89,6 +89,19 @@ __device__ __forceinline__ int sext4(uint32_t n) {
 __device__ __forceinline__ v4i unpack4(uint2 p) {
     constexpr uint32_t LO = 0x0F0F0F0Fu;
     return v4i{sext4(p.x & LO), sext4((p.x >> 4) & LO), sext4(p.y & LO), sext4((p.y >> 4) & LO)};
+}
+
+// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ...
+// lds): lane l's bytes land at lds + 16 l, lds wave-uniform (it goes to M0);
+// lanes past the buffer's extent write zeros.  The load counts in vmcnt like
+// any other.  The builtin exists only for the device target: the host pass,
+// which emits the kernels' launch stubs, would drop every template instance
+// that names it, so only the device pass sees it.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, int8_t *lds, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff,
+                                             0, 0, 0);
+#endif
 }
 
 __device__ __forceinline__ v4i mfma(const v4i &a, const v4i &b, const v4i &c) {
@@ -158,10 +171,13 @@ __global__ void __launch_bounds__(64 * T_WAVES)
 k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
             const float *__restrict__ xs, const float *__restrict__ ws, int M, int N, int K,
             void *__restrict__ Y, int64_t ldy, int tiles_m, int tiles_n, int vec_ok) {
-    // LDS: 4 weight slices during the k loop, then 8 wave tiles of the epilogue
+    // LDS: the ring of weight slices during the k loop (8 with 8-bit weights,
+    // 4 with 4-bit ones), then 8 wave tiles of the epilogue
     constexpr int EPI_PITCH = 128 * 2 + 16;            // bytes per row of 128 fp16, padded
     constexpr int EPI_WAVE = 32 * EPI_PITCH;            // 32 rows per wave
-    constexpr int LDS_BYTES = (4 * T_SLICE > T_WAVES * EPI_WAVE) ? 4 * T_SLICE : T_WAVES * EPI_WAVE;
+    constexpr int RING = W4 ? 4 : 8;
+    constexpr int LDS_BYTES =
+        (RING * T_SLICE > T_WAVES * EPI_WAVE) ? RING * T_SLICE : T_WAVES * EPI_WAVE;
     __shared__ __align__(16) int8_t lds_raw[LDS_BYTES];
     int8_t (*ldsw)[T_SLICE] = reinterpret_cast<int8_t (*)[T_SLICE]>(lds_raw);
 
@@ -250,6 +266,77 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
         else *reinterpret_cast<v4i *>(&ldsw[buf][tid * 16]) = wst[slot];
     };
 
+    if constexpr (!W4) {
+    // 8-bit weights go straight from global memory into the LDS ring (slice t
+    // in buffer t & 7), 4 steps ahead of their use: no register staging and
+    // no LDS store, and 3 steps between a slice's load and its first reader,
+    // enough for weights that come from HBM.  Wave w loads fragment w of the
+    // slice (its lanes' 16 bytes land in lane order, as the readers expect).
+    int8_t *ring = lds_raw;
+    auto dma_w = [&](int t) {
+        lds_load16(rw, ring + (t & 7) * T_SLICE + wave * T_FRAG, wbase + winw(t));
+    };
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dma_w(s);
+#pragma unroll
+    for (int s = 0; s < 3; ++s) load_x(s, s);
+    __builtin_amdgcn_s_waitcnt(0x0F73);        // vmcnt(3): slices 0..3 have landed
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wf[j] = *reinterpret_cast<const v4i *>(ring + j * T_FRAG + lane * 16);
+
+    const int nsteps = (KW + 3) & ~3;
+    for (int t0 = 0; t0 < nsteps; t0 += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int t = t0 + u;
+            const int8_t *nb = ring + ((t + 1) & 7) * T_SLICE;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) acc[i][j] = mfma(wf[j], xr[u][i], acc[i][j]);
+                wf[j] = *reinterpret_cast<const v4i *>(nb + j * T_FRAG + lane * 16);
+                // the step's three global loads (weight slice t+4 into its
+                // buffer, then the two activation fragments of t+3) spread
+                // over its products, each pinned in place: issued together at
+                // the top of the step, the two waves of a SIMD queued all their
+                // loads at once and then waited on the address path with no
+                // products to issue
+                if (j == 1) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    dma_w(t + 4);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (j == 4) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    xr[(u + 3) & 3][0] = bload(rx, xbase[0] + win(t + 3));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (j == 7) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    xr[(u + 3) & 3][1] = bload(rx, xbase[1] + win(t + 3));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            // Slice t+2, read from the next step on, was loaded at step t-2;
+            // 8 loads were issued after it (2 in its step, 3 in each later
+            // one), and memory loads complete in order, so vmcnt(8) means it
+            // has landed in this wave's part of the buffer; the barrier then
+            // publishes every wave's part.  The buffer a step loads into
+            // (slice t+4: buffer (t-4) & 7) was last read in step t-5.
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(0x0F78);    // vmcnt(8)
+            __builtin_amdgcn_s_barrier();
+            // keep each step's products inside the step: hoisting them above
+            // the barrier would put them right behind the LDS reads they use
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // the slices loaded past the last step still land in LDS, which the
+    // epilogue reuses: wait for them
+    __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
+    } else {
+    // 4-bit weights: staged through registers, widened on their way to LDS
     // prologue: weight slices 0 and 1 in LDS, slice 2 staged, activations 0..2 in flight
 #pragma unroll
     for (int s = 0; s < 3; ++s) load_x(s, s);
@@ -313,6 +400,8 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
             // the barrier would put them right behind the LDS reads they use
             __builtin_amdgcn_sched_barrier(0);
         }
+    }
+
     }
 
     // epilogue.  fp16 output goes through LDS (the weight buffers are free
