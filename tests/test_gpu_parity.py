@@ -343,7 +343,10 @@ GEMM_SHAPES = [(1, 1, 16), (3, 5, 48), (17, 100, 80), (40, 100, 320), (49, 1000,
                (9, 64, 4096), (25, 33, 256), (32, 48, 1024),
                (16, 28672, 128), (9, 28672, 64), (24, 8192, 64), (32, 12304, 64), (20, 8200, 64),
                (64, 70, 4096), (65, 33, 64), (100, 200, 64), (128, 128, 4096),
-               (130, 129, 1040), (256, 384, 2048), (1, 28672, 128), (16, 300, 8192), (513, 77, 112)]
+               (130, 129, 1040), (256, 384, 2048), (1, 28672, 128), (16, 300, 8192), (513, 77, 112),
+               # 256 x 256 tiles (their rounds of 256 CUs beat the 256 x 128 ones'): ragged M,
+               # N (a partial row block) and K, and a full-width one
+               (4000, 4040, 80), (4096, 8192, 64)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
@@ -455,6 +458,29 @@ def test_pack_unpack_helpers(sq, dev, rows, K, ld):
     sq.sq_unpack_i8(packed, back[:, :K])
     out = H(back)
     assert np.array_equal(out[:, :K], codes[:, :K]) and np.all(out[:, K:] == 9)
+
+
+def test_gemm_wide_tile_path_strided_output(sq, dev, orc):
+    """The 256 x 256 tile kernel (4000 x 4040: 256 wide tiles in one round
+    against 512 narrow ones in two) with output rows of stride 4049 starting 3
+    elements into the buffer, so the 16-byte row stores are off and every
+    output takes the element path; and with an aligned stride."""
+    import torch
+    M, N, K = 4000, 4040, 64
+    xq = W.random_i8(1200, M, K)
+    wq = W.random_i8(1201, N, K)
+    xs = W.random_scales(1202, M)
+    ws = W.random_scales(1203, N)
+    ref = orc.dequant(orc.gemm_i32(xq, wq), xs, ws)
+    for ldy, off in ((4049, 3), (4048, 8)):
+        big = torch.full((M * ldy + 64,), 5.0, dtype=torch.float16, device=dev)
+        view = big[off:off + M * ldy].view(M, ldy)[:, :N]
+        sq.sq_w8a8_gemm(T(pack(xq), dev), T(xs, dev), T(pack(wq), dev), T(ws, dev), view, K)
+        out = H(big)
+        assert np.all(out[:off] == 5.0) and np.all(out[off + M * ldy:] == 5.0)
+        out = out[off:off + M * ldy].reshape(M, ldy)
+        assert np.all(out[:, N:] == 5.0)
+        assert_f16_close(out[:, :N], ref)
 
 
 @pytest.mark.parametrize("M,N,ldy,off", [(100, 72, 80, 0), (300, 130, 136, 8), (257, 64, 72, 4)])

@@ -37,6 +37,9 @@
 //   - workgroups are numbered so that the 32 tiles one XCD (and its L2) runs
 //     form a 4 x 8 block of the tile grid, which shares activation and weight
 //     rows.
+// k_gemm_wide (M > 64, where enough 256 x 256 tiles fill the CUs, 8-bit
+// weights): the same loop with 256 channels per workgroup, so a CU moves a
+// third fewer operand bytes per product.
 // k_gemm_skinny (M <= 64, decode): one workgroup per 16 output channels; its
 // 4 waves split the k windows, stream the weight fragments (the dominant HBM
 // traffic) with 8 1 KiB loads in flight each (non-temporal for up to 32
@@ -695,6 +698,208 @@ void launch_skinny(int cb, dim3 grid, hipStream_t st, const int8_t *xq, const in
     }
 }
 
+// ---- wide tiles: 256 tokens x 256 channels ---------------------------------------------
+
+constexpr int W_BN = 256;             // channels per tile (16 row blocks)
+constexpr int W_SLICE = 16 * T_FRAG;  // weight bytes per k-step
+
+// Like k_gemm_tile with twice the channels per workgroup: wave w owns tokens
+// [32w, 32w + 32) x 256 channels (32 accumulators of 16 x 16).  The 16 KiB
+// weight slice of a k-step goes straight into an 8-deep LDS ring, 4 steps
+// ahead (wave w loads fragments w and w + 8).  Weight fragments are read from
+// LDS one half-step ahead of their products through a ring of 8 registers:
+// after the products of fragment j, fragment j + 8 of this step (j < 8) or
+// fragment j - 8 of the next step (j >= 8).  Per k-step a CU moves 32 KiB of
+// operands for 2 x the products of the 256 x 128 tile (24 KiB).
+template <bool F16OUT>
+__global__ void __launch_bounds__(64 * T_WAVES)
+k_gemm_wide(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
+            const float *__restrict__ xs, const float *__restrict__ ws, int M, int N, int K,
+            void *__restrict__ Y, int64_t ldy, int tiles_m, int tiles_n, int vec_ok) {
+    constexpr int EPI_PITCH = W_BN * 2 + 16;           // bytes per row of 256 fp16, padded
+    constexpr int EPI_WAVE = 32 * EPI_PITCH;            // 32 rows per wave
+    constexpr int LDS_BYTES =
+        (8 * W_SLICE > T_WAVES * EPI_WAVE) ? 8 * W_SLICE : T_WAVES * EPI_WAVE;
+    __shared__ __align__(16) int8_t lds_raw[LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * T_BM;
+    const int n0 = tn * W_BN;
+    const int KW = (K + 63) >> 6;
+    const int rbx = (M + 15) >> 4, rbw = (N + 15) >> 4;
+    const int nbx = min(16, rbx - (m0 >> 4));
+    const int nbw = min(16, rbw - (n0 >> 4));
+    const __amdgpu_buffer_rsrc_t rx =
+        make_rsrc(X + (int64_t)(m0 >> 4) * KW * T_FRAG, (int64_t)nbx * KW * T_FRAG);
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(W + (int64_t)(n0 >> 4) * KW * T_FRAG, (int64_t)nbw * KW * T_FRAG);
+
+    float xsv[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int m = m0 + wave * 32 + i * 16 + (lane & 15);
+        xsv[i] = (F16OUT && m < M) ? xs[m] : 0.0f;
+    }
+    uint32_t xbase[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int b = wave * 2 + i;
+        xbase[i] = b < nbx ? (uint32_t)(b * KW * T_FRAG + lane * 16) : OOB_BASE;
+    }
+    uint32_t wbase[2];   // this wave's two fragments of every slice: w and w + 8
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int b = wave + 8 * h;
+        wbase[h] = b < nbw ? (uint32_t)(b * KW * T_FRAG + lane * 16) : OOB_BASE;
+    }
+    auto win = [&](int t) -> uint32_t { return t < KW ? (uint32_t)t * T_FRAG : OOB_WIN; };
+
+    v4i acc[2][16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    v4i xr[4][2];
+    v4i wf[8];
+    int8_t *ring = lds_raw;
+    auto dma_w = [&](int h, int t) {
+        lds_load16(rw, ring + (t & 7) * W_SLICE + (wave + 8 * h) * T_FRAG, wbase[h] + win(t));
+    };
+    auto load_x = [&](int slot, int t) {
+        const uint32_t wo = win(t);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) xr[slot][i] = bload(rx, xbase[i] + wo);
+    };
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        dma_w(0, s);
+        dma_w(1, s);
+    }
+#pragma unroll
+    for (int s = 0; s < 3; ++s) load_x(s, s);
+    __builtin_amdgcn_s_waitcnt(0x0F73);        // vmcnt(3): slices 0..3 have landed
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wf[j] = *reinterpret_cast<const v4i *>(ring + j * T_FRAG + lane * 16);
+
+    const int nsteps = (KW + 3) & ~3;
+    for (int t0 = 0; t0 < nsteps; t0 += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int t = t0 + u;
+            const int8_t *cur = ring + (t & 7) * W_SLICE;
+            const int8_t *nxt = ring + ((t + 1) & 7) * W_SLICE;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) acc[i][j] = mfma(wf[j & 7], xr[u][i], acc[i][j]);
+                wf[j & 7] = *reinterpret_cast<const v4i *>(
+                    (j < 8 ? cur + (j + 8) * T_FRAG : nxt + (j - 8) * T_FRAG) + lane * 16);
+                // the step's four global loads (the two fragments of weight
+                // slice t+4, then the two activation fragments of t+3) spread
+                // over its products, each pinned in place
+                if (j == 0) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    dma_w(0, t + 4);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (j == 4) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    dma_w(1, t + 4);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (j == 10) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    xr[(u + 3) & 3][0] = bload(rx, xbase[0] + win(t + 3));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (j == 14) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    xr[(u + 3) & 3][1] = bload(rx, xbase[1] + win(t + 3));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            // Slice t+2, read from the next step on, was loaded at step t-2;
+            // 10 loads were issued after its second fragment (2 in its step,
+            // 4 in each later one), and loads complete in order, so vmcnt(10)
+            // means it has landed; the barrier publishes every wave's part.
+            // The buffer a step loads into (slice t+4: buffer (t-4) & 7) was
+            // last read in step t-4.
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(0x0F7A);    // vmcnt(10)
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // the slices loaded past the last step still land in LDS, which the
+    // epilogue reuses: wait for them
+    __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
+
+    // epilogue as in k_gemm_tile, rows of 512 bytes; the weight scales are
+    // loaded here (16 float4 per lane would not fit beside the loop)
+    if (F16OUT && (vec_ok & 2)) {
+        constexpr int PITCH = EPI_PITCH;
+        int8_t *tile = lds_raw + wave * EPI_WAVE;     // this wave's 16.5 KiB
+        __syncthreads();                              // every wave is done with the slices
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int n = n0 + j * 16 + (lane >> 4) * 4;
+            float4 w4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (n + 3 < N) {
+                w4 = *reinterpret_cast<const float4 *>(ws + n);
+            } else {
+                if (n < N) w4.x = ws[n];
+                if (n + 1 < N) w4.y = ws[n + 1];
+                if (n + 2 < N) w4.z = ws[n + 2];
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const v4i &a = acc[i][j];
+                const uint32_t lo = (uint32_t)f2h_bits(((float)a[0] * xsv[i]) * w4.x) |
+                                    ((uint32_t)f2h_bits(((float)a[1] * xsv[i]) * w4.y) << 16);
+                const uint32_t hi = (uint32_t)f2h_bits(((float)a[2] * xsv[i]) * w4.z) |
+                                    ((uint32_t)f2h_bits(((float)a[3] * xsv[i]) * w4.w) << 16);
+                *reinterpret_cast<uint2 *>(tile + (i * 16 + (lane & 15)) * PITCH +
+                                           (j * 16 + (lane >> 4) * 4) * 2) = make_uint2(lo, hi);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0): this wave's LDS writes done
+        // 32 rows x 32 chunks of 16 bytes, 16 per lane; 2 rows per instruction
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const int r = c * 2 + (lane >> 5);
+            const int m = m0 + wave * 32 + r;
+            const int n = n0 + (lane & 31) * 8;
+            const uint4 v = *reinterpret_cast<const uint4 *>(tile + r * PITCH + (lane & 31) * 16);
+            if (m < M) {
+                uint16_t *dst = reinterpret_cast<uint16_t *>(Y) + (int64_t)m * ldy + n;
+                if (n + 7 < N) {
+                    const v4i vv = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+                    __builtin_nontemporal_store(vv, reinterpret_cast<v4i *>(dst));
+                } else {
+                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (n + e < N) dst[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int m = m0 + wave * 32 + i * 16 + (lane & 15);
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                store4<F16OUT>(Y, ldy, (vec_ok & 1) != 0, m, n0 + j * 16 + (lane >> 4) * 4, M, N,
+                               acc[i][j], xsv[i], ws);
+        }
+    }
+}
+
 template <bool W4>
 hipError_t launch_gemm_any(const int8_t *xq, const float *x_scale, const int8_t *wq,
                            const float *w_scale, int64_t M, int64_t N, int64_t K, void *y,
@@ -710,6 +915,22 @@ hipError_t launch_gemm_any(const int8_t *xq, const float *x_scale, const int8_t 
     const int m = (int)M, n = (int)N, k = (int)K;
     if (M > 64) {
         const int tiles_m = (m + T_BM - 1) / T_BM;
+        // 256 x 256 tiles (8-bit weights) where their rounds of 256 CUs cost
+        // less: one takes ~1.8-1.9 times a 256 x 128 tile on a CU (measured
+        // at 4096^3 and 8192 x 8192 -> 24576)
+        const int64_t narrow = (int64_t)tiles_m * ((n + T_BN - 1) / T_BN);
+        const int64_t wide = (int64_t)tiles_m * ((n + W_BN - 1) / W_BN);
+        if (!W4 && 9 * ((wide + 255) / 256) < 5 * ((narrow + 255) / 256)) {
+            const int tiles_n = (n + W_BN - 1) / W_BN;
+            const dim3 grid((unsigned)(tiles_m * tiles_n));
+            if (f16)
+                k_gemm_wide<true><<<grid, dim3(64 * T_WAVES), 0, st>>>(
+                    xq, wq, x_scale, w_scale, m, n, k, y, ldy, tiles_m, tiles_n, vec_ok);
+            else
+                k_gemm_wide<false><<<grid, dim3(64 * T_WAVES), 0, st>>>(
+                    xq, wq, x_scale, w_scale, m, n, k, y, ldy, tiles_m, tiles_n, vec_ok);
+            return hipGetLastError();
+        }
         const int tiles_n = (n + T_BN - 1) / T_BN;
         const dim3 grid((unsigned)(tiles_m * tiles_n));
         if (f16)
