@@ -251,159 +251,156 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
         for (int j = 0; j < 8; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
     v4i xr[4][2];    // activation ring: steps t .. t+3
-    // weight staging ring: steps t+2, t+3 (W4: the packed 8 bytes, widened on
-    // their way to LDS)
-    typename std::conditional<W4, uint2, v4i>::type wst[2];
     v4i wf[8];       // weight fragments of the current step
     auto load_x = [&](int slot, int t) {
         const uint32_t wo = win(t);
 #pragma unroll
         for (int i = 0; i < 2; ++i) xr[slot][i] = bload(rx, xbase[i] + wo);
     };
-    auto load_w = [&](int slot, int t) {
-        if constexpr (W4) wst[slot] = bload8(rw, wbase + winw(t));
-        else wst[slot] = bload(rw, wbase + winw(t));
-    };
-    auto store_w = [&](int slot, int buf) {
-        if constexpr (W4) *reinterpret_cast<v4i *>(&ldsw[buf][tid * 16]) = unpack4(wst[slot]);
-        else *reinterpret_cast<v4i *>(&ldsw[buf][tid * 16]) = wst[slot];
-    };
 
     if constexpr (!W4) {
-    // 8-bit weights go straight from global memory into the LDS ring (slice t
-    // in buffer t & 7), 4 steps ahead of their use: no register staging and
-    // no LDS store, and 3 steps between a slice's load and its first reader,
-    // enough for weights that come from HBM.  Wave w loads fragment w of the
-    // slice (its lanes' 16 bytes land in lane order, as the readers expect).
-    int8_t *ring = lds_raw;
-    auto dma_w = [&](int t) {
-        lds_load16(rw, ring + (t & 7) * T_SLICE + wave * T_FRAG, wbase + winw(t));
-    };
+        // 8-bit weights go straight from global memory into the LDS ring (slice t
+        // in buffer t & 7), 4 steps ahead of their use: no register staging and
+        // no LDS store, and 3 steps between a slice's load and its first reader,
+        // enough for weights that come from HBM.  Wave w loads fragment w of the
+        // slice (its lanes' 16 bytes land in lane order, as the readers expect).
+        int8_t *ring = lds_raw;
+        auto dma_w = [&](int t) {
+            lds_load16(rw, ring + (t & 7) * T_SLICE + wave * T_FRAG, wbase + winw(t));
+        };
 #pragma unroll
-    for (int s = 0; s < 4; ++s) dma_w(s);
+        for (int s = 0; s < 4; ++s) dma_w(s);
 #pragma unroll
-    for (int s = 0; s < 3; ++s) load_x(s, s);
-    __builtin_amdgcn_s_waitcnt(0x0F73);        // vmcnt(3): slices 0..3 have landed
-    __syncthreads();
+        for (int s = 0; s < 3; ++s) load_x(s, s);
+        __builtin_amdgcn_s_waitcnt(0x0F73);        // vmcnt(3): slices 0..3 have landed
+        __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 8; ++j) wf[j] = *reinterpret_cast<const v4i *>(ring + j * T_FRAG + lane * 16);
+        for (int j = 0; j < 8; ++j)
+            wf[j] = *reinterpret_cast<const v4i *>(ring + j * T_FRAG + lane * 16);
 
-    const int nsteps = (KW + 3) & ~3;
-    for (int t0 = 0; t0 < nsteps; t0 += 4) {
+        const int nsteps = (KW + 3) & ~3;
+        for (int t0 = 0; t0 < nsteps; t0 += 4) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int t = t0 + u;
-            const int8_t *nb = ring + ((t + 1) & 7) * T_SLICE;
+            for (int u = 0; u < 4; ++u) {
+                const int t = t0 + u;
+                const int8_t *nb = ring + ((t + 1) & 7) * T_SLICE;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+                for (int j = 0; j < 8; ++j) {
 #pragma unroll
-                for (int i = 0; i < 2; ++i) acc[i][j] = mfma(wf[j], xr[u][i], acc[i][j]);
-                wf[j] = *reinterpret_cast<const v4i *>(nb + j * T_FRAG + lane * 16);
-                // the step's three global loads (weight slice t+4 into its
-                // buffer, then the two activation fragments of t+3) spread
-                // over its products, each pinned in place: issued together at
-                // the top of the step, the two waves of a SIMD queued all their
-                // loads at once and then waited on the address path with no
-                // products to issue
-                if (j == 1) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    dma_w(t + 4);
-                    __builtin_amdgcn_sched_barrier(0);
+                    for (int i = 0; i < 2; ++i) acc[i][j] = mfma(wf[j], xr[u][i], acc[i][j]);
+                    wf[j] = *reinterpret_cast<const v4i *>(nb + j * T_FRAG + lane * 16);
+                    // the step's three global loads (weight slice t+4 into its
+                    // buffer, then the two activation fragments of t+3) spread
+                    // over its products, each pinned in place: issued together at
+                    // the top of the step, the two waves of a SIMD queued all their
+                    // loads at once and then waited on the address path with no
+                    // products to issue
+                    if (j == 1) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        dma_w(t + 4);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if (j == 4) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        xr[(u + 3) & 3][0] = bload(rx, xbase[0] + win(t + 3));
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if (j == 7) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        xr[(u + 3) & 3][1] = bload(rx, xbase[1] + win(t + 3));
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
-                if (j == 4) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    xr[(u + 3) & 3][0] = bload(rx, xbase[0] + win(t + 3));
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                if (j == 7) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    xr[(u + 3) & 3][1] = bload(rx, xbase[1] + win(t + 3));
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                // Slice t+2, read from the next step on, was loaded at step t-2;
+                // 8 loads were issued after it (2 in its step, 3 in each later
+                // one), and memory loads complete in order, so vmcnt(8) means it
+                // has landed in this wave's part of the buffer; the barrier then
+                // publishes every wave's part.  The buffer a step loads into
+                // (slice t+4: buffer (t-4) & 7) was last read in step t-5.
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_waitcnt(0x0F78);    // vmcnt(8)
+                __builtin_amdgcn_s_barrier();
+                // keep each step's products inside the step: hoisting them above
+                // the barrier would put them right behind the LDS reads they use
+                __builtin_amdgcn_sched_barrier(0);
             }
-            // Slice t+2, read from the next step on, was loaded at step t-2;
-            // 8 loads were issued after it (2 in its step, 3 in each later
-            // one), and memory loads complete in order, so vmcnt(8) means it
-            // has landed in this wave's part of the buffer; the barrier then
-            // publishes every wave's part.  The buffer a step loads into
-            // (slice t+4: buffer (t-4) & 7) was last read in step t-5.
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt(0x0F78);    // vmcnt(8)
-            __builtin_amdgcn_s_barrier();
-            // keep each step's products inside the step: hoisting them above
-            // the barrier would put them right behind the LDS reads they use
-            __builtin_amdgcn_sched_barrier(0);
         }
-    }
-    // the slices loaded past the last step still land in LDS, which the
-    // epilogue reuses: wait for them
-    __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
+        // the slices loaded past the last step still land in LDS, which the
+        // epilogue reuses: wait for them
+        __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
     } else {
-    // 4-bit weights: staged through registers, widened on their way to LDS
-    // prologue: weight slices 0 and 1 in LDS, slice 2 staged, activations 0..2 in flight
+        // 4-bit weights: staged through registers (the packed 8 bytes of slices
+        // t+2 and t+3), widened on their way into a ring of 4 LDS buffers
+        uint2 wst[2];
+        auto load_w = [&](int slot, int t) { wst[slot] = bload8(rw, wbase + winw(t)); };
+        auto store_w = [&](int slot, int buf) {
+            *reinterpret_cast<v4i *>(&ldsw[buf][tid * 16]) = unpack4(wst[slot]);
+        };
+        // prologue: weight slices 0 and 1 in LDS, slice 2 staged, activations 0..2 in flight
 #pragma unroll
-    for (int s = 0; s < 3; ++s) load_x(s, s);
-    load_w(0, 0);
-    load_w(1, 1);
-    store_w(0, 0);
-    store_w(1, 1);
-    load_w(0, 2);
-    __syncthreads();
+        for (int s = 0; s < 3; ++s) load_x(s, s);
+        load_w(0, 0);
+        load_w(1, 1);
+        store_w(0, 0);
+        store_w(1, 1);
+        load_w(0, 2);
+        __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 8; ++j) wf[j] = *reinterpret_cast<const v4i *>(&ldsw[0][j * T_FRAG + lane * 16]);
+        for (int j = 0; j < 8; ++j)
+            wf[j] = *reinterpret_cast<const v4i *>(&ldsw[0][j * T_FRAG + lane * 16]);
 
-    const int nsteps = (KW + 3) & ~3;
-    for (int t0 = 0; t0 < nsteps; t0 += 4) {
+        const int nsteps = (KW + 3) & ~3;
+        for (int t0 = 0; t0 < nsteps; t0 += 4) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int t = t0 + u;
-            const int nb = (u + 1) & 3;
+            for (int u = 0; u < 4; ++u) {
+                const int t = t0 + u;
+                const int nb = (u + 1) & 3;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+                for (int j = 0; j < 8; ++j) {
 #pragma unroll
-                for (int i = 0; i < 2; ++i) acc[i][j] = mfma(wf[j], xr[u][i], acc[i][j]);
-                wf[j] = *reinterpret_cast<const v4i *>(&ldsw[nb][j * T_FRAG + lane * 16]);
-                // The step's three global loads (weight slice t+3, then the two
-                // activation fragments of t+3) and the LDS store of slice t+2
-                // are spread over its products, each pinned in place: issued
-                // together at the top of the step, the two waves of a SIMD
-                // queued all their loads at once and then waited on the
-                // address path with no products to issue.  The slice stored
-                // here was loaded a step earlier, so its wait leaves the later
-                // loads in flight.
-                if (j == 1) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    load_w((u + 1) & 1, t + 3);
-                    __builtin_amdgcn_sched_barrier(0);
+                    for (int i = 0; i < 2; ++i) acc[i][j] = mfma(wf[j], xr[u][i], acc[i][j]);
+                    wf[j] = *reinterpret_cast<const v4i *>(&ldsw[nb][j * T_FRAG + lane * 16]);
+                    // The step's three global loads (weight slice t+3, then the two
+                    // activation fragments of t+3) and the LDS store of slice t+2
+                    // are spread over its products, each pinned in place: issued
+                    // together at the top of the step, the two waves of a SIMD
+                    // queued all their loads at once and then waited on the
+                    // address path with no products to issue.  The slice stored
+                    // here was loaded a step earlier, so its wait leaves the later
+                    // loads in flight.
+                    if (j == 1) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        load_w((u + 1) & 1, t + 3);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if (j == 4) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        xr[(u + 3) & 3][0] = bload(rx, xbase[0] + win(t + 3));
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if (j == 5) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        store_w(u & 1, (u + 2) & 3);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if (j == 6) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        xr[(u + 3) & 3][1] = bload(rx, xbase[1] + win(t + 3));
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
-                if (j == 4) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    xr[(u + 3) & 3][0] = bload(rx, xbase[0] + win(t + 3));
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                if (j == 5) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    store_w(u & 1, (u + 2) & 3);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                if (j == 6) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    xr[(u + 3) & 3][1] = bload(rx, xbase[1] + win(t + 3));
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                // Before the barrier only the store must be complete: LDS
+                // operations of a wave complete in order, so at most the 2 later
+                // fragment reads (6 and 7) may still be in flight (they read slice
+                // t+1, which nobody overwrites before two more barriers).
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_waitcnt(0xc07f | (2 << 8));   // lgkmcnt(2)
+                __builtin_amdgcn_s_barrier();
+                // keep each step's products inside the step: hoisting them above
+                // the barrier would put them right behind the LDS reads they use
+                __builtin_amdgcn_sched_barrier(0);
             }
-            // Before the barrier only the store must be complete: LDS
-            // operations of a wave complete in order, so at most the 2 later
-            // fragment reads (6 and 7) may still be in flight (they read slice
-            // t+1, which nobody overwrites before two more barriers).
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt(0xc07f | (2 << 8));   // lgkmcnt(2)
-            __builtin_amdgcn_s_barrier();
-            // keep each step's products inside the step: hoisting them above
-            // the barrier would put them right behind the LDS reads they use
-            __builtin_amdgcn_sched_barrier(0);
         }
-    }
 
     }
 
