@@ -331,6 +331,9 @@ def main():
                     help="bracket the product kernel with HIP events on every n-th timed step")
     ap.add_argument("--stage-steps", type=int, default=20,
                     help="steps of the separate, untimed pass with an event between stages")
+    ap.add_argument("--layer-launches", type=int, default=100,
+                    help="quant + product pairs of the serving-time layer timed back to back "
+                         "between one event pair (0: take the stage pass's two stages)")
     ap.add_argument("--norm-launches", type=int, default=100,
                     help="launches of the fused RMS-norm + quantization (and of the plain "
                          "quantizer) timed between one pair of events (0: skip)")
@@ -457,6 +460,29 @@ def main():
             per[n] += ev[j].elapsed_time(ev[j + 1])
     per = {n: v / max(1, args.stage_steps) for n, v in per.items()}    # ms per call
 
+    # The serving-time layer as a deployed model runs it (the weights folded
+    # offline): quantization + product, --layer-launches pairs back to back on
+    # the stream between one event pair, on the step's folded weights.
+    layer_ms = per["quant"] + per["gemm"]
+    layer_how = "stage pass (events between the calls)"
+    if args.layer_launches > 0:
+        def layer_pair():
+            st = L.sq_quant_act_per_token(p["x"], M, K, K, p["inv"], p["xq"], p["xsc"], hs)
+            st |= L.sq_w8a8_gemm(p["xq"], p["xsc"], p["wq"], p["wsc"], M, N, K, p["y"], N,
+                                 sq.SQ_OUT_F16, hs)
+            if st:
+                raise RuntimeError("layer launch failed")
+        for _ in range(5):
+            layer_pair()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.layer_launches):
+            layer_pair()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        layer_ms = e0.elapsed_time(e1) / args.layer_launches
+        layer_how = f"{args.layer_launches} quant + product pairs back to back, one event pair"
+
     # The normalization in front of the layer with 1/s folded into its weight:
     # the fused RMS-norm + quantization against the plain quantizer on the
     # same batch, each timed as a run of launches between one event pair
@@ -540,7 +566,6 @@ def main():
     ops = 2.0 * M * N * K
     ms_step = wall * 1e3 / args.steps
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
-    layer_ms = per["quant"] + per["gemm"]
     layer_tops = ops / (layer_ms * 1e-3) / 1e12 if layer_ms > 0 else 0.0
     traffic = read_traffic(wl.name)
     # algorithmic HBM bytes of the runtime layer per batch (int8 weights and
@@ -565,7 +590,7 @@ def main():
                    "step": "calibrate + smooth/fold + per-token quant + W8A8 GEMM"},
         "stage_ms": {n: round(v, 4) for n, v in per.items()},
         "layer": {"what": "serving-time layer: per-token quant + W8A8 GEMM (weights folded offline)",
-                  "ms": round(layer_ms, 4), "tops": round(layer_tops, 2),
+                  "how": layer_how, "ms": round(layer_ms, 4), "tops": round(layer_tops, 2),
                   "frac_int8_peak": round(layer_tops / PEAK_INT8_TOPS, 4),
                   "hbm_gbs_algorithmic": round(layer_bytes / (layer_ms * 1e-3) / 1e9, 1)
                   if layer_ms > 0 else 0.0},
