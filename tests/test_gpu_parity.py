@@ -389,6 +389,20 @@ def test_gemm_extreme_sums_and_strided_output(sq, dev, orc):
     assert_f16_close(out[:, :24], orc.dequant(orc.gemm_i32(xq, wq), xs, ws))
 
 
+def test_gemm_tile_path_at_max_k(sq, dev, orc):
+    """65 tokens (the tile kernel) at the largest K the library takes: window
+    offsets up to 2047 KiB per row block, int32 sums near their bound."""
+    M, N, K = 65, 40, 131056
+    xq = W.random_i8(920, M, K, -128, 127)
+    wq = W.random_i8(921, N, K, -128, 127)
+    acc = sq.gemm(T(pack(xq), dev), None, T(pack(wq), dev), None, M, N, K, out_kind=sq.SQ_OUT_I32)
+    assert np.array_equal(H(acc), orc.gemm_i32(xq, wq))
+    xs = W.random_scales(922, M, 1e-6, 1e-5)
+    ws = W.random_scales(923, N, 1e-6, 1e-5)
+    y = sq.gemm(T(pack(xq), dev), T(xs, dev), T(pack(wq), dev), T(ws, dev), M, N, K)
+    assert_f16_close(H(y), orc.dequant(orc.gemm_i32(xq, wq), xs, ws))
+
+
 def test_gemm_nan_row_propagates(sq, dev, orc):
     xq = W.random_i8(910, 4, 64)
     wq = W.random_i8(911, 8, 64)
