@@ -111,6 +111,7 @@ def test_rmsnorm_quant_matches_oracle(sq, dev, orc, name, m):
 @pytest.mark.parametrize("M,K,ld", [(1, 16, 16), (3, 48, 56), (37, 4096, 4096), (17, 2064, 2064),
                                     (9, 6144, 6144), (3, 7184, 7192), (33, 8192, 8200),
                                     (2, 8208, 8208), (64, 16384, 16384), (65, 8192, 8192),
+                                    (100, 4096, 4104), (600, 11008, 11008), (520, 16384, 16392),
                                     (5, 32784, 32784), (1, 131056, 131056)])
 def test_rmsnorm_quant_ragged_long_and_strided(sq, dev, orc, M, K, ld):
     h = W.random_f16(800 + K, M, ld, 3.0)

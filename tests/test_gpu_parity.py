@@ -299,10 +299,15 @@ def test_quant_matches_oracle(sq, dev, orc, name):
 
 
 # up to 64 tokens and K <= 16384 the one-token-per-workgroup form runs (one or
-# two chunks per lane), beyond it the 8-row forms
+# two chunks per lane); beyond 64 tokens the row-group form (2 rows per
+# workgroup up to 512 tokens, 4 beyond; 2 waves per row up to K = 8192, 4 up
+# to 16384), and past K = 16384 the 8-row streaming form
 @pytest.mark.parametrize("M,K,ld", [(1, 16, 16), (3, 48, 56), (17, 2064, 2064), (2, 4112, 4128),
                                     (4, 11008, 11024), (64, 16384, 16384), (33, 8192, 8192),
                                     (65, 4096, 4096), (64, 16400, 16400),
+                                    (70, 16, 16), (100, 4096, 4104), (513, 1040, 1040),
+                                    (300, 11008, 11024), (520, 8208, 8208), (600, 16384, 16392),
+                                    (130, 16400, 16400),
                                     (5, 32784, 32784), (2, 40000, 40000), (1, 131056, 131056)])
 def test_quant_ragged_long_and_strided(sq, dev, orc, M, K, ld):
     x = W.random_f16(600 + K, M, ld, 2.0)

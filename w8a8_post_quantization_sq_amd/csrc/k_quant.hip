@@ -232,25 +232,29 @@ k_quant_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
     }
 }
 
-// Register-resident variant for K <= 8192: 1024 threads, 8 rows, 2 waves per
-// row.  Every lane loads all its chunks of its row at once (the only HBM read
-// of X), keeps x * inv_s in registers through the row reduction (wave
-// shuffles, then the 2 waves of a row through LDS), quantizes, and writes its
-// codes into an LDS copy of the 8 rows; the group then leaves LDS as packed
-// 16-byte pieces, consecutive lanes on consecutive rows (128-byte runs).
-template <int CPL, bool NORM, int QMAX>
-__global__ void __launch_bounds__(1024)
+// Register-resident variant for K <= 16384: RG rows per workgroup, WPR waves
+// per row (RG * WPR <= 16).  Every lane loads all its chunks of its row at
+// once (the only HBM read of X), keeps x * inv_s in registers through the row
+// reduction (wave shuffles, then the WPR waves of a row through LDS),
+// quantizes, and writes its codes into an LDS copy of the RG rows; the group
+// then leaves LDS as packed 16-byte pieces, consecutive lanes on consecutive
+// rows (runs of RG * 16 bytes).  Workgroups of 512 threads let two share a CU
+// at up to 128 registers a lane, so one group's loads overlap another's
+// reduction and stores.
+template <int CPL, bool NORM, int QMAX, int RG, int WPR>
+__global__ void __launch_bounds__(RG * WPR * 64)
 k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
                  const float *__restrict__ inv_s, double eps, int8_t *__restrict__ xq,
                  float *__restrict__ x_scale) {
-    extern __shared__ __align__(16) int8_t codes[];     // [8][KW * 64]
+    static_assert(RG * WPR <= 16 && (RG == 2 || RG == 4 || RG == 8), "group shape");
+    extern __shared__ __align__(16) int8_t codes[];     // [RG][KW * 64]
     __shared__ uint32_t s_max[16];
     __shared__ double s_ss[16];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;                   // 0..15
-    const int r = wave >> 1;                             // row of the group
-    const int h = wave & 1;                              // which half of the row's chunks
-    const int64_t m0 = (int64_t)blockIdx.x * QR;
+    const int wave = threadIdx.x >> 6;
+    const int r = wave / WPR;                            // row of the group
+    const int h = wave % WPR;                            // which of the row's chunk phases
+    const int64_t m0 = (int64_t)blockIdx.x * RG;
     const int64_t m = m0 + r;
     const int64_t KW = (K + 63) >> 6;
     const int64_t pitch = KW * 64;
@@ -268,12 +272,12 @@ k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t l
         Chunk ch[ROUND];
 #pragma unroll
         for (int c = 0; c < ROUND; ++c) {
-            const int64_t k = ((int64_t)((c0 + c) * 2 + h) * 64 + lane) * 8;
+            const int64_t k = ((int64_t)((c0 + c) * WPR + h) * 64 + lane) * 8;
             if (real && k < K) ch[c] = load8(row, inv_s, k);
         }
 #pragma unroll
         for (int c = 0; c < ROUND; ++c) {
-            const int64_t k = ((int64_t)((c0 + c) * 2 + h) * 64 + lane) * 8;
+            const int64_t k = ((int64_t)((c0 + c) * WPR + h) * 64 + lane) * 8;
             if (real && k < K) scale8<NORM>(ch[c], v[c0 + c], amax, &ss);
         }
     }
@@ -284,8 +288,12 @@ k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t l
         if (NORM) s_ss[wave] = ss;
     }
     __syncthreads();
-    const uint32_t a0 = s_max[2 * r], a1 = s_max[2 * r + 1];
-    const uint32_t arow = a0 > a1 ? a0 : a1;
+    uint32_t arow = 0;
+#pragma unroll
+    for (int i = 0; i < WPR; ++i) {
+        const uint32_t t = s_max[r * WPR + i];
+        arow = arow > t ? arow : t;
+    }
     float scale, rr;
     bool zero;
     row_params<QMAX>(arow, scale, rr, zero);
@@ -293,27 +301,32 @@ k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t l
     zero = zero || !real;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-        const int64_t k = ((int64_t)(c * 2 + h) * 64 + lane) * 8;
+        const int64_t k = ((int64_t)(c * WPR + h) * 64 + lane) * 8;
         if (k < pitch)   // codes past K (padding) are zero
             *reinterpret_cast<uint2 *>(codes + r * pitch + k) =
                 (k < K) ? quant8<QMAX>(v[c], rr, zero) : make_uint2(0u, 0u);
     }
-    // the normalized scale once the row's values are no longer held
-    if (NORM && real && h == 0 && lane == 0)
-        x_scale[m] = norm_scale(arow, s_ss[2 * r] + s_ss[2 * r + 1], K, eps);
+    // the normalized scale once the row's values are no longer held (the
+    // row's partial sums added in wave order)
+    if (NORM && real && h == 0 && lane == 0) {
+        double t = 0.0;
+#pragma unroll
+        for (int i = 0; i < WPR; ++i) t += s_ss[r * WPR + i];
+        x_scale[m] = norm_scale(arow, t, K, eps);
+    }
     __syncthreads();
     const int64_t rb = m0 >> 4;
-    const int half = (int)(m0 & 15);
+    const int first = (int)(m0 & 15);                    // the group's first row in its block
     int8_t *base = xq + ((rb * KW) << 10);
-    const int64_t pieces = (int64_t)QR * 4 * KW;
-    for (int64_t p = threadIdx.x; p < pieces; p += 1024) {
-        const int pr = (int)(p & 7);
-        const int q = (int)((p >> 3) & 3);
-        const int64_t kw = p >> 5;
+    const int64_t pieces = (int64_t)RG * 4 * KW;
+    for (int64_t p = threadIdx.x; p < pieces; p += RG * WPR * 64) {
+        const int pr = (int)(p % RG);
+        const int q = (int)((p / RG) & 3);
+        const int64_t kw = p / (RG * 4);
         // plain stores: the product reads the codes next, and finds them in
         // the caches (non-temporal stores sent them to HBM, which cost the
         // product ~2 us at 2048 x 4096)
-        *reinterpret_cast<v4i *>(base + ((kw * 64 + q * 16 + half + pr) << 4)) =
+        *reinterpret_cast<v4i *>(base + ((kw * 64 + q * 16 + first + pr) << 4)) =
             *reinterpret_cast<const v4i *>(codes + pr * pitch + kw * 64 + q * 16);
     }
 }
@@ -395,19 +408,35 @@ hipError_t launch_rows(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, con
             k_quant_row1<2, NORM, QMAX><<<g, dim3(1024), 0, st>>>(x, M, K, ldx, inv_s, eps, xq, x_scale);
         return hipGetLastError();
     }
-    // every row of the padded row blocks, 8 rows per workgroup
-    const int64_t groups = (M + 15) / 16 * 2;
-    const int64_t cpl = (K + 1023) / 1024;        // chunks of 8 per lane, 2 waves per row
-    const size_t lds = (size_t)QR * ((K + 63) / 64) * 64;
-    const dim3 g((unsigned)groups);
-#define SQ_QR(C) \
-    k_quant_rows_reg<C, NORM, QMAX><<<g, dim3(1024), lds, st>>>(x, M, K, ldx, inv_s, eps, xq, \
-                                                                 x_scale)
-    if (cpl <= 1) SQ_QR(1);
-    else if (cpl <= 2) SQ_QR(2);
-    else if (cpl <= 4) SQ_QR(4);
-    else if (cpl <= 8) SQ_QR(8);     // up to 8192 channels: 64 KiB LDS
-    else k_quant_rows<NORM, QMAX><<<g, dim3(512), 0, st>>>(x, M, K, ldx, inv_s, eps, xq, x_scale);
+    // every row of the padded row blocks: 4 rows per workgroup, or 2 where
+    // that leaves too few workgroups for the CUs; 2 waves per row up to 8192
+    // channels, 4 up to 16384
+    const int64_t blocks = (M + 15) / 16;
+    const int64_t KW = (K + 63) / 64;
+#define SQ_QR(C, RG, WPR)                                                                        \
+    k_quant_rows_reg<C, NORM, QMAX, RG, WPR>                                                     \
+        <<<dim3((unsigned)(blocks * (16 / RG))), dim3(RG * WPR * 64), (size_t)RG * KW * 64, st>>>( \
+            x, M, K, ldx, inv_s, eps, xq, x_scale)
+    if (K <= 8192) {
+        const int64_t cpl = (K + 1023) / 1024;    // chunks of 8 per lane
+        if (M > 512) {
+            if (cpl <= 1) SQ_QR(1, 4, 2);
+            else if (cpl <= 2) SQ_QR(2, 4, 2);
+            else if (cpl <= 4) SQ_QR(4, 4, 2);
+            else SQ_QR(8, 4, 2);
+        } else {
+            if (cpl <= 1) SQ_QR(1, 2, 2);
+            else if (cpl <= 2) SQ_QR(2, 2, 2);
+            else if (cpl <= 4) SQ_QR(4, 2, 2);
+            else SQ_QR(8, 2, 2);
+        }
+    } else if (K <= 16384) {
+        if (M > 512) SQ_QR(8, 4, 4);
+        else SQ_QR(8, 2, 4);
+    } else {
+        k_quant_rows<NORM, QMAX><<<dim3((unsigned)(blocks * 2)), dim3(512), 0, st>>>(
+            x, M, K, ldx, inv_s, eps, xq, x_scale);
+    }
 #undef SQ_QR
     return hipGetLastError();
 }
