@@ -357,8 +357,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; multi-GPU runs are not part of it "
-              "(use --gpus 1)", file=sys.stderr)
+        print("bench.py: the library runs on one GPU; a sharded multi-GPU path is not "
+              "implemented (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch
