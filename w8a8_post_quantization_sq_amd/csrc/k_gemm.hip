@@ -268,11 +268,20 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
         auto dma_w = [&](int t) {
             lds_load16(rw, ring + (t & 7) * T_SLICE + wave * T_FRAG, wbase + winw(t));
         };
+        // Prologue: slices 0..3 and activation steps 0..2, interleaved (slice s,
+        // then step s's two fragments), so the first products wait only for
+        // the first two slices and not for the whole burst every CU issues at
+        // once: after slice 1, 6 loads follow (steps 1 and 2, slices 2 and 3).
 #pragma unroll
-        for (int s = 0; s < 4; ++s) dma_w(s);
-#pragma unroll
-        for (int s = 0; s < 3; ++s) load_x(s, s);
-        __builtin_amdgcn_s_waitcnt(0x0F73);        // vmcnt(3): slices 0..3 have landed
+        for (int s = 0; s < 3; ++s) {
+            __builtin_amdgcn_sched_barrier(0);
+            dma_w(s);
+            load_x(s, s);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        dma_w(3);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0x0F76);        // vmcnt(6): slices 0 and 1 have landed
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < 8; ++j)
@@ -315,10 +324,15 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
                 // 8 loads were issued after it (2 in its step, 3 in each later
                 // one), and memory loads complete in order, so vmcnt(8) means it
                 // has landed in this wave's part of the buffer; the barrier then
-                // publishes every wave's part.  The buffer a step loads into
-                // (slice t+4: buffer (t-4) & 7) was last read in step t-5.
+                // publishes every wave's part.  Slices 2 and 3 came with the
+                // prologue, 6 loads before the end of steps 0 and 1.  The buffer
+                // a step loads into (slice t+4: buffer (t-4) & 7) was last read
+                // in step t-5.
                 __builtin_amdgcn_sched_barrier(0);
-                __builtin_amdgcn_s_waitcnt(0x0F78);    // vmcnt(8)
+                if (t < 2)
+                    __builtin_amdgcn_s_waitcnt(0x0F76);    // vmcnt(6)
+                else
+                    __builtin_amdgcn_s_waitcnt(0x0F78);    // vmcnt(8)
                 __builtin_amdgcn_s_barrier();
                 // keep each step's products inside the step: hoisting them above
                 // the barrier would put them right behind the LDS reads they use
