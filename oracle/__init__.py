@@ -17,8 +17,9 @@ Pages cited:
   [P4] Pith review of arXiv 2506.01967 ("Smooth Rotation")
   [P5] "Quantization" (learn-kernels.com)
 
-Parity unpinned: ``quant_error_report`` only reports layer-wise error; the
-pages print no values to pin it against.
+``quant_error_report`` (layer-wise error) is pinned by hand-worked one-token
+cases and by an exact-grid case with zero error; the pages print no values for
+it on real layers.
 """
 from __future__ import annotations
 
@@ -342,8 +343,9 @@ def unquantized_fp16_rewrite(x: np.ndarray, w: np.ndarray, s: np.ndarray, inv_s:
 def quant_error_report(x: np.ndarray, x_cal: np.ndarray, w: np.ndarray, alpha: Optional[float]):
     """Layer-wise squared-Frobenius error ||Y_q - XW||^2 / ||XW||^2 of the W8A8
     layer, smoothed with strength alpha, or unsmoothed (S = I) for None
-    ([P4] core discovery measures this quantity).  Parity unpinned: the pages
-    print no values for it."""
+    ([P4] core discovery measures this quantity).  The pages print no values
+    for it; tests pin it on hand-worked one-token cases (S = I and alpha = 0,
+    1/2, 1) and on inputs on the int8 grid, where it is exactly 0."""
     ref = matmul_fp64(x, w)
     if alpha is None:
         K = x.shape[1]

@@ -421,6 +421,42 @@ def test_quality_report_smoothing_helps_on_outliers(orc):
     assert e_sq < e_id
 
 
+def test_quality_report_hand_cases(orc):
+    """The layer error ||Y_q - XW||^2 / ||XW||^2 on one token x = [1, 0.5] and one
+    output channel w = [1, 1], worked by hand from the definitions (x_cal = x):
+    - S = I, and alpha = 0 (s_j = 1 / max|W_j| = 1): 0.5 * 127 = 63.5 rounds to
+      64 (ties to even), the weights are exact, Y_q = (127 + 64) / 127;
+    - alpha = 1 (s = max|X_j| = [1, 0.5]): the activation codes become exact
+      [127, 127] and the weight row 0.5 takes the same tie, so the same error;
+    - alpha = 1/2 (s = [1, sqrt(1/2)]): 0.7071 * 127 = 89.80 rounds to 90 on both
+      sides, Y_q = (127^2 + 90^2) / 127^2 = 24229 / 16129.
+    The scales 1/127 are float32, so the values hold to ~1e-5 relative."""
+    x = np.array([[1.0, 0.5]], np.float16)
+    w = np.array([[1.0], [1.0]], np.float16)
+    ref = 1.5 ** 2
+    tie = (191.0 / 127.0 - 1.5) ** 2 / ref            # = 1 / 145161
+    half = (24229.0 / 16129.0 - 1.5) ** 2 / ref
+    for alpha in (None, 0.0, 1.0):
+        assert orc.quant_error_report(x, x, w, alpha) == pytest.approx(tie, rel=1e-4)
+    assert orc.quant_error_report(x, x, w, 0.5) == pytest.approx(half, rel=1e-4)
+    assert half < tie / 3
+
+
+def test_quality_report_zero_on_the_grid(orc):
+    """Tokens and weight columns that are multiples of 2^-7 with a largest
+    magnitude of exactly 127 * 2^-7 quantize without error when S = I
+    (r = 127 / (127 * 2^-7) = 128 exactly), so the layer error is exactly 0."""
+    rng = np.random.default_rng(21)
+    M, K, N = 6, 64, 5
+    xc = rng.integers(-126, 127, size=(M, K))
+    xc[:, 7] = 127
+    wc = rng.integers(-126, 127, size=(K, N))
+    wc[9, :] = -127
+    x = (xc * 2.0 ** -7).astype(np.float16)
+    w = (wc * 2.0 ** -7).astype(np.float16)
+    assert orc.quant_error_report(x, x, w, None) == 0.0
+
+
 # ---- the input generator ------------------------------------------------------------
 
 def test_generator_chunked_draws_match_single_draw():
