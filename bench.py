@@ -116,7 +116,9 @@ def prefill_leg(torch, workloads, sq, L, dev, stream, hs, launches):
     (8192 x 8192 -> 3 x 8192, one smoothed X for the three projections)
     configurations, on their own calibrated, folded and quantized codes (the
     matrix cores' power, and so their clock, depends on the codes), each as
-    `launches` launches between one event pair."""
+    `launches` launches between one event pair; and the per-token quantizer of
+    the same batches, `launches` launches likewise (HBM-bound: 2MK bytes of X,
+    MK of codes, 4M of scales)."""
     out = {"peak": PEAK_INT8_TOPS, "unit": "TOP/s"}
     for name in ("down11008", "prefill8192x3"):
         wl = workloads.WORKLOADS[name]
@@ -142,7 +144,23 @@ def prefill_leg(torch, workloads, sq, L, dev, stream, hs, launches):
                                        xsc.data_ptr(), hs)
         if st:
             raise RuntimeError(f"{name}: preparing the product failed")
-        del w, x, xcal
+        del w, xcal
+
+        def quant():
+            return L.sq_quant_act_per_token(x.data_ptr(), M, K, K, inv.data_ptr(), xq.data_ptr(),
+                                            xsc.data_ptr(), hs)
+        for _ in range(3):
+            if quant():
+                raise RuntimeError(f"{name}: quantizer failed")
+        q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        q0.record(stream)
+        for _ in range(launches):
+            quant()
+        q1.record(stream)
+        torch.cuda.synchronize()
+        q_us = q0.elapsed_time(q1) * 1e3 / launches
+        q_gbs = (3.0 * M * K + 4.0 * M) / (q_us * 1e-6) / 1e9
+        del x
 
         def run():
             return L.sq_w8a8_gemm(xq.data_ptr(), xsc.data_ptr(), wq.data_ptr(), wsc.data_ptr(), M,
@@ -159,8 +177,11 @@ def prefill_leg(torch, workloads, sq, L, dev, stream, hs, launches):
         us = e0.elapsed_time(e1) * 1e3 / launches
         tops = 2.0 * M * N * K / (us * 1e-6) / 1e12
         out[name] = {"M": M, "K": K, "N": N, "us": round(us, 2), "tops": round(tops, 1),
-                     "frac": round(tops / PEAK_INT8_TOPS, 4)}
-        log(f"product {name}: {us:.1f} us, {tops:.0f} TOP/s")
+                     "frac": round(tops / PEAK_INT8_TOPS, 4),
+                     "quant_us": round(q_us, 2), "quant_gbs": round(q_gbs, 1),
+                     "quant_frac_hbm": round(q_gbs / PEAK_HBM_GBS, 4)}
+        log(f"product {name}: {us:.1f} us, {tops:.0f} TOP/s; quantizer {q_us:.1f} us, "
+            f"{q_gbs:.0f} GB/s")
         del xq, wq, y
     return out
 
