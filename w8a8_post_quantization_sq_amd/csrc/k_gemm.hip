@@ -324,10 +324,11 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
                 // 8 loads were issued after it (2 in its step, 3 in each later
                 // one), and memory loads complete in order, so vmcnt(8) means it
                 // has landed in this wave's part of the buffer; the barrier then
-                // publishes every wave's part.  Slices 2 and 3 came with the
-                // prologue, 6 loads before the end of steps 0 and 1.  The buffer
-                // a step loads into (slice t+4: buffer (t-4) & 7) was last read
-                // in step t-5.
+                // publishes every wave's part.  Slices 2 and 3 were issued in
+                // the prologue, and only 6 loads follow each of them by the end of
+                // steps 0 and 1 respectively, so those two steps wait on vmcnt(6).
+                // The buffer a step loads into (slice t+4: buffer (t-4) & 7) was
+                // last read in step t-5.
                 __builtin_amdgcn_sched_barrier(0);
                 if (t < 2)
                     __builtin_amdgcn_s_waitcnt(0x0F76);    // vmcnt(6)
