@@ -141,6 +141,16 @@ def w4a4_layer(x: np.ndarray, w: np.ndarray, s: np.ndarray, inv_s: np.ndarray, r
     return y, xs
 
 
+def act_step(x_scale: np.ndarray, d: int, rotate: bool) -> float:
+    """Mean activation step size in the orthonormal convention.  The 4-bit
+    quantizer's scale is max|v| / 7 of v = (x / s) H with the unnormalized H,
+    whose entries are +-1; the rotation of [P4] key machinery is R = H / sqrt(d)
+    (entries +-1/sqrt(d)), so the step of (x / s) R is scale / sqrt(d).
+    Unrotated, the step is the scale itself."""
+    step = np.asarray(x_scale, np.float64) / (np.sqrt(d) if rotate else 1.0)
+    return float(np.mean(step))
+
+
 def w4a4_compare(x: np.ndarray, x_cal: np.ndarray, w: np.ndarray,
                  rows: Optional[np.ndarray] = None) -> Dict[str, Dict[str, float]]:
     """Original, smoothing alone (alpha 1/2), rotation alone and smoothing then
@@ -160,7 +170,6 @@ def w4a4_compare(x: np.ndarray, x_cal: np.ndarray, w: np.ndarray,
                 continue        # no statistics involved
             s, inv = factors(stat, w, alpha)
             y, xs = w4a4_layer(x, w, s, inv, rot, rows)
-            step = xs.astype(np.float64) / (np.sqrt(d) if rot else 1.0)
             out[f"{name}/{tag}"] = {"layer_error": layer_error(y, ref),
-                                    "act_step": float(np.mean(step))}
+                                    "act_step": act_step(xs, d, rot)}
     return out

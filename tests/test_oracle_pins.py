@@ -375,6 +375,57 @@ def test_chain_bound_catches_planted_mistakes(orc):
     assert orc.rel_fro(y_tr, ref) > 1.5 * orc.rel_fro(c.y64, ref)
 
 
+def _layer_inputs(orc, name, rows):
+    wl = W.WORKLOADS[name]
+    inp = W.generate(wl, m=rows)
+    s, inv, st = orc.smoothing_factors(orc.calibrate_absmax(inp.x_cal), orc.row_absmax(inp.w),
+                                       wl.alpha)
+    assert st == 0
+    wq, wsc = orc.fold_quant_weights(inp.w, s)
+    return np.ascontiguousarray(inp.x), s, inv, wq, wsc
+
+
+def _layer_equals_staged(orc, block, x, inv, wq, wsc):
+    """block(x, inv_s, wq, w_scale) against A4, A5 and A6 called one by one
+    (each pinned on its own above), bit for bit in float64."""
+    xq, xs = orc.quant_act_per_token(x, inv)
+    staged = orc.dequant(orc.gemm_i32(xq, wq), xs, wsc)
+    got = block(x, inv, wq, wsc)
+    return got.shape == staged.shape and np.array_equal(got.view(np.uint64),
+                                                        staged.view(np.uint64))
+
+
+@pytest.mark.parametrize("name,rows", [("tiny", None), ("qkv4096", 64)])
+def test_layer_block_equals_the_staged_chain(orc, name, rows):
+    """The CPU baseline's unit of work (quantization + int32 product +
+    dequantization in one C call, on a block of tokens) is exactly the
+    per-stage oracle chain: the tiny workload, and a 64-token block of the
+    2048 x 4096 x 4096 layer with its real folded weights."""
+    x, s, inv, wq, wsc = _layer_inputs(orc, name, rows)
+    assert _layer_equals_staged(orc, orc.layer_block, x, inv, wq, wsc)
+
+
+@pytest.mark.parametrize("mutant", ["s_for_inv_s", "scales_reversed", "tokens_rolled",
+                                    "unsmoothed_codes"])
+def test_layer_block_pin_catches_swapped_arguments(orc, mutant):
+    """A block computed from the wrong arguments (s where 1/s belongs, the
+    weight scales out of order, the token rows shifted, codes folded without
+    s) fails the comparison above."""
+    x, s, inv, wq, wsc = _layer_inputs(orc, "tiny", None)
+    wq_plain, wsc_plain = orc.fold_quant_weights(W.generate(W.WORKLOADS["tiny"]).w,
+                                                 np.ones_like(s))
+
+    def bad(x_, inv_, wq_, wsc_):
+        if mutant == "s_for_inv_s":
+            return orc.layer_block(x_, s, wq_, wsc_)
+        if mutant == "scales_reversed":
+            return orc.layer_block(x_, inv_, wq_, np.ascontiguousarray(wsc_[::-1]))
+        if mutant == "tokens_rolled":
+            return orc.layer_block(np.ascontiguousarray(np.roll(x_, 1, axis=0)), inv_, wq_, wsc_)
+        return orc.layer_block(x_, inv_, wq_plain, wsc_plain)
+    assert not _layer_equals_staged(orc, bad, x, inv, wq, wsc)
+
+
 @pytest.mark.parametrize("name", ["tiny", "qkv4096"])
 def test_unquantized_fp16_rewrite(orc, name):
     """Before quantizing, the smoothed graph in fp16 matches fp64 X W within

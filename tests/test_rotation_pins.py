@@ -165,3 +165,69 @@ def test_eq8_and_eq9_on_a_massive_outlier_token(orc, d):
     got = np.max(np.abs(rot(so)))
     assert got == pytest.approx(eq9_fixed, rel=1e-6)
     assert got == pytest.approx(eq9_printed * np.sqrt(d), rel=1e-6)
+
+
+# ---- the activation step of the four-way comparison ---------------------------------
+#
+# One token worked by hand (d = 16): x = 8 e_0, calibration on the token itself,
+# weight row 0 with maximum 0.5 and every other row zero.  Channels other than
+# 0 have a zero statistic and take s = 1; s_0 = sqrt(8 / 0.5) = 4, so x / s is
+# 2 e_0 exactly.  e_0 H is row 0 of the Sylvester matrix, all ones, so the
+# rotated token is 2 (or 8 without smoothing) in every channel and its maximum
+# is that value; the quantizer's scale is max / 7 in float, and the step in the
+# orthonormal convention R = H / sqrt(d) is scale / 4.
+
+def _hand_case_steps():
+    d = 16
+    x = np.zeros((1, d), np.float16)
+    x[0, 0] = 8.0
+    w = np.zeros((d, 3), np.float16)
+    w[0] = [0.5, -0.25, 0.125]
+    return d, x, w
+
+
+def _hand_case_expected():
+    sev = np.float32(7.0)
+    smooth = float(np.float32(2.0) / sev)       # max of x / s = 2
+    plain = float(np.float32(8.0) / sev)        # max of x = 8
+    return {"original": plain, "smooth": smooth, "rotate": plain / 4.0,
+            "smooth_rotate": smooth / 4.0}
+
+
+def _steps_match_hand_case(q):
+    d, x, w = _hand_case_steps()
+    got = q.w4a4_compare(x, x, w)
+    want = _hand_case_expected()
+    for key, meas in got.items():
+        if meas["act_step"] != want[key.split("/")[0]]:
+            return False
+    return True
+
+
+def test_w4a4_activation_step_hand_case():
+    from oracle import quality as q
+    d, x, w = _hand_case_steps()
+    got = q.w4a4_compare(x, x, w)
+    assert set(k.split("/")[0] for k in got) == set(q.W4A4_METHODS)
+    want = _hand_case_expected()
+    for key, meas in got.items():
+        assert meas["act_step"] == want[key.split("/")[0]], key
+    assert _steps_match_hand_case(q)
+
+
+@pytest.mark.parametrize("mutant", ["divide_by_d", "no_rotation_factor", "always_rotated"])
+def test_w4a4_activation_step_catches_planted_mistakes(monkeypatch, mutant):
+    """The step measure with a plausible mistake planted in the oracle (the
+    printed Eq. (9)'s d instead of sqrt(d); the unnormalized transform's scale
+    taken as the step; every method treated as rotated) fails the hand case."""
+    from oracle import quality as q
+
+    def bad(x_scale, d, rotate):
+        xs = np.asarray(x_scale, np.float64)
+        if mutant == "divide_by_d":
+            return float(np.mean(xs / (d if rotate else 1.0)))
+        if mutant == "no_rotation_factor":
+            return float(np.mean(xs))
+        return float(np.mean(xs / np.sqrt(d)))
+    monkeypatch.setattr(q, "act_step", bad)
+    assert not _steps_match_hand_case(q)
