@@ -305,6 +305,99 @@ def test_binding_refuses_cpu_tensors(sq):
         sq.sq_calibrate_absmax(x.float(), ax)
 
 
+def _cpu_operands(sq, M=4, K=64, N=32):
+    import torch
+    f16, f32, i8 = torch.float16, torch.float32, torch.int8
+    return dict(
+        x=torch.zeros(M, K, dtype=f16), w=torch.zeros(K, N, dtype=f16),
+        vk=torch.zeros(K, dtype=f32), vm=torch.zeros(M, dtype=f32), vn=torch.zeros(N, dtype=f32),
+        xq=torch.zeros(sq.packed_bytes(M, K), dtype=i8),
+        wq=torch.zeros(sq.packed_bytes(N, K), dtype=i8),
+        wq4=torch.zeros(sq.packed4_bytes(N, K), dtype=torch.uint8),
+        y=torch.zeros(M, N, dtype=f16), g=torch.zeros(K, dtype=f16),
+        work=torch.zeros(sq.sq_w4_workspace_bytes(K, N), dtype=torch.uint8), K=K)
+
+
+def _short(t):
+    return t[:-1]
+
+
+# (call, argument that is one entry short); every call is checked for its
+# vectors' sizes before the device, so CPU tensors reach these checks
+SHORT_VECTOR_CASES = [
+    ("calibrate", "act_absmax"), ("fold", "smooth_out"), ("fold", "inv_smooth_out"),
+    ("fold", "w_scale"), ("fold", "act_absmax"), ("fold_in", "smooth_in"),
+    ("quant", "inv_smooth"), ("quant", "x_scale"), ("gemm", "x_scale"), ("gemm", "w_scale"),
+    ("norm_weight", "inv_smooth"), ("norm_weight", "gamma_out"), ("rmsnorm", "gamma_folded"),
+    ("rmsnorm", "x_scale"), ("factors", "act_absmax"), ("factors", "smooth_out"),
+    ("factors", "inv_smooth_out"), ("w4_fold", "smooth"), ("w4_fold", "w_scale"),
+    ("a4_quant", "inv_smooth"), ("a4_quant", "x_scale"), ("w4_gemm", "x_scale"),
+    ("w4_gemm", "w_scale")]
+
+
+def _binding_call(sq, call, o, bad=None):
+    def v(name, t):
+        return _short(t) if name == bad else t
+    K = o["K"]
+    if call == "calibrate":
+        return sq.sq_calibrate_absmax(o["x"], v("act_absmax", o["vk"]))
+    if call == "fold":
+        return sq.sq_smooth_fold_weights(o["w"], v("act_absmax", o["vk"]), 0.5, None,
+                                         v("smooth_out", o["vk"]), v("inv_smooth_out", o["vk"]),
+                                         o["wq"], v("w_scale", o["vn"]))
+    if call == "fold_in":
+        return sq.sq_smooth_fold_weights(o["w"], None, 0.5, v("smooth_in", o["vk"]), o["vk"],
+                                         o["vk"], o["wq"], o["vn"])
+    if call == "quant":
+        return sq.sq_quant_act_per_token(o["x"], v("inv_smooth", o["vk"]), o["xq"],
+                                         v("x_scale", o["vm"]))
+    if call == "gemm":
+        return sq.sq_w8a8_gemm(o["xq"], v("x_scale", o["vm"]), o["wq"], v("w_scale", o["vn"]),
+                               o["y"], K)
+    if call == "norm_weight":
+        return sq.sq_fold_norm_weight(o["g"], v("inv_smooth", o["vk"]), v("gamma_out", o["vk"]))
+    if call == "rmsnorm":
+        return sq.sq_rmsnorm_quant_per_token(o["x"], v("gamma_folded", o["vk"]), 1e-5, o["xq"],
+                                             v("x_scale", o["vm"]))
+    if call == "factors":
+        return sq.sq_smoothing_factors(o["w"], v("act_absmax", o["vk"]), 0.5,
+                                       v("smooth_out", o["vk"]), v("inv_smooth_out", o["vk"]))
+    if call == "w4_fold":
+        return sq.sq_w4_fold_weights(o["w"], v("smooth", o["vk"]), True, o["wq4"],
+                                     v("w_scale", o["vn"]), o["work"])
+    if call == "a4_quant":
+        return sq.sq_a4_quant_per_token(o["x"], v("inv_smooth", o["vk"]), True, o["xq"],
+                                        v("x_scale", o["vm"]))
+    if call == "w4_gemm":
+        return sq.sq_w4_gemm(o["xq"], v("x_scale", o["vm"]), o["wq4"], v("w_scale", o["vn"]),
+                             o["y"], K)
+    raise AssertionError(call)
+
+
+@pytest.mark.parametrize("call,arg", SHORT_VECTOR_CASES)
+def test_binding_rejects_short_vectors(sq, call, arg):
+    """A vector with fewer entries than the kernels index (K, M or N) is
+    refused by the binding before anything reaches the library."""
+    o = _cpu_operands(sq)
+    with pytest.raises(ValueError, match=f"{arg}: expected at least"):
+        _binding_call(sq, call, o, bad=arg)
+
+
+@pytest.mark.parametrize("call", sorted(set(c for c, _ in SHORT_VECTOR_CASES)))
+def test_binding_full_size_cpu_operands_stop_at_the_device_check(sq, call):
+    """With every size right, CPU tensors are refused as not on a GPU (the
+    size checks above run first; there is no CPU path)."""
+    o = _cpu_operands(sq)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        _binding_call(sq, call, o)
+
+
+def test_binding_fp16_product_needs_scales(sq):
+    o = _cpu_operands(sq)
+    with pytest.raises(ValueError, match="x_scale and w_scale"):
+        sq.sq_w8a8_gemm(o["xq"], None, o["wq"], o["vn"], o["y"], o["K"])
+
+
 # ---- packed layout ----------------------------------------------------------------
 
 def test_packed_bytes(sq):

@@ -160,6 +160,17 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _torch_stream(stream, device):
+    """The torch stream object of `stream`: the current stream of `device` for
+    None, a raw hipStream_t handle (int) wrapped as an external stream."""
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if hasattr(stream, "cuda_stream"):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
 def _stream(stream, device) -> int:
     torch = _torch()
     if stream is None:
@@ -167,17 +178,33 @@ def _stream(stream, device) -> int:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _need(t, dtype, name, ndim=None):
-    torch = _torch()
+def _need(t, dtype, name, ndim=None, numel=None):
+    """dtype, rank, a contiguous last dimension and, for vectors, at least
+    `numel` entries (the kernels index them up to that count).  The device is
+    checked afterwards, for all of a call's tensors at once (_on_one_gpu)."""
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
-    if not t.is_cuda:
-        raise ValueError(f"{name}: expected a GPU tensor (there is no CPU path)")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name}: expected {ndim} dims, got {t.dim()}")
     if t.dim() >= 1 and t.stride(-1) != 1 and t.numel() > 1:
         raise ValueError(f"{name}: the last dimension must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: expected at least {numel} entries, got {t.numel()}")
     return t
+
+
+def _on_one_gpu(**tensors):
+    """Every given tensor (None entries skipped) is a GPU tensor, all on one device."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name}: expected a GPU tensor (there is no CPU path)")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name}: on {t.device}, the call's other tensors on {dev}")
 
 
 def _ld(t) -> int:
@@ -185,14 +212,20 @@ def _ld(t) -> int:
 
 
 # ---- the four calls, same names as the C ABI -----------------------------------
+#
+# Each wrapper checks dtypes, ranks and sizes first (every vector needs as many
+# entries as the kernels index), then that all its tensors sit on one GPU, and
+# only then calls the library, which checks the rest (alignment, strides,
+# limits) before it launches anything.
 
 def sq_calibrate_absmax(x_cal, act_absmax, accumulate: bool = False, stream=None) -> None:
     """act_absmax[j] (float32 [K]) := max_t |x_cal[t][j]| (with accumulate: also
     over its previous contents).  x_cal: float16 [T][K]."""
     torch = _torch()
     _need(x_cal, torch.float16, "x_cal", 2)
-    _need(act_absmax, torch.float32, "act_absmax", 1)
     T, K = x_cal.shape
+    _need(act_absmax, torch.float32, "act_absmax", 1, K)
+    _on_one_gpu(x_cal=x_cal, act_absmax=act_absmax)
     _check(lib().sq_calibrate_absmax(_ptr(x_cal), T, K, _ld(x_cal), _ptr(act_absmax),
                                      1 if accumulate else 0, _stream(stream, x_cal.device)),
            "sq_calibrate_absmax")
@@ -215,14 +248,16 @@ def sq_smooth_fold_weights(w, act_absmax, alpha: float, smooth_in, smooth_out, i
     torch = _torch()
     _need(w, torch.float16, "w", 2)
     K, N = w.shape
-    for t, n in ((smooth_out, "smooth_out"), (inv_smooth_out, "inv_smooth_out"),
-                 (w_scale, "w_scale")):
-        _need(t, torch.float32, n, 1)
+    _need(smooth_out, torch.float32, "smooth_out", 1, K)
+    _need(inv_smooth_out, torch.float32, "inv_smooth_out", 1, K)
+    _need(w_scale, torch.float32, "w_scale", 1, N)
     if act_absmax is not None:
-        _need(act_absmax, torch.float32, "act_absmax", 1)
+        _need(act_absmax, torch.float32, "act_absmax", 1, K)
     if smooth_in is not None:
-        _need(smooth_in, torch.float32, "smooth_in", 1)
+        _need(smooth_in, torch.float32, "smooth_in", 1, K)
     _need_packed(wq, N, K, "wq")
+    _on_one_gpu(w=w, act_absmax=act_absmax, smooth_in=smooth_in, smooth_out=smooth_out,
+                inv_smooth_out=inv_smooth_out, wq=wq, w_scale=w_scale)
     _check(lib().sq_smooth_fold_weights(_ptr(w), K, N, _ld(w), _ptr(act_absmax), float(alpha),
                                         _ptr(smooth_in), _ptr(smooth_out), _ptr(inv_smooth_out),
                                         _ptr(wq), _ptr(w_scale), _stream(stream, w.device)),
@@ -234,29 +269,42 @@ def sq_quant_act_per_token(x, inv_smooth, xq, x_scale, stream=None) -> None:
     x (float16 [M][K]) times inv_smooth."""
     torch = _torch()
     _need(x, torch.float16, "x", 2)
-    _need(inv_smooth, torch.float32, "inv_smooth", 1)
-    _need(x_scale, torch.float32, "x_scale", 1)
     M, K = x.shape
+    _need(inv_smooth, torch.float32, "inv_smooth", 1, K)
+    _need(x_scale, torch.float32, "x_scale", 1, M)
     _need_packed(xq, M, K, "xq")
+    _on_one_gpu(x=x, inv_smooth=inv_smooth, xq=xq, x_scale=x_scale)
     _check(lib().sq_quant_act_per_token(_ptr(x), M, K, _ld(x), _ptr(inv_smooth), _ptr(xq),
                                         _ptr(x_scale), _stream(stream, x.device)),
            "sq_quant_act_per_token")
+
+
+def _gemm_operands(xq, x_scale, w_scale, y, out_kind):
+    torch = _torch()
+    if out_kind == SQ_OUT_F16:
+        _need(y, torch.float16, "y", 2)
+        M, N = y.shape
+        if x_scale is None or w_scale is None:
+            raise ValueError("x_scale and w_scale are needed for fp16 output")
+        _need(x_scale, torch.float32, "x_scale", 1, M)
+        _need(w_scale, torch.float32, "w_scale", 1, N)
+    else:
+        _need(y, torch.int32, "y", 2)
+        M, N = y.shape
+        for t, name, n in ((x_scale, "x_scale", M), (w_scale, "w_scale", N)):
+            if t is not None:          # unused by the raw sums, but checked if given
+                _need(t, torch.float32, name, 1, n)
+    return M, N
 
 
 def sq_w8a8_gemm(xq, x_scale, wq, w_scale, y, K: int, out_kind: int = SQ_OUT_F16,
                  stream=None) -> None:
     """y [M][N] (float16, or int32 raw sums) from packed xq (M tokens) and
     packed wq (N channels) of K codes each."""
-    torch = _torch()
-    if out_kind == SQ_OUT_F16:
-        _need(x_scale, torch.float32, "x_scale", 1)
-        _need(w_scale, torch.float32, "w_scale", 1)
-        _need(y, torch.float16, "y", 2)
-    else:
-        _need(y, torch.int32, "y", 2)
-    M, N = y.shape
+    M, N = _gemm_operands(xq, x_scale, w_scale, y, out_kind)
     _need_packed(xq, M, K, "xq")
     _need_packed(wq, N, K, "wq")
+    _on_one_gpu(xq=xq, x_scale=x_scale, wq=wq, w_scale=w_scale, y=y)
     _check(lib().sq_w8a8_gemm(_ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), M, N, int(K),
                               _ptr(y), _ld(y), int(out_kind), _stream(stream, xq.device)),
            "sq_w8a8_gemm")
@@ -267,11 +315,10 @@ def sq_fold_norm_weight(gamma, inv_smooth, gamma_out, stream=None) -> None:
     normalization's weight gamma (float16 [K]) with 1/s folded in."""
     torch = _torch()
     _need(gamma, torch.float16, "gamma", 1)
-    _need(inv_smooth, torch.float32, "inv_smooth", 1)
-    _need(gamma_out, torch.float32, "gamma_out", 1)
     K = gamma.shape[0]
-    if inv_smooth.shape[0] < K or gamma_out.shape[0] < K:
-        raise ValueError("inv_smooth and gamma_out need K entries")
+    _need(inv_smooth, torch.float32, "inv_smooth", 1, K)
+    _need(gamma_out, torch.float32, "gamma_out", 1, K)
+    _on_one_gpu(gamma=gamma, inv_smooth=inv_smooth, gamma_out=gamma_out)
     _check(lib().sq_fold_norm_weight(_ptr(gamma), K, _ptr(inv_smooth), _ptr(gamma_out),
                                      _stream(stream, gamma.device)), "sq_fold_norm_weight")
 
@@ -281,10 +328,11 @@ def sq_rmsnorm_quant_per_token(h, gamma_folded, eps: float, xq, x_scale, stream=
     RMS-normalized hidden state h (float16 [M][K]) with the folded weight."""
     torch = _torch()
     _need(h, torch.float16, "h", 2)
-    _need(gamma_folded, torch.float32, "gamma_folded", 1)
-    _need(x_scale, torch.float32, "x_scale", 1)
     M, K = h.shape
+    _need(gamma_folded, torch.float32, "gamma_folded", 1, K)
+    _need(x_scale, torch.float32, "x_scale", 1, M)
     _need_packed(xq, M, K, "xq")
+    _on_one_gpu(h=h, gamma_folded=gamma_folded, xq=xq, x_scale=x_scale)
     _check(lib().sq_rmsnorm_quant_per_token(_ptr(h), M, K, _ld(h), _ptr(gamma_folded),
                                             float(eps), _ptr(xq), _ptr(x_scale),
                                             _stream(stream, h.device)),
@@ -296,10 +344,12 @@ def sq_smoothing_factors(w, act_absmax, alpha: float, smooth_out, inv_smooth_out
     """s and 1/s (float32 [K]) from the statistics and w (float16 [K][N])."""
     torch = _torch()
     _need(w, torch.float16, "w", 2)
-    _need(act_absmax, torch.float32, "act_absmax", 1)
-    _need(smooth_out, torch.float32, "smooth_out", 1)
-    _need(inv_smooth_out, torch.float32, "inv_smooth_out", 1)
     K, N = w.shape
+    _need(act_absmax, torch.float32, "act_absmax", 1, K)
+    _need(smooth_out, torch.float32, "smooth_out", 1, K)
+    _need(inv_smooth_out, torch.float32, "inv_smooth_out", 1, K)
+    _on_one_gpu(w=w, act_absmax=act_absmax, smooth_out=smooth_out,
+                inv_smooth_out=inv_smooth_out)
     _check(lib().sq_smoothing_factors(_ptr(w), K, N, _ld(w), _ptr(act_absmax), float(alpha),
                                       _ptr(smooth_out), _ptr(inv_smooth_out),
                                       _stream(stream, w.device)), "sq_smoothing_factors")
@@ -323,16 +373,17 @@ def sq_w4_fold_weights(w, smooth, rotate: bool, wq4, w_scale, workspace, stream=
     sq_w4_workspace_bytes(K, N) bytes."""
     torch = _torch()
     _need(w, torch.float16, "w", 2)
-    _need(smooth, torch.float32, "smooth", 1)
-    _need(w_scale, torch.float32, "w_scale", 1)
     K, N = w.shape
+    _need(smooth, torch.float32, "smooth", 1, K)
+    _need(w_scale, torch.float32, "w_scale", 1, N)
     _need_packed4(wq4, N, K, "wq4")
-    wq = wq4
-    if not workspace.is_cuda or workspace.numel() * workspace.element_size() < \
-            sq_w4_workspace_bytes(K, N):
-        raise ValueError("workspace: expected a GPU buffer of sq_w4_workspace_bytes(K, N) bytes")
+    if not workspace.is_contiguous() or \
+            workspace.numel() * workspace.element_size() < sq_w4_workspace_bytes(K, N):
+        raise ValueError("workspace: expected a contiguous buffer of "
+                         "sq_w4_workspace_bytes(K, N) bytes")
+    _on_one_gpu(w=w, smooth=smooth, wq4=wq4, w_scale=w_scale, workspace=workspace)
     _check(lib().sq_w4_fold_weights(_ptr(w), K, N, _ld(w), _ptr(smooth), 1 if rotate else 0,
-                                    _ptr(wq), _ptr(w_scale), _ptr(workspace),
+                                    _ptr(wq4), _ptr(w_scale), _ptr(workspace),
                                     _stream(stream, w.device)), "sq_w4_fold_weights")
 
 
@@ -340,16 +391,10 @@ def sq_w4_gemm(xq, x_scale, wq4, w_scale, y, K: int, out_kind: int = SQ_OUT_F16,
                stream=None) -> None:
     """y [M][N] from packed int8 xq (M tokens) and packed 4-bit wq4 (N
     channels) of K codes each."""
-    torch = _torch()
-    if out_kind == SQ_OUT_F16:
-        _need(x_scale, torch.float32, "x_scale", 1)
-        _need(w_scale, torch.float32, "w_scale", 1)
-        _need(y, torch.float16, "y", 2)
-    else:
-        _need(y, torch.int32, "y", 2)
-    M, N = y.shape
+    M, N = _gemm_operands(xq, x_scale, w_scale, y, out_kind)
     _need_packed(xq, M, K, "xq")
     _need_packed4(wq4, N, K, "wq4")
+    _on_one_gpu(xq=xq, x_scale=x_scale, wq4=wq4, w_scale=w_scale, y=y)
     _check(lib().sq_w4_gemm(_ptr(xq), _ptr(x_scale), _ptr(wq4), _ptr(w_scale), M, N, int(K),
                             _ptr(y), _ld(y), int(out_kind), _stream(stream, xq.device)),
            "sq_w4_gemm")
@@ -360,10 +405,11 @@ def sq_a4_quant_per_token(x, inv_smooth, rotate: bool, xq, x_scale, stream=None)
     x / s with rotate False."""
     torch = _torch()
     _need(x, torch.float16, "x", 2)
-    _need(inv_smooth, torch.float32, "inv_smooth", 1)
-    _need(x_scale, torch.float32, "x_scale", 1)
     M, K = x.shape
+    _need(inv_smooth, torch.float32, "inv_smooth", 1, K)
+    _need(x_scale, torch.float32, "x_scale", 1, M)
     _need_packed(xq, M, K, "xq")
+    _on_one_gpu(x=x, inv_smooth=inv_smooth, xq=xq, x_scale=x_scale)
     _check(lib().sq_a4_quant_per_token(_ptr(x), M, K, _ld(x), _ptr(inv_smooth),
                                        1 if rotate else 0, _ptr(xq), _ptr(x_scale),
                                        _stream(stream, x.device)), "sq_a4_quant_per_token")
@@ -375,6 +421,7 @@ def sq_pack_i8(src, dst, stream=None) -> None:
     _need(src, torch.int8, "src", 2)
     rows, K = src.shape
     _need_packed(dst, rows, K, "dst")
+    _on_one_gpu(src=src, dst=dst)
     _check(lib().sq_pack_i8(_ptr(src), rows, K, _ld(src), _ptr(dst), _stream(stream, src.device)),
            "sq_pack_i8")
 
@@ -385,6 +432,7 @@ def sq_unpack_i8(src, dst, stream=None) -> None:
     _need(dst, torch.int8, "dst", 2)
     rows, K = dst.shape
     _need_packed(src, rows, K, "src")
+    _on_one_gpu(src=src, dst=dst)
     _check(lib().sq_unpack_i8(_ptr(src), rows, K, _ptr(dst), _ld(dst), _stream(stream, dst.device)),
            "sq_unpack_i8")
 
@@ -402,11 +450,22 @@ class Folded:
     N: int = 0
 
 
+def _alloc_stream(stream, device):
+    """Torch stream on which a helper allocates its outputs and temporaries:
+    the stream the library call runs on, so that the caching allocator hands a
+    freed block to later work on that stream only (stream-ordered reuse) and
+    never to another stream while a kernel may still read it."""
+    return _torch_stream(stream, device)
+
+
 def calibrate(x_cal, act_absmax=None, stream=None):
     torch = _torch()
-    out = act_absmax if act_absmax is not None else torch.empty(
-        x_cal.shape[1], dtype=torch.float32, device=x_cal.device)
-    sq_calibrate_absmax(x_cal, out, accumulate=act_absmax is not None, stream=stream)
+    st = _alloc_stream(stream, x_cal.device)
+    out = act_absmax
+    if out is None:
+        with torch.cuda.stream(st):
+            out = torch.empty(x_cal.shape[1], dtype=torch.float32, device=x_cal.device)
+    sq_calibrate_absmax(x_cal, out, accumulate=act_absmax is not None, stream=st)
     return out
 
 
@@ -414,12 +473,14 @@ def fold(w, act_absmax, alpha: float, smooth_in=None, stream=None) -> Folded:
     torch = _torch()
     K, N = w.shape
     dev = w.device
-    f = Folded(torch.empty(K, dtype=torch.float32, device=dev),
-               torch.empty(K, dtype=torch.float32, device=dev),
-               torch.empty(packed_bytes(N, K), dtype=torch.int8, device=dev),
-               torch.empty(N, dtype=torch.float32, device=dev), K, N)
+    st = _alloc_stream(stream, dev)
+    with torch.cuda.stream(st):
+        f = Folded(torch.empty(K, dtype=torch.float32, device=dev),
+                   torch.empty(K, dtype=torch.float32, device=dev),
+                   torch.empty(packed_bytes(N, K), dtype=torch.int8, device=dev),
+                   torch.empty(N, dtype=torch.float32, device=dev), K, N)
     sq_smooth_fold_weights(w, act_absmax, alpha, smooth_in, f.smooth, f.inv_smooth, f.wq,
-                           f.w_scale, stream=stream)
+                           f.w_scale, stream=st)
     return f
 
 
@@ -427,9 +488,11 @@ def quant(x, inv_smooth, stream=None):
     """Returns (packed xq, x_scale)."""
     torch = _torch()
     M, K = x.shape
-    xq = torch.empty(packed_bytes(M, K), dtype=torch.int8, device=x.device)
-    xs = torch.empty(M, dtype=torch.float32, device=x.device)
-    sq_quant_act_per_token(x, inv_smooth, xq, xs, stream=stream)
+    st = _alloc_stream(stream, x.device)
+    with torch.cuda.stream(st):
+        xq = torch.empty(packed_bytes(M, K), dtype=torch.int8, device=x.device)
+        xs = torch.empty(M, dtype=torch.float32, device=x.device)
+    sq_quant_act_per_token(x, inv_smooth, xq, xs, stream=st)
     return xq, xs
 
 
@@ -437,16 +500,20 @@ def gemm(xq, x_scale, wq, w_scale, M: int, N: int, K: int, out_kind: int = SQ_OU
          stream=None):
     torch = _torch()
     dt = torch.float16 if out_kind == SQ_OUT_F16 else torch.int32
-    y = torch.empty((M, N), dtype=dt, device=xq.device)
-    sq_w8a8_gemm(xq, x_scale, wq, w_scale, y, K, out_kind, stream=stream)
+    st = _alloc_stream(stream, xq.device)
+    with torch.cuda.stream(st):
+        y = torch.empty((M, N), dtype=dt, device=xq.device)
+    sq_w8a8_gemm(xq, x_scale, wq, w_scale, y, K, out_kind, stream=st)
     return y
 
 
 def fold_norm_weight(gamma, inv_smooth, stream=None):
     """Returns gamma / s as float32 [K]."""
     torch = _torch()
-    out = torch.empty(gamma.shape[0], dtype=torch.float32, device=gamma.device)
-    sq_fold_norm_weight(gamma, inv_smooth, out, stream=stream)
+    st = _alloc_stream(stream, gamma.device)
+    with torch.cuda.stream(st):
+        out = torch.empty(gamma.shape[0], dtype=torch.float32, device=gamma.device)
+    sq_fold_norm_weight(gamma, inv_smooth, out, stream=st)
     return out
 
 
@@ -454,9 +521,11 @@ def rmsnorm_quant(h, gamma_folded, eps: float, stream=None):
     """Returns (packed xq, x_scale) of the normalized, smoothed hidden state."""
     torch = _torch()
     M, K = h.shape
-    xq = torch.empty(packed_bytes(M, K), dtype=torch.int8, device=h.device)
-    xs = torch.empty(M, dtype=torch.float32, device=h.device)
-    sq_rmsnorm_quant_per_token(h, gamma_folded, eps, xq, xs, stream=stream)
+    st = _alloc_stream(stream, h.device)
+    with torch.cuda.stream(st):
+        xq = torch.empty(packed_bytes(M, K), dtype=torch.int8, device=h.device)
+        xs = torch.empty(M, dtype=torch.float32, device=h.device)
+    sq_rmsnorm_quant_per_token(h, gamma_folded, eps, xq, xs, stream=st)
     return xq, xs
 
 
@@ -464,22 +533,27 @@ def smoothing_factors(w, act_absmax, alpha: float, stream=None):
     """Returns (s, 1/s) as float32 [K]."""
     torch = _torch()
     K = w.shape[0]
-    s = torch.empty(K, dtype=torch.float32, device=w.device)
-    inv = torch.empty(K, dtype=torch.float32, device=w.device)
-    sq_smoothing_factors(w, act_absmax, alpha, s, inv, stream=stream)
+    st = _alloc_stream(stream, w.device)
+    with torch.cuda.stream(st):
+        s = torch.empty(K, dtype=torch.float32, device=w.device)
+        inv = torch.empty(K, dtype=torch.float32, device=w.device)
+    sq_smoothing_factors(w, act_absmax, alpha, s, inv, stream=st)
     return s, inv
 
 
 def fold4(w, smooth, rotate: bool, stream=None):
-    """Returns (packed 4-bit codes of the N output channels (uint8), w_scale)."""
+    """Returns (packed 4-bit codes of the N output channels (uint8), w_scale).
+    The workspace is allocated on the call's stream, so its block is reused
+    only by later work on that stream once the call's kernels are queued."""
     torch = _torch()
     K, N = w.shape
-    wq = torch.empty(packed4_bytes(N, K), dtype=torch.uint8, device=w.device)
-    ws = torch.empty(N, dtype=torch.float32, device=w.device)
-    work = torch.empty(max(16, sq_w4_workspace_bytes(K, N)), dtype=torch.uint8, device=w.device)
-    sq_w4_fold_weights(w, smooth, rotate, wq, ws, work, stream=stream)
-    if hasattr(stream, "cuda_stream"):
-        work.record_stream(stream)      # freed only once that stream is past the call
+    st = _alloc_stream(stream, w.device)
+    with torch.cuda.stream(st):
+        wq = torch.empty(packed4_bytes(N, K), dtype=torch.uint8, device=w.device)
+        ws = torch.empty(N, dtype=torch.float32, device=w.device)
+        work = torch.empty(max(16, sq_w4_workspace_bytes(K, N)), dtype=torch.uint8,
+                           device=w.device)
+    sq_w4_fold_weights(w, smooth, rotate, wq, ws, work, stream=st)
     return wq, ws
 
 
@@ -487,8 +561,10 @@ def gemm4(xq, x_scale, wq4, w_scale, M: int, N: int, K: int, out_kind: int = SQ_
           stream=None):
     torch = _torch()
     dt = torch.float16 if out_kind == SQ_OUT_F16 else torch.int32
-    y = torch.empty((M, N), dtype=dt, device=xq.device)
-    sq_w4_gemm(xq, x_scale, wq4, w_scale, y, K, out_kind, stream=stream)
+    st = _alloc_stream(stream, xq.device)
+    with torch.cuda.stream(st):
+        y = torch.empty((M, N), dtype=dt, device=xq.device)
+    sq_w4_gemm(xq, x_scale, wq4, w_scale, y, K, out_kind, stream=st)
     return y
 
 
@@ -496,28 +572,38 @@ def quant4(x, inv_smooth, rotate: bool, stream=None):
     """Returns (packed 4-bit codes of the M tokens, x_scale)."""
     torch = _torch()
     M, K = x.shape
-    xq = torch.empty(packed_bytes(M, K), dtype=torch.int8, device=x.device)
-    xs = torch.empty(M, dtype=torch.float32, device=x.device)
-    sq_a4_quant_per_token(x, inv_smooth, rotate, xq, xs, stream=stream)
+    st = _alloc_stream(stream, x.device)
+    with torch.cuda.stream(st):
+        xq = torch.empty(packed_bytes(M, K), dtype=torch.int8, device=x.device)
+        xs = torch.empty(M, dtype=torch.float32, device=x.device)
+    sq_a4_quant_per_token(x, inv_smooth, rotate, xq, xs, stream=st)
     return xq, xs
 
 
 def pack_i8(codes, stream=None):
     torch = _torch()
     rows, K = codes.shape
-    dst = torch.empty(packed_bytes(rows, K), dtype=torch.int8, device=codes.device)
-    sq_pack_i8(codes, dst, stream=stream)
+    st = _alloc_stream(stream, codes.device)
+    with torch.cuda.stream(st):
+        dst = torch.empty(packed_bytes(rows, K), dtype=torch.int8, device=codes.device)
+    sq_pack_i8(codes, dst, stream=st)
     return dst
 
 
 def unpack_i8(packed, rows: int, K: int, stream=None):
     torch = _torch()
-    dst = torch.empty((rows, K), dtype=torch.int8, device=packed.device)
-    sq_unpack_i8(packed, dst, stream=stream)
+    st = _alloc_stream(stream, packed.device)
+    with torch.cuda.stream(st):
+        dst = torch.empty((rows, K), dtype=torch.int8, device=packed.device)
+    sq_unpack_i8(packed, dst, stream=st)
     return dst
 
 
 def smoothed_linear(x, folded: Folded, stream=None):
-    """Serving-time layer: per-token quantization of x, then the W8A8 product."""
-    xq, xs = quant(x, folded.inv_smooth, stream=stream)
-    return gemm(xq, xs, folded.wq, folded.w_scale, x.shape[0], folded.N, folded.K, stream=stream)
+    """Serving-time layer: per-token quantization of x, then the W8A8 product.
+    The intermediate codes and scales are allocated on the call's stream and
+    dropped after the product is queued there; the allocator reuses their
+    blocks only for later work on the same stream."""
+    st = _alloc_stream(stream, x.device)
+    xq, xs = quant(x, folded.inv_smooth, stream=st)
+    return gemm(xq, xs, folded.wq, folded.w_scale, x.shape[0], folded.N, folded.K, stream=st)
