@@ -440,6 +440,7 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
             }
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0): this wave's LDS writes done
+        wave_lds_exchange();                          // lanes read what other lanes wrote
         // 32 rows x 16 chunks of 16 bytes, 8 per lane; 4 rows per instruction
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -880,6 +881,7 @@ k_gemm_wide(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
             }
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0): this wave's LDS writes done
+        wave_lds_exchange();                          // lanes read what other lanes wrote
         // 32 rows x 32 chunks of 16 bytes, 16 per lane; 2 rows per instruction
 #pragma unroll
         for (int c = 0; c < 16; ++c) {

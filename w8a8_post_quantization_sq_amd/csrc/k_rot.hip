@@ -187,9 +187,10 @@ k_quant4_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
 // (h = 0..63, j < V/64), the six high index bits in registers for the stages
 // h = V .. K/2.  No butterfly crosses lanes.  The transpose area, 64 rows of
 // 64 floats padded to 68 per wave (writes and reads free of bank conflicts),
-// is the wave's own, so the transpose needs no workgroup barrier; it is reused
-// for the wave's codes, and one barrier before the packed stores (which take
-// all 4 rows) is the only one.
+// is the wave's own, so the transpose needs no workgroup barrier (a wave-level
+// ordering of its lanes' accesses suffices); it is reused for the wave's
+// codes, and one barrier before the packed stores (which take all 4 rows) is
+// the only one.
 constexpr int RT = 4;     // rows per workgroup
 constexpr int TP = 68;    // padded floats per transpose row
 
@@ -257,10 +258,13 @@ k_quant4_rot_t(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx
             *reinterpret_cast<float4 *>(tr + lane * TP + r4) =
                 make_float4(v[64 * j + r4], v[64 * j + r4 + 1], v[64 * j + r4 + 2],
                             v[64 * j + r4 + 3]);
-        // the area is this wave's own and a wave's LDS operations complete in
-        // order, so the reads see the writes without a workgroup barrier
+        // the area is this wave's own: the exchange between its lanes needs
+        // no workgroup barrier, only the ordering of the wave's own accesses
+        wave_lds_exchange();
 #pragma unroll
         for (int h = 0; h < 64; ++h) v[64 * j + h] = tr[h * TP + lane];
+        // the next block's writes (or the codes below) reuse the area
+        wave_lds_exchange();
     }
     // stages h = V .. K/2: the six high index bits, now the register index h
 #pragma unroll

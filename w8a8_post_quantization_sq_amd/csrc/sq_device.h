@@ -31,4 +31,16 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
+// Lanes of one wave exchanging data through LDS: orders this lane's earlier
+// LDS writes before its later reads of what other lanes wrote (and its reads
+// before later writes to the same area).  The hardware keeps a wave's LDS
+// operations in order; the wavefront-scope release/acquire pair around a wave
+// barrier keeps the compiler from moving a lane's access across the exchange,
+// which per-thread alias analysis alone would allow.  No workgroup barrier.
+__device__ __forceinline__ void wave_lds_exchange() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 }  // namespace sq
