@@ -73,12 +73,38 @@ def assert_f16_close(y_gpu, y64_ref):
     return err
 
 
-def sample_rows(M, n, seed):
-    if M <= n:
+def gemm_i32_threads(orc, xq, wq, threads=8):
+    """The oracle's int32 product, its token rows split into blocks that run
+    on host threads (the C call releases the interpreter lock); each block is
+    the oracle's own computation, so the result is the oracle's."""
+    from concurrent.futures import ThreadPoolExecutor
+    M = xq.shape[0]
+    step = max(1, (M + threads - 1) // threads)
+    blocks = [(r, min(M, r + step)) for r in range(0, M, step)]
+    with ThreadPoolExecutor(len(blocks)) as ex:
+        parts = list(ex.map(lambda b: orc.gemm_i32(np.ascontiguousarray(xq[b[0]:b[1]]), wq),
+                            blocks))
+    return np.concatenate(parts, axis=0)
+
+
+def tile_rows(M, tile=256, wave_rows=32, seed=0):
+    """Token rows that touch every tile row of the product's 256-token tiles:
+    the first and last row of each tile (so both sides of every tile boundary,
+    255/256, ..., and M - 1), and one more per tile inside the 32-row slice of
+    wave t % 8 (tile t), at a seeded offset, so that across tiles every wave
+    position of the workgroup is compared.  All N columns of each row are
+    compared, which covers every tile column.  Up to 64 tokens (the decode
+    kernels, no token tiles) every row."""
+    if M <= 64:
         return np.arange(M)
     rng = np.random.default_rng(seed)
-    mid = rng.choice(np.arange(1, M - 1), n - 2, replace=False)
-    return np.sort(np.concatenate([[0, M - 1], mid]))
+    rows = []
+    for t in range((M + tile - 1) // tile):
+        lo, hi = t * tile, min(M, (t + 1) * tile) - 1
+        w = t % (tile // wave_rows)
+        mid = min(hi, lo + w * wave_rows + int(rng.integers(0, wave_rows)))
+        rows += [lo, mid, hi]
+    return np.unique(np.asarray(rows, np.int64))
 
 
 ALL = ["tiny", "qkv4096", "down11008", "decode8192", "prefill8192x3"]
@@ -169,6 +195,35 @@ def test_fold_matches_oracle(sq, dev, orc, name, alpha):
     g = H(f.wq)
     assert np.array_equal(unpack(g, wl.N, wl.K), wq)
     assert padding_is_zero(g, wl.N, wl.K)
+
+
+@pytest.mark.parametrize("alpha", [0.5, 0.25, 0.75, 0.8])
+def test_smoothing_factors_random_statistics(sq, dev, orc, alpha):
+    """s and 1/s for 131056 channels of random positive statistics, bit for bit
+    against the oracle.  The kernel forms s_j in double (square roots at
+    alpha = 1/2, the device's pow otherwise) and the oracle with the host's
+    pow; both are within about one double ulp of the exact value, so the
+    rounded floats agree unless that value lies within ~2^-52 of a float
+    rounding boundary: this sample checks it on many more channels than the
+    workloads have.  ax is a float drawn log-uniformly over [2^-24, 2^16), aw
+    every kind of positive finite fp16 magnitude (subnormals included), held
+    in a one-column W of row stride 8."""
+    import torch
+    K = 131056
+    rng = np.random.default_rng(2000 + int(alpha * 100))
+    ax = np.exp2(rng.uniform(-24.0, 16.0, K)).astype(np.float32)
+    bits = rng.integers(1, 0x7C00, K).astype(np.uint16)          # +subnormal .. 65504
+    sign = rng.integers(0, 2, K).astype(np.uint16) << 15
+    w = np.zeros((K, 8), np.float16)
+    w[:, 0] = (bits | sign).view(np.float16)
+    aw = np.abs(w[:, 0].astype(np.float32))
+    ref_s, ref_inv, st = orc.smoothing_factors(ax, aw, alpha)
+    assert st == 0
+    s_, inv_ = sq.smoothing_factors(T(w, dev)[:, :1], T(ax, dev), alpha)
+    gs, gi = H(s_), H(inv_)
+    nbad = int(np.sum(gs.view(np.uint32) != ref_s.view(np.uint32)))
+    print(f"[factors] alpha={alpha}: {K - nbad}/{K} bit-equal", flush=True)
+    assert bits_equal(gs, ref_s) and bits_equal(gi, ref_inv)
 
 
 def test_fold_given_factors_and_consumer_slices(sq, dev, orc):
@@ -420,29 +475,38 @@ def test_gemm_nan_row_propagates(sq, dev, orc):
 
 # ---- the whole chain ------------------------------------------------------------------------
 
-E2E = [("tiny", 0.5, 16), ("qkv4096", 0.5, 24), ("down11008", 0.5, 16), ("down11008", 0.8, 16),
-       ("decode8192", 0.5, 16), ("prefill8192x3", 0.5, 6)]
+# (workload, alpha, tokens served or None for the workload's own count).  The
+# decode workload is also served at 1 and 4 tokens: its first 1 or 4 tokens
+# against the same 8192 x 28672 folded weights, as the benchmark times them.
+# Rows compared: every row up to 64 tokens; beyond, tile_rows (every 256-token
+# tile row, both sides of every tile boundary, every wave position).
+E2E = [("tiny", 0.5, None), ("qkv4096", 0.5, None), ("down11008", 0.5, None),
+       ("down11008", 0.8, None), ("decode8192", 0.5, 1), ("decode8192", 0.5, 4),
+       ("decode8192", 0.5, None), ("prefill8192x3", 0.5, None)]
 
 
-@pytest.mark.parametrize("name,alpha,nrows", E2E)
-def test_end_to_end(sq, dev, orc, name, alpha, nrows):
+@pytest.mark.parametrize("name,alpha,m", E2E)
+def test_end_to_end(sq, dev, orc, name, alpha, m):
     wl, inp = wl_inputs(name)
-    print(f"[e2e] {name} alpha={alpha} M={wl.M} K={wl.K} N={wl.N}", flush=True)
-    xg = T(inp.x, dev)
+    x = inp.x if m is None else np.ascontiguousarray(inp.x[:m])
+    M = x.shape[0]
+    print(f"[e2e] {name} alpha={alpha} M={M} K={wl.K} N={wl.N}", flush=True)
+    xg = T(x, dev)
     ax = sq.calibrate(T(inp.x_cal, dev))
     f = sq.fold(T(inp.w, dev), ax, alpha)
     xq, xs = sq.quant(xg, f.inv_smooth)
-    y = sq.gemm(xq, xs, f.wq, f.w_scale, wl.M, wl.N, wl.K)
-    acc = sq.gemm(xq, xs, f.wq, f.w_scale, wl.M, wl.N, wl.K, out_kind=sq.SQ_OUT_I32)
-    rows = sample_rows(wl.M, nrows, 17)
-    ref = orc.smoothed_linear(inp.x, inp.x_cal, inp.w, alpha, rows=rows)
+    y = sq.gemm(xq, xs, f.wq, f.w_scale, M, wl.N, wl.K)
+    acc = sq.gemm(xq, xs, f.wq, f.w_scale, M, wl.N, wl.K, out_kind=sq.SQ_OUT_I32)
+    rows = tile_rows(M, seed=17)
+    print(f"[e2e] {name}: comparing {len(rows)} of {M} token rows", flush=True)
+    ref = orc.smoothed_linear(x, inp.x_cal, inp.w, alpha, rows=rows)
     assert ref.status == 0
     assert bits_equal(H(ax), ref.ax)
     assert bits_equal(H(f.smooth), ref.s) and bits_equal(H(f.inv_smooth), ref.inv_s)
     assert bits_equal(H(f.w_scale), ref.w_scale)
     assert np.array_equal(unpack(H(f.wq), wl.N, wl.K), ref.wq)
     assert bits_equal(H(xs), ref.x_scale)
-    assert np.array_equal(unpack(H(xq), wl.M, wl.K), ref.xq)
+    assert np.array_equal(unpack(H(xq), M, wl.K), ref.xq)
     accg = H(acc)[rows]
     assert np.array_equal(accg, ref.acc)
     err = assert_f16_close(H(y)[rows], ref.y64)
@@ -500,6 +564,25 @@ def test_gemm_wide_tile_path_strided_output(sq, dev, orc):
         out = out[off:off + M * ldy].reshape(M, ldy)
         assert np.all(out[:, N:] == 5.0)
         assert_f16_close(out[:, :N], ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(4000, 4040, 1040), (4096, 4096, 2064)])
+def test_gemm_wide_tile_path_deep_k_full_output(sq, dev, orc, M, N, K):
+    """The 256 x 256 tile kernel over more k windows than its 8-deep LDS ring
+    holds (17 and 33 windows, the last one ragged), so the ring wraps and the
+    steady-state waits run: every int32 sum and every fp16 output against
+    the oracle, ragged tiles included (4000 x 4040)."""
+    print(f"[gemm wide] {M}x{N}x{K}", flush=True)
+    xq = W.random_i8(1300 + K, M, K, -128, 127)
+    wq = W.random_i8(1301 + K, N, K, -128, 127)
+    ref = gemm_i32_threads(orc, xq, wq)
+    px, pw = T(pack(xq), dev), T(pack(wq), dev)
+    acc = sq.gemm(px, None, pw, None, M, N, K, out_kind=sq.SQ_OUT_I32)
+    assert np.array_equal(H(acc), ref)
+    xs = W.random_scales(1302, M, 1e-5, 1e-4)
+    ws = W.random_scales(1303, N, 1e-5, 1e-4)
+    y = sq.gemm(px, T(xs, dev), pw, T(ws, dev), M, N, K)
+    assert_f16_close(H(y), orc.dequant(ref, xs, ws))
 
 
 @pytest.mark.parametrize("M,N,ldy,off", [(100, 72, 80, 0), (300, 130, 136, 8), (257, 64, 72, 4)])
