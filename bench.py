@@ -1,32 +1,31 @@
 #!/usr/bin/env python3
 """Benchmark of the SmoothQuant-smoothed W8A8 linear layer on one MI355X.
 
-One step is one pass of every stage of the layer over one batch of synthetic
-input, each through the C ABI on one HIP stream:
-  A1 sq_calibrate_absmax     per-channel max |X| over the 512 calibration tokens
-  A2+A3 sq_smooth_fold_weights  smoothing factors, fold into W, int8 per channel
-  A4 sq_quant_act_per_token  per-token int8 quantization of the batch X
+The timed step is the serving-time layer over one batch of synthetic input:
+  A4 sq_quant_act_per_token  per-token int8 quantization of the batch X (1/s fused)
   A5+A6 sq_w8a8_gemm         int8 matrix-core product + fp16 epilogue
+on weights calibrated, smoothed and folded offline (A1 sq_calibrate_absmax,
+A2+A3 sq_smooth_fold_weights), which run once per weight matrix, not per batch
+("Quantization", learn-kernels.com, para. 2: the transform is applied offline,
+before serving).  The offline rows are timed in the same run: a separate pass
+of every row A1..A6 per step (`full_step`) and a per-stage breakdown.
 The default workload is the LLaMA-7B q/k/v-style layer: X fp16 2048 x 4096
 (1% of channels x U(50, 100)), W fp16 4096 x 4096 ~ N(0, 0.02^2), alpha 0.5,
 calibration on a separate 512-token draw.
 
-Printed: one JSON line with the whole-step throughput (2MNK per step / wall
-time), the product kernel against the int8 matrix-core roofline (its duration
-from HIP events around it on the library's stream, on every 10th timed step),
-the per-stage GPU times from a separate pass with events between the stages,
-the serving-time layer (A4 + A5/A6, the two calls a deployed layer makes per
-batch), and, outside the step: the product at the other large-token
-configurations (down_proj 2048 x 11008 -> 4096, prefill 8192 x 8192 -> 3 x 8192),
-the decode-size layer (M = 1, 4 and 16 tokens
-against an 8192 x 28672 layer, the metric's M <= 16 half, as GB/s of its
-weights), the fused RMS-norm + quantization that replaces A4 when 1/s is
-folded into the normalization in front of the layer, the rotated 4-bit
-quantizer of Smooth Rotation against the unrotated one, the matrix cores'
-and HBM's attainable rates measured on this GPU (a matrix-instruction loop
-with the product's register pattern on the workload's codes, a 1 GiB
-streaming read) beside the published peaks, and the CPU oracle timed on a
-bounded sample as a baseline.
+Printed: one JSON line with the layer throughput (2MNK per step / wall time),
+the product kernel against the int8 matrix-core roofline (its launch duration
+from batches of back-to-back launches between HIP events on the library's
+stream), the GPU's graphics clock sampled during those launches, and, outside
+the step: the product at the other large-token configurations (down_proj
+2048 x 11008 -> 4096, prefill 8192 x 8192 -> 3 x 8192), the decode-size layer
+(M = 1, 4 and 16 tokens against an 8192 x 28672 layer, the metric's M <= 16
+half, as GB/s of its algorithmic bytes and of its weights), the fused RMS-norm
++ quantization that replaces A4 when 1/s is folded into the normalization in
+front of the layer, the rotated 4-bit quantizer of Smooth Rotation against the
+unrotated one, the matrix cores' and HBM's attainable rates measured on this
+GPU beside the published peaks, and the CPU oracle timed on a bounded sample
+on the host's cores as a baseline.
 """
 import argparse
 import hashlib
@@ -79,38 +78,161 @@ def read_traffic(workload):
         return None
 
 
-def cpu_baseline(inp, wl, budget_s):
-    """The CPU oracle, as it stands, on a bounded sample of the same step:
-    A1-A3 in full, then A4-A6 on blocks of 64 tokens until the time budget is
-    spent; the step time is scaled to the whole batch."""
+def host_threads():
+    """Threads for the oracle on this host: the CPUs this process may run on,
+    at most 16 (one GPU's share of a GPU server's host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_layer_sample(inp, wl, budget_s, threads):
+    """The CPU oracle, as it stands, on a bounded sample of one workload: A1-A3
+    once in full (single-threaded C), then the serving-time layer A4-A6
+    (oracle.layer_block, one C call per block of 64 tokens, which releases the
+    interpreter lock) with the blocks spread over `threads` host threads, one
+    round of `threads` blocks at a time, until the batch is done or `budget_s`
+    seconds are spent; the layer time is scaled to the whole batch."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import oracle
+    w = inp.w                     # (the consumers' weights side by side)
     t0 = time.perf_counter()
     ax = oracle.calibrate_absmax(inp.x_cal)
-    s, inv, st = oracle.smoothing_factors(ax, oracle.row_absmax(inp.w), wl.alpha)
-    wq, wsc = oracle.fold_quant_weights(inp.w, s)
+    s, inv, st = oracle.smoothing_factors(ax, oracle.row_absmax(w), wl.alpha)
+    wq, wsc = oracle.fold_quant_weights(w, s)
     t_off = time.perf_counter() - t0
-    rows = 0
+    del w
+    blk = 64
+    starts = list(range(0, wl.M, blk))
+
+    def block(r):
+        oracle.layer_block(np.ascontiguousarray(inp.x[r:r + blk]), inv, wq, wsc)
+        return min(blk, wl.M - r)
+
+    done = 0
     t1 = time.perf_counter()
-    while rows < wl.M:
-        r1 = min(wl.M, rows + 64)
-        oracle.layer_block(np.ascontiguousarray(inp.x[rows:r1]), inv, wq, wsc)
-        rows = r1
-        if time.perf_counter() - t1 > budget_s:
-            break
+    with ThreadPoolExecutor(threads) as ex:
+        for i in range(0, len(starts), threads):
+            done += sum(ex.map(block, starts[i:i + threads]))
+            if time.perf_counter() - t1 > budget_s:
+                break
     t_layer = time.perf_counter() - t1
-    t_step = t_off + t_layer * (wl.M / rows)
+    t_batch = t_layer * (wl.M / done)
     ops = 2.0 * wl.M * wl.N * wl.K
-    return {
-        "value": ops / t_step / 1e12, "unit": "TOP/s", "cores": 1, "kind": "oracle",
-        "sample": (f"single-threaded C oracle: calibration, factors and fold in full "
-                   f"({t_off:.2f} s), quantization + int32 product + dequantization on the "
-                   f"first {rows} of {wl.M} tokens ({t_layer:.2f} s), scaled to the batch: "
-                   f"{t_step:.1f} s per step"),
+    return {"tops": ops / t_batch / 1e12, "tokens": done, "of_tokens": wl.M,
+            "layer_s": round(t_layer, 3), "layer_s_per_batch": round(t_batch, 3),
+            "offline_s": round(t_off, 3)}
+
+
+def cpu_baseline(samples, threads):
+    """The bench line's cpu_baseline object from the per-workload samples
+    (the first one is the step's workload and gives `value`)."""
+    (name, first), rest = samples[0], samples[1:]
+    out = {
+        "value": first["tops"], "unit": "TOP/s", "cores": threads, "kind": "oracle",
+        "cpu_model": cpu_model(),
+        "sample": (f"C oracle on {threads} host threads ({cpu_model()}): calibration, factors and "
+                   f"fold once in full ({first['offline_s']:.2f} s, one thread); quantization + "
+                   f"int32 product + dequantization of {first['tokens']} of {first['of_tokens']} "
+                   f"tokens in blocks of 64 ({first['layer_s']:.2f} s), scaled to the batch: "
+                   f"{first['layer_s_per_batch']:.2f} s per batch of the {name} layer"),
+        "workloads": {n: v for n, v in samples},
     }
+    return out
 
 
-def prefill_leg(torch, workloads, sq, L, dev, stream, hs, launches):
+class ClockSampler:
+    """The GPU's graphics clock, sampled from the driver's metrics table
+    (amdsmi) on a host thread while GPU work runs; reports the median and
+    range of the samples in MHz, or why it could not."""
+
+    def __init__(self, torch, dev, period_s=0.0005):
+        self.samples, self.err, self.h, self.smi = [], None, None, None
+        self.period = period_s
+        self._stop = None
+        self._thr = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            h = handles[0] if len(handles) == 1 else None
+            if h is None:
+                props = torch.cuda.get_device_properties(dev)
+                bus = getattr(props, "pci_bus_id", None)
+                for c in handles:
+                    bdf = str(amdsmi.amdsmi_get_gpu_device_bdf(c)).lower()
+                    if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
+                        h = c
+                if h is None:
+                    raise RuntimeError(f"{len(handles)} GPUs and none matched cuda:0's bus")
+            self.smi, self.h = amdsmi, h
+            self._read()
+        except Exception as e:      # no amdsmi, no metrics table: report why
+            self.err = f"{type(e).__name__}: {e}"
+
+    def _read(self):
+        m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
+        vals = []
+        for key in ("current_gfxclks", "current_gfxclk"):
+            v = m.get(key)
+            for x in (v if isinstance(v, (list, tuple)) else [v]):
+                if isinstance(x, (int, float)) and 0 < x < 10000:
+                    vals.append(float(x))
+            if vals:
+                break
+        if not vals:
+            raise RuntimeError("no graphics clock in the metrics table")
+        return sum(vals) / len(vals)
+
+    def start(self):
+        import threading
+        if self.err:
+            return self
+        self.samples = []
+        self._stop = threading.Event()
+
+        def loop():
+            while not self._stop.is_set():
+                try:
+                    self.samples.append(self._read())
+                except Exception as e:
+                    self.err = f"{type(e).__name__}: {e}"
+                    return
+                time.sleep(self.period)
+        self._thr = threading.Thread(target=loop, daemon=True)
+        self._thr.start()
+        return self
+
+    def stop(self):
+        if self._thr is not None:
+            self._stop.set()
+            self._thr.join()
+            self._thr = None
+        if self.err or not self.samples:
+            return {"mhz": None, "why": self.err or "no samples"}
+        v = sorted(self.samples)
+        return {"mhz": round(v[len(v) // 2], 1), "min": round(v[0], 1), "max": round(v[-1], 1),
+                "samples": len(v),
+                "how": "amdsmi gpu_metrics current graphics clock (mean over XCDs), sampled "
+                       "on a host thread during the launches"}
+
+
+def prefill_leg(torch, workloads, sq, L, dev, stream, hs, launches, clock, hosts):
     """The metric's M >= 2048 half beyond the step's workload: the product at
     the down_proj-style (2048 x 11008 -> 4096, alpha 0.5) and the large-prefill
     (8192 x 8192 -> 3 x 8192, one smoothed X for the three projections)
@@ -118,16 +240,17 @@ def prefill_leg(torch, workloads, sq, L, dev, stream, hs, launches):
     matrix cores' power, and so their clock, depends on the codes), each as
     `launches` launches between one event pair; and the per-token quantizer of
     the same batches, `launches` launches likewise (HBM-bound: 2MK bytes of X,
-    MK of codes, 4M of scales)."""
+    MK of codes, 4M of scales).  The graphics clock is sampled during the
+    product launches; the host inputs are kept in `hosts` for the CPU baseline."""
     out = {"peak": PEAK_INT8_TOPS, "unit": "TOP/s"}
     for name in ("down11008", "prefill8192x3"):
         wl = workloads.WORKLOADS[name]
         inp = workloads.generate(wl)
+        hosts[name] = inp
         M, K, N = wl.M, wl.K, wl.N
         x = torch.from_numpy(inp.x).to(dev)
         xcal = torch.from_numpy(inp.x_cal).to(dev)
         w = torch.from_numpy(inp.w).to(dev)
-        del inp
         ax = torch.empty(K, dtype=torch.float32, device=dev)
         s = torch.empty(K, dtype=torch.float32, device=dev)
         inv = torch.empty(K, dtype=torch.float32, device=dev)
@@ -169,17 +292,25 @@ def prefill_leg(torch, workloads, sq, L, dev, stream, hs, launches):
             if run():
                 raise RuntimeError(f"{name}: product failed")
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        clock.start()
         e0.record(stream)
         for _ in range(launches):
             run()
         e1.record(stream)
         torch.cuda.synchronize()
+        clk = clock.stop()
         us = e0.elapsed_time(e1) * 1e3 / launches
         tops = 2.0 * M * N * K / (us * 1e-6) / 1e12
+        # the layer at this configuration: the quantizer's and the product's
+        # per-launch times added (each measured back to back above)
+        layer_tops = 2.0 * M * N * K / ((us + q_us) * 1e-6) / 1e12
         out[name] = {"M": M, "K": K, "N": N, "us": round(us, 2), "tops": round(tops, 1),
                      "frac": round(tops / PEAK_INT8_TOPS, 4),
                      "quant_us": round(q_us, 2), "quant_gbs": round(q_gbs, 1),
-                     "quant_frac_hbm": round(q_gbs / PEAK_HBM_GBS, 4)}
+                     "quant_frac_hbm": round(q_gbs / PEAK_HBM_GBS, 4),
+                     "layer_tops": round(layer_tops, 1),
+                     "layer_frac": round(layer_tops / PEAK_INT8_TOPS, 4),
+                     "clock": clk}
         log(f"product {name}: {us:.1f} us, {tops:.0f} TOP/s; quantizer {q_us:.1f} us, "
             f"{q_gbs:.0f} GB/s")
         del xq, wq, y
@@ -192,7 +323,8 @@ def decode_leg(torch, workloads, sq, L, dev, stream, hs, launches):
     (940 MB, beyond the 256 MB Infinity Cache) and the copies taken in turn, so
     every product streams its weights from HBM.  Per token count, the product
     alone and quantization + product (M = 1, 4, 16), each as `launches`
-    launches between one event pair; GB/s = the weights' bytes / time."""
+    launches between one event pair; GB/s = the algorithmic bytes (weights,
+    weight scales, X, 1/s, Y) / time, and the weights' bytes alone / time."""
     wl = workloads.WORKLOADS["decode8192"]
     inp = workloads.generate(wl)
     K, N = wl.K, wl.N
@@ -240,7 +372,15 @@ def decode_leg(torch, workloads, sq, L, dev, stream, hs, launches):
             res[with_quant] = e0.elapsed_time(e1) * 1e3 / launches
         gb_layer = N * K / (res[True] * 1e-6) / 1e9
         gb_gemm = N * K / (res[False] * 1e-6) / 1e9
+        # algorithmic bytes of the layer: int8 weights, weight scales, fp16 X
+        # in, 1/s, fp16 Y out (the codes' round trip between the two kernels
+        # is the implementation's cost, charged against the time)
+        alg = K * N + 4 * N + 2 * m * K + 4 * K + 2 * m * N
+        gb_alg = alg / (res[True] * 1e-6) / 1e9
         out[f"M{m}"] = {"layer_us": round(res[True], 2), "gemm_us": round(res[False], 2),
+                        "algorithmic_bytes": alg,
+                        "layer_alg_gbs": round(gb_alg, 1),
+                        "layer_alg_frac": round(gb_alg / PEAK_HBM_GBS, 4),
                         "layer_gbs": round(gb_layer, 1), "gemm_gbs": round(gb_gemm, 1),
                         "layer_frac": round(gb_layer / PEAK_HBM_GBS, 4),
                         "gemm_frac": round(gb_gemm / PEAK_HBM_GBS, 4)}
@@ -343,18 +483,25 @@ def attainable_leg(torch, sq, dev, stream, hs, wq, xq):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--steps", type=int, default=400,
+                    help="timed steps: serving-time layers (quantization + product) back to back")
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="qkv4096",
                     help="qkv4096 | down11008 | prefill8192x3 | tiny")
     ap.add_argument("--alpha", type=float, default=None)
-    ap.add_argument("--event-every", type=int, default=10,
-                    help="bracket the product kernel with HIP events on every n-th timed step")
+    ap.add_argument("--full-steps", type=int, default=50,
+                    help="steps of the separate pass over every row A1..A6 (calibrate, fold, "
+                         "quantize, product) per batch (0: skip)")
     ap.add_argument("--stage-steps", type=int, default=20,
                     help="steps of the separate, untimed pass with an event between stages")
-    ap.add_argument("--layer-launches", type=int, default=100,
-                    help="quant + product pairs of the serving-time layer timed back to back "
-                         "between one event pair (0: take the stage pass's two stages)")
+    ap.add_argument("--product-batches", type=int, default=20,
+                    help="batches of back-to-back product launches, each between one event "
+                         "pair, for the roofline's launch duration and its spread")
+    ap.add_argument("--product-launches", type=int, default=10,
+                    help="product launches per batch")
+    ap.add_argument("--clock-launches", type=int, default=1000,
+                    help="back-to-back product launches during which the graphics clock is "
+                         "sampled (0: skip)")
     ap.add_argument("--norm-launches", type=int, default=100,
                     help="launches of the fused RMS-norm + quantization (and of the plain "
                          "quantizer) timed between one pair of events (0: skip)")
@@ -371,7 +518,8 @@ def main():
                     help="measure the matrix cores' and HBM's attainable rates on this GPU "
                          "(libsq_probe.so) and report them beside the published peaks (0: skip)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
-                    help="seconds of oracle layer work in the CPU baseline (0: skip)")
+                    help="seconds of oracle layer work on the step's workload in the CPU "
+                         "baseline; the other large-token workloads get a quarter each (0: skip)")
     ap.add_argument("--copy-kernel", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 3 plain device copies of MIB MiB "
                          "(the reference for calibrating rocprofv3's FETCH_SIZE/WRITE_SIZE)")
@@ -425,84 +573,124 @@ def main():
                                             wsc=wsc, xq=xq, xsc=xsc, y=y).items()}
     alpha = float(wl.alpha)
 
-    def step(ev=None, gemm_ev=None):
-        # each call goes straight through the C ABI with the tensors' device pointers
-        if ev: ev[0].record(stream)
+    def offline():
+        # A1-A3: calibration statistics, factors, fold (once per weight matrix)
         st = L.sq_calibrate_absmax(p["xcal"], T, K, K, p["ax"], 0, hs)
-        if ev: ev[1].record(stream)
         st |= L.sq_smooth_fold_weights(p["w"], K, N, N, p["ax"], alpha, None, p["s"], p["inv"],
                                        p["wq"], p["wsc"], hs)
-        if ev: ev[2].record(stream)
-        st |= L.sq_quant_act_per_token(p["x"], M, K, K, p["inv"], p["xq"], p["xsc"], hs)
-        if ev: ev[3].record(stream)
-        if gemm_ev: gemm_ev[0].record(stream)
+        if st:
+            raise RuntimeError(f"offline rows failed: status bits {st}")
+
+    def layer():
+        # A4-A6: the serving-time layer, each call straight through the C ABI
+        st = L.sq_quant_act_per_token(p["x"], M, K, K, p["inv"], p["xq"], p["xsc"], hs)
         st |= L.sq_w8a8_gemm(p["xq"], p["xsc"], p["wq"], p["wsc"], M, N, K, p["y"], N,
                              sq.SQ_OUT_F16, hs)
-        if gemm_ev: gemm_ev[1].record(stream)
-        if ev: ev[4].record(stream)
         if st:
-            raise RuntimeError(f"library call failed: status bits {st}")
+            raise RuntimeError(f"layer call failed: status bits {st}")
 
+    def product():
+        if L.sq_w8a8_gemm(p["xq"], p["xsc"], p["wq"], p["wsc"], M, N, K, p["y"], N,
+                          sq.SQ_OUT_F16, hs):
+            raise RuntimeError("product call failed")
+
+    offline()
     for _ in range(args.warmup):
-        step()
+        layer()
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
-    # Timed region: the only events in it bracket the product kernel, on every
-    # --event-every-th step (each event record adds ~3 us of its own to the
-    # device timeline, so bracketing every step would inflate the step time).
-    every = max(1, args.event_every)
-    gemm_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-                   for _ in range(0, args.steps, every)]
+    # Timed region: exactly --steps serving-time layers, nothing else on the
+    # stream, bracketed by device synchronizations.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(gemm_ev=gemm_events[i // every] if i % every == 0 else None)
+    for _ in range(args.steps):
+        layer()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    log(f"timed {args.steps} steps in {wall:.3f} s")
-    gemm_samples = sorted(a.elapsed_time(b) for a, b in gemm_events)
-    gemm_ms = sum(gemm_samples) / len(gemm_samples)
+    log(f"timed {args.steps} layer steps in {wall * 1e3:.3f} ms")
+    ops = 2.0 * M * N * K
+    ms_step = wall * 1e3 / args.steps
+    value = ops * args.steps / wall / 1e12
 
-    def pct(q):
-        return gemm_samples[min(len(gemm_samples) - 1, int(q * len(gemm_samples)))] * 1e3
+    # Every row A1..A6 per step (calibration, factors and fold with its one
+    # host wait, quantization, product), timed the same way.
+    full = None
+    if args.full_steps > 0:
+        for _ in range(5):
+            offline()
+            layer()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.full_steps):
+            offline()
+            layer()
+        torch.cuda.synchronize()
+        fwall = time.perf_counter() - t1
+        full = {"what": "every row per step: calibrate + smooth/fold + per-token quant + W8A8 "
+                        "product (the fold waits once on the host for s)",
+                "steps": args.full_steps, "ms_per_step": round(fwall * 1e3 / args.full_steps, 4),
+                "tops": round(ops * args.full_steps / fwall / 1e12, 2)}
+        log(f"full step (A1..A6): {fwall * 1e3 / args.full_steps:.4f} ms")
 
     # Per-stage breakdown, from a separate pass with an event between stages
-    # (those events lengthen these steps a little; the headline is not taken here).
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
-              for _ in range(args.stage_steps)]
-    for i in range(args.stage_steps):
-        step(ev=events[i])
-    torch.cuda.synchronize()
+    # (those events lengthen these steps a little).
     names = ["calibrate", "fold", "quant", "gemm"]
     per = {n: 0.0 for n in names}
-    for ev in events:
-        for j, n in enumerate(names):
-            per[n] += ev[j].elapsed_time(ev[j + 1])
-    per = {n: v / max(1, args.stage_steps) for n, v in per.items()}    # ms per call
+    if args.stage_steps > 0:
+        for _ in range(args.stage_steps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            ev[0].record(stream)
+            L.sq_calibrate_absmax(p["xcal"], T, K, K, p["ax"], 0, hs)
+            ev[1].record(stream)
+            L.sq_smooth_fold_weights(p["w"], K, N, N, p["ax"], alpha, None, p["s"], p["inv"],
+                                     p["wq"], p["wsc"], hs)
+            ev[2].record(stream)
+            L.sq_quant_act_per_token(p["x"], M, K, K, p["inv"], p["xq"], p["xsc"], hs)
+            ev[3].record(stream)
+            product()
+            ev[4].record(stream)
+            torch.cuda.synchronize()
+            for j, n in enumerate(names):
+                per[n] += ev[j].elapsed_time(ev[j + 1]) / args.stage_steps
 
-    # The serving-time layer as a deployed model runs it (the weights folded
-    # offline): quantization + product, --layer-launches pairs back to back on
-    # the stream between one event pair, on the step's folded weights.
-    layer_ms = per["quant"] + per["gemm"]
-    layer_how = "stage pass (events between the calls)"
-    if args.layer_launches > 0:
-        def layer_pair():
-            st = L.sq_quant_act_per_token(p["x"], M, K, K, p["inv"], p["xq"], p["xsc"], hs)
-            st |= L.sq_w8a8_gemm(p["xq"], p["xsc"], p["wq"], p["wsc"], M, N, K, p["y"], N,
-                                 sq.SQ_OUT_F16, hs)
-            if st:
-                raise RuntimeError("layer launch failed")
-        for _ in range(5):
-            layer_pair()
+    # The product kernel alone for the roofline: --product-batches batches of
+    # --product-launches back-to-back launches, each batch between one event
+    # pair on the library's stream (the events' own device time is spread over
+    # the batch); per-launch duration = batch time / launches.
+    for _ in range(10):
+        product()
+    batch_us = []
+    for _ in range(max(1, args.product_batches)):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(args.layer_launches):
-            layer_pair()
+        for _ in range(max(1, args.product_launches)):
+            product()
         e1.record(stream)
         torch.cuda.synchronize()
-        layer_ms = e0.elapsed_time(e1) / args.layer_launches
-        layer_how = f"{args.layer_launches} quant + product pairs back to back, one event pair"
+        batch_us.append(e0.elapsed_time(e1) * 1e3 / max(1, args.product_launches))
+    batch_us.sort()
+    gemm_us = sum(batch_us) / len(batch_us)
+
+    def pct(q):
+        return batch_us[min(len(batch_us) - 1, int(q * len(batch_us)))]
+
+    # The graphics clock while the product runs back to back.
+    clock = ClockSampler(torch, dev)
+    clk = {"mhz": None, "why": "skipped"}
+    if args.clock_launches > 0:
+        clock.start()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.clock_launches):
+            product()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        clk = clock.stop()
+        clk["launches"] = args.clock_launches
+        clk["product_us"] = round(e0.elapsed_time(e1) * 1e3 / args.clock_launches, 2)
+        log(f"graphics clock during {args.clock_launches} products: {clk.get('mhz')} MHz "
+            f"({clk.get('why', '')}), {clk['product_us']} us per product")
 
     # The normalization in front of the layer with 1/s folded into its weight:
     # the fused RMS-norm + quantization against the plain quantizer on the
@@ -539,6 +727,8 @@ def main():
         norm = {"what": "RMS norm with 1/s folded into its weight, fused with per-token quant "
                         "(sq_rmsnorm_quant_per_token; replaces a separate norm pass)",
                 "us": round(us[True], 3), "plain_quant_us": round(us[False], 3),
+                "plain_quant_gbs": round(nbytes / (us[False] * 1e-6) / 1e9, 1),
+                "plain_quant_frac": round(nbytes / (us[False] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                 "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4),
                 "per_launch": f"2MK (h) + MK (codes) + 4M + 4K = {nbytes} bytes",
@@ -575,19 +765,20 @@ def main():
                "per_launch": f"2MK (x) + MK (codes, one per byte) + 4M + 4K = {nbytes} bytes",
                "transform_flops": int(M * K * (K.bit_length() - 1))}
         log(f"rotated 4-bit quant {us[1]:.2f} us, unrotated {us[0]:.2f} us")
+        # the 8-bit codes again for what follows
+        L.sq_quant_act_per_token(p["x"], M, K, K, p["inv"], p["xq"], p["xsc"], hs)
 
+    hosts = {}
     prefill = None
     if args.prefill_launches > 0:
-        prefill = prefill_leg(torch, workloads, sq, L, dev, stream, hs, args.prefill_launches)
+        prefill = prefill_leg(torch, workloads, sq, L, dev, stream, hs, args.prefill_launches,
+                              clock, hosts)
 
     decode = None
     if args.decode_launches > 0:
         decode = decode_leg(torch, workloads, sq, L, dev, stream, hs, args.decode_launches)
 
-    ops = 2.0 * M * N * K
-    ms_step = wall * 1e3 / args.steps
-    gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
-    layer_tops = ops / (layer_ms * 1e-3) / 1e12 if layer_ms > 0 else 0.0
+    gemm_tops = ops / (gemm_us * 1e-6) / 1e12
     traffic = read_traffic(wl.name)
     # algorithmic HBM bytes of the runtime layer per batch (int8 weights and
     # scales, fp16 X in, 1/s, fp16 Y out)
@@ -595,12 +786,12 @@ def main():
 
     out = {
         "metric": "W8A8 smoothed-linear TOPS (M>=2048) & GB/s (M<=16), % of MI355X roofline",
-        "value": round(ops * args.steps / wall / 1e12, 3),
+        "value": round(value, 3),
         "unit": "TOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -608,20 +799,26 @@ def main():
         "data": "synthetic (seeded, outlier structure of the workload; no trained weights)",
         "config": {"workload": f"{wl.name}: {wl.description}", "M": M, "K": K, "N": N,
                    "alpha": wl.alpha, "calibration_tokens": T, "seed": wl.seed,
-                   "step": "calibrate + smooth/fold + per-token quant + W8A8 GEMM"},
+                   "step": "serving-time layer: per-token quant (1/s fused) + W8A8 product, on "
+                           "weights calibrated and folded offline"},
+        "layer": {"what": "the step: sq_quant_act_per_token + sq_w8a8_gemm",
+                  "us": round(ms_step * 1e3, 2), "tops": round(value, 2),
+                  "frac_int8_peak": round(value / PEAK_INT8_TOPS, 4),
+                  "hbm_gbs_algorithmic": round(layer_bytes / (ms_step * 1e-3) / 1e9, 1)},
+        "full_step": full,
         "stage_ms": {n: round(v, 4) for n, v in per.items()},
-        "layer": {"what": "serving-time layer: per-token quant + W8A8 GEMM (weights folded offline)",
-                  "how": layer_how, "ms": round(layer_ms, 4), "tops": round(layer_tops, 2),
-                  "frac_int8_peak": round(layer_tops / PEAK_INT8_TOPS, 4),
-                  "hbm_gbs_algorithmic": round(layer_bytes / (layer_ms * 1e-3) / 1e9, 1)
-                  if layer_ms > 0 else 0.0},
         "roofline": {"kernel": "k_gemm_w8a8 (sq_w8a8_gemm)", "bound": "mfma",
                      "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                      "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": traffic,
-                     "launch_us": {"mean": round(gemm_ms * 1e3, 2), "p10": round(pct(0.1), 2),
+                     "launch_us": {"mean": round(gemm_us, 2), "p10": round(pct(0.1), 2),
                                    "p50": round(pct(0.5), 2), "p90": round(pct(0.9), 2),
-                                   "samples": len(gemm_samples)},
-                     "per_launch": f"2*M*N*K = {ops:.4g} int8 ops per launch"},
+                                   "batches": len(batch_us),
+                                   "launches": len(batch_us) * max(1, args.product_launches),
+                                   "how": "per-launch average of each batch of back-to-back "
+                                          "launches between one HIP event pair; percentiles "
+                                          "over the batches"},
+                     "per_launch": f"2*M*N*K = {ops:.4g} int8 ops per launch",
+                     "clock": clk},
         "prefill": prefill,
         "decode": decode,
         "norm_fold": norm,
@@ -633,12 +830,19 @@ def main():
         att["product_frac_of_mfma"] = round(gemm_tops / att["mfma_int8_tops"], 4)
         if decode:
             att["decode_layer_frac_of_read"] = {
-                k: round(v["layer_gbs"] / att["hbm_read_gbs"], 4)
+                k: round(v["layer_alg_gbs"] / att["hbm_read_gbs"], 4)
                 for k, v in decode.items() if k in ("M1", "M4", "M16")}
         out["attainable"] = att
     if args.cpu_budget > 0:
-        log("timing the CPU oracle baseline")
-        out["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_budget)
+        threads = host_threads()
+        log(f"timing the CPU oracle baseline on {threads} threads")
+        samples = [(wl.name, cpu_layer_sample(inp, wl, args.cpu_budget, threads))]
+        for name in ("down11008", "prefill8192x3"):
+            if name in hosts and name != wl.name:
+                samples.append((name, cpu_layer_sample(hosts[name], workloads.WORKLOADS[name],
+                                                       args.cpu_budget / 4, threads)))
+                log(f"CPU oracle {name}: {samples[-1][1]['tops']:.4f} TOP/s")
+        out["cpu_baseline"] = cpu_baseline(samples, threads)
     print(json.dumps(out), flush=True)
 
 
