@@ -165,6 +165,30 @@ sq_status sq_smooth_fold_weights(const void *w_f16, int64_t K, int64_t N, int64_
                                  float *smooth_out, float *inv_smooth_out,
                                  int8_t *wq, float *w_scale, void *stream);
 
+/* Largest N that sq_smooth_fold_weights_noalloc takes: its column maxima live
+ * in a fixed device array of SQ_NOALLOC_MAX_N floats (512 KiB) per GPU. */
+#define SQ_NOALLOC_MAX_N 131072
+
+/*
+ * sq_smooth_fold_weights for callers that cannot allocate device or pinned
+ * host memory (code under stream capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, outputs, argument checks and data
+ * errors as sq_smooth_fold_weights; additionally SQ_ERR_SHAPE when
+ * N > SQ_NOALLOC_MAX_N (nothing is launched).  The call allocates nothing:
+ * the column maxima and a status word live in a file-scope device array of
+ * the library (one per GPU, held until the process ends, its address looked
+ * up once per device), the factors are checked on the device, and the call
+ * copies 4 bytes of status to the host and waits for the whole stream before
+ * it returns.  Every call on one GPU shares that array: calls that overlap on
+ * one GPU (other threads or streams) race and must be serialized by the
+ * caller.
+ */
+sq_status sq_smooth_fold_weights_noalloc(const void *w_f16, int64_t K, int64_t N, int64_t ldw,
+                                         const float *act_absmax, float alpha,
+                                         const float *smooth_in, float *smooth_out,
+                                         float *inv_smooth_out, int8_t *wq, float *w_scale,
+                                         void *stream);
+
 /*
  * The smoothing factors alone, without the 8-bit fold: s and 1/s exactly as
  * sq_smooth_fold_weights computes them (same formula, same checks, same

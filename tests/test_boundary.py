@@ -121,6 +121,34 @@ def test_fold_rejects(sq, kw, expect):
     assert sq.status_str(_fold(sq, **kw)).startswith(expect)
 
 
+def _fold_noalloc(sq, w=P, K=64, N=32, ldw=32, ax=P, alpha=0.5, sin=None, s=P, inv=P, wq=P,
+                  ws=P):
+    return sq.lib().sq_smooth_fold_weights_noalloc(w, K, N, ldw, ax, alpha, sin, s, inv, wq, ws,
+                                                   None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(s=None), "SQ_ERR_NULL"),
+    (dict(ax=None), "SQ_ERR_NULL"),
+    (dict(wq=None), "SQ_ERR_NULL"),
+    (dict(K=72), "SQ_ERR_SHAPE"),
+    (dict(ldw=16), "SQ_ERR_SHAPE"),
+    (dict(N=131073, ldw=131080), "SQ_ERR_SHAPE"),    # N > SQ_NOALLOC_MAX_N
+    (dict(w=MIS), "SQ_ERR_ALIGN"),
+    (dict(ldw=36), "SQ_ERR_ALIGN"),
+    (dict(alpha=1.5), "SQ_ERR_ALPHA"),
+])
+def test_fold_noalloc_rejects(sq, kw, expect):
+    """The allocation-free fold checks its arguments like the fold, and a
+    width beyond its fixed scratch, before any HIP call."""
+    assert sq.status_str(_fold_noalloc(sq, **kw)).startswith(expect)
+
+
+def test_noalloc_limit_matches_binding(sq):
+    text = open(HEADER).read()
+    assert int(re.search(r"#define SQ_NOALLOC_MAX_N (\d+)", text).group(1)) == sq.SQ_NOALLOC_MAX_N
+
+
 # ---- quant ------------------------------------------------------------------------
 
 @pytest.mark.parametrize("args,expect", [

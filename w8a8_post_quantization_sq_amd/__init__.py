@@ -7,7 +7,8 @@ library's gfx950 kernels.  There is no CPU fallback: without the built
 library, or without a GPU, the calls raise.
 
 Same-name calls (caller-allocated outputs, as in the C ABI):
-    sq_calibrate_absmax, sq_smooth_fold_weights, sq_quant_act_per_token,
+    sq_calibrate_absmax, sq_smooth_fold_weights, sq_smooth_fold_weights_noalloc,
+    sq_quant_act_per_token,
     sq_w8a8_gemm, sq_packed_bytes, sq_pack_i8, sq_unpack_i8,
     sq_fold_norm_weight, sq_rmsnorm_quant_per_token, sq_smoothing_factors,
     sq_w4_workspace_bytes, sq_w4_fold_weights, sq_a4_quant_per_token,
@@ -30,6 +31,7 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsq.so")
 
+SQ_NOALLOC_MAX_N = 131072
 SQ_OK = 0
 SQ_ERR_NULL = 1
 SQ_ERR_SHAPE = 2
@@ -48,7 +50,8 @@ EXPORTS = ("sq_status_str", "sq_version", "sq_packed_bytes", "sq_calibrate_absma
            "sq_smooth_fold_weights", "sq_quant_act_per_token", "sq_w8a8_gemm", "sq_pack_i8",
            "sq_unpack_i8", "sq_fold_norm_weight", "sq_rmsnorm_quant_per_token",
            "sq_smoothing_factors", "sq_w4_workspace_bytes", "sq_w4_fold_weights",
-           "sq_a4_quant_per_token", "sq_packed4_bytes", "sq_w4_gemm")
+           "sq_a4_quant_per_token", "sq_packed4_bytes", "sq_w4_gemm",
+           "sq_smooth_fold_weights_noalloc")
 
 _LIB = None
 
@@ -77,6 +80,9 @@ def lib() -> ctypes.CDLL:
         L.sq_calibrate_absmax.argtypes = [vp, i64, i64, i64, vp, ci, vp]
         L.sq_smooth_fold_weights.restype = ci
         L.sq_smooth_fold_weights.argtypes = [vp, i64, i64, i64, vp, f32, vp, vp, vp, vp, vp, vp]
+        L.sq_smooth_fold_weights_noalloc.restype = ci
+        L.sq_smooth_fold_weights_noalloc.argtypes = [vp, i64, i64, i64, vp, f32, vp, vp, vp, vp,
+                                                     vp, vp]
         L.sq_quant_act_per_token.restype = ci
         L.sq_quant_act_per_token.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
         L.sq_w8a8_gemm.restype = ci
@@ -262,6 +268,29 @@ def sq_smooth_fold_weights(w, act_absmax, alpha: float, smooth_in, smooth_out, i
                                         _ptr(smooth_in), _ptr(smooth_out), _ptr(inv_smooth_out),
                                         _ptr(wq), _ptr(w_scale), _stream(stream, w.device)),
            "sq_smooth_fold_weights")
+
+
+def sq_smooth_fold_weights_noalloc(w, act_absmax, alpha: float, smooth_in, smooth_out,
+                                   inv_smooth_out, wq, w_scale, stream=None) -> None:
+    """sq_smooth_fold_weights without any allocation in the library (scratch in
+    its static per-device array; N <= SQ_NOALLOC_MAX_N); same arguments."""
+    torch = _torch()
+    _need(w, torch.float16, "w", 2)
+    K, N = w.shape
+    _need(smooth_out, torch.float32, "smooth_out", 1, K)
+    _need(inv_smooth_out, torch.float32, "inv_smooth_out", 1, K)
+    _need(w_scale, torch.float32, "w_scale", 1, N)
+    if act_absmax is not None:
+        _need(act_absmax, torch.float32, "act_absmax", 1, K)
+    if smooth_in is not None:
+        _need(smooth_in, torch.float32, "smooth_in", 1, K)
+    _need_packed(wq, N, K, "wq")
+    _on_one_gpu(w=w, act_absmax=act_absmax, smooth_in=smooth_in, smooth_out=smooth_out,
+                inv_smooth_out=inv_smooth_out, wq=wq, w_scale=w_scale)
+    _check(lib().sq_smooth_fold_weights_noalloc(
+        _ptr(w), K, N, _ld(w), _ptr(act_absmax), float(alpha), _ptr(smooth_in), _ptr(smooth_out),
+        _ptr(inv_smooth_out), _ptr(wq), _ptr(w_scale), _stream(stream, w.device)),
+        "sq_smooth_fold_weights_noalloc")
 
 
 def sq_quant_act_per_token(x, inv_smooth, xq, x_scale, stream=None) -> None:

@@ -20,6 +20,10 @@
 //                     w_scale[n] = amax_n / 127
 #include <math.h>
 
+#include <mutex>
+#include <vector>
+
+#include "sq.h"
 #include "sq_device.h"
 
 namespace sq {
@@ -56,7 +60,7 @@ __global__ void __launch_bounds__(64)
 k_row_smooth(const uint16_t *__restrict__ w, int64_t K, int64_t N, int64_t ldw,
              const float *__restrict__ ax, const float *__restrict__ smooth_in, double alpha,
              float *__restrict__ s_out, float *__restrict__ inv_out, float *__restrict__ s_host,
-             float *__restrict__ amax) {
+             float *__restrict__ amax, uint32_t *__restrict__ status) {
     if (amax)   // (the factors alone need no column maxima)
         for (int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x; i < N; i += (int64_t)gridDim.x * 64)
             amax[i] = 0.0f;
@@ -128,16 +132,27 @@ k_row_smooth(const uint16_t *__restrict__ w, int64_t K, int64_t N, int64_t ldw,
         else
             s = (float)(pow_ratio(a, aw, alpha));
     }
+    const float inv = 1.0f / s;   // IEEE-correct float division
     s_out[j] = s;
-    inv_out[j] = 1.0f / s;   // IEEE-correct float division
+    inv_out[j] = inv;
     if (s_host) s_host[j] = s;   // for the host's check, without a copy kernel
+    if (status) {
+        // the same check on the device: bit 0 a NaN factor (a bad statistic
+        // or given factor), bit 1 a factor or reciprocal that is zero,
+        // infinite, subnormal or negative
+        const uint32_t bad = __builtin_isnan(s) ? 1u
+                             : (!__builtin_isnormal(s) || !__builtin_isnormal(inv) || s < 0.0f) ? 2u
+                                                                                                : 0u;
+        if (bad) atomicOr(status, bad);
+    }
 }
 
 hipError_t launch_row_smooth(const uint16_t *w, int64_t K, int64_t N, int64_t ldw,
                              const float *ax, const float *smooth_in, float alpha, float *s_out,
-                             float *inv_out, float *s_host, float *amax, hipStream_t st) {
+                             float *inv_out, float *s_host, float *amax, uint32_t *status,
+                             hipStream_t st) {
     k_row_smooth<<<dim3((unsigned)((K + RS_ROWS - 1) / RS_ROWS)), dim3(64), 0, st>>>(
-        w, K, N, ldw, ax, smooth_in, (double)alpha, s_out, inv_out, s_host, amax);
+        w, K, N, ldw, ax, smooth_in, (double)alpha, s_out, inv_out, s_host, amax, status);
     return hipGetLastError();
 }
 
@@ -351,6 +366,44 @@ hipError_t launch_fold_quant(const uint16_t *w, int64_t K, int64_t N, int64_t ld
     const dim3 grid((unsigned)((N + FQ_TN - 1) / FQ_TN), (unsigned)((K + FQ_TK - 1) / FQ_TK));
     k_fold_quant<<<grid, dim3(256), 0, st>>>(w, K, N, ldw, s, amax, wq, w_scale);
     return hipGetLastError();
+}
+
+// ---- the fold's scratch for callers that cannot allocate ------------------------------
+//
+// sq_smooth_fold_weights_noalloc takes its column maxima (N floats) and its
+// status word from this file-scope device array instead of the per-(thread,
+// device) buffers the allocating fold makes.  Each GPU holds its own copy
+// from the library's load until the process ends.  In host code `scratch` is
+// only a stand-in for the symbol: its device address on a device comes from
+// hipGetSymbolAddress with that device current, once per device, and only
+// that address is ever passed to kernels or copies.
+constexpr int64_t NOALLOC_WORDS = (int64_t)SQ_NOALLOC_MAX_N + 64;   // maxima, then the status
+static __device__ __align__(256) uint32_t scratch[NOALLOC_WORDS];
+
+hipError_t noalloc_scratch(int dev, float **amax, uint32_t **status) {
+    static std::mutex mu;
+    static std::vector<void *> addr;     // per device, found once
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev < 0) return hipErrorInvalidDevice;
+    if ((int)addr.size() <= dev) addr.resize((size_t)dev + 1, nullptr);
+    if (!addr[(size_t)dev]) {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[(size_t)dev] = p;
+    }
+    *amax = static_cast<float *>(addr[(size_t)dev]);
+    *status = static_cast<uint32_t *>(addr[(size_t)dev]) + SQ_NOALLOC_MAX_N;
+    return hipSuccess;
 }
 
 }  // namespace sq

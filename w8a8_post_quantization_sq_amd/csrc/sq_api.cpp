@@ -4,7 +4,9 @@
 // work is the fold's check of the smoothing factors it has just computed,
 // which overlaps the rest of the fold on the device.  The fold keeps a little
 // state per (thread, device): a host buffer for the factors and a device
-// scratch for the column maxima.
+// scratch for the column maxima.  Its allocation-free variant uses the
+// library's static per-device array instead and checks the factors on the
+// device.
 #include <math.h>
 #include <stdint.h>
 
@@ -162,11 +164,11 @@ SQ_API sq_status sq_calibrate_absmax(const void *x_cal_f16, int64_t T, int64_t K
                                               act_absmax, accumulate != 0, as_stream(stream)));
 }
 
-SQ_API sq_status sq_smooth_fold_weights(const void *w_f16, int64_t K, int64_t N, int64_t ldw,
-                                        const float *act_absmax, float alpha,
-                                        const float *smooth_in, float *smooth_out,
-                                        float *inv_smooth_out, int8_t *wq, float *w_scale,
-                                        void *stream) {
+// The fold's argument checks, shared by both fold entry points.
+static sq_status fold_args(const void *w_f16, int64_t K, int64_t N, int64_t ldw,
+                           const float *act_absmax, float alpha, const float *smooth_in,
+                           const float *smooth_out, const float *inv_smooth_out, const int8_t *wq,
+                           const float *w_scale) {
     if (!smooth_out || !inv_smooth_out || (!smooth_in && !act_absmax)) return SQ_ERR_NULL;
     if (N > 0 && (!w_f16 || !wq || !w_scale)) return SQ_ERR_NULL;
     if (N < 0 || N >= kMaxDim || !k_ok(K) || (N > 0 && ldw < N)) return SQ_ERR_SHAPE;
@@ -176,6 +178,17 @@ SQ_API sq_status sq_smooth_fold_weights(const void *w_f16, int64_t K, int64_t N,
     if (N > 0 && (!aligned16(w_f16) || !aligned16(wq) || !aligned16(w_scale) || (ldw % 8) != 0))
         return SQ_ERR_ALIGN;
     if (!smooth_in && !(alpha >= 0.0f && alpha <= 1.0f)) return SQ_ERR_ALPHA;
+    return SQ_OK;
+}
+
+SQ_API sq_status sq_smooth_fold_weights(const void *w_f16, int64_t K, int64_t N, int64_t ldw,
+                                        const float *act_absmax, float alpha,
+                                        const float *smooth_in, float *smooth_out,
+                                        float *inv_smooth_out, int8_t *wq, float *w_scale,
+                                        void *stream) {
+    const sq_status a = fold_args(w_f16, K, N, ldw, act_absmax, alpha, smooth_in, smooth_out,
+                                  inv_smooth_out, wq, w_scale);
+    if (a != SQ_OK) return a;
 
     const hipStream_t st = as_stream(stream);
     const uint16_t *w = static_cast<const uint16_t *>(w_f16);
@@ -187,7 +200,7 @@ SQ_API sq_status sq_smooth_fold_weights(const void *w_f16, int64_t K, int64_t N,
     // on the stream while the host waits for it.  With N == 0 no row is read
     // (aw = 0).
     e = sq::launch_row_smooth(w, K, N, ldw, act_absmax, smooth_in, alpha, smooth_out,
-                              inv_smooth_out, g->host_dev, g->amax, st);
+                              inv_smooth_out, g->host_dev, g->amax, nullptr, st);
     if (e == hipSuccess) e = hipEventRecord(g->ready, st);
     if (e != hipSuccess) return SQ_ERR_HIP;
     if (N > 0) {
@@ -201,6 +214,51 @@ SQ_API sq_status sq_smooth_fold_weights(const void *w_f16, int64_t K, int64_t N,
     if (e != hipSuccess || ew != hipSuccess) return SQ_ERR_HIP;
 
     return check_factors(g->host, K);
+}
+
+// The same fold without allocating: column maxima and the factors' status in
+// the library's per-device scratch array, the check of the factors done on
+// the device, one 4-byte copy of the status to the host and one wait for the
+// stream at the end.  No hipMalloc, hipHostMalloc, hipFree or event.
+SQ_API sq_status sq_smooth_fold_weights_noalloc(const void *w_f16, int64_t K, int64_t N,
+                                                int64_t ldw, const float *act_absmax, float alpha,
+                                                const float *smooth_in, float *smooth_out,
+                                                float *inv_smooth_out, int8_t *wq,
+                                                float *w_scale, void *stream) {
+    const sq_status a = fold_args(w_f16, K, N, ldw, act_absmax, alpha, smooth_in, smooth_out,
+                                  inv_smooth_out, wq, w_scale);
+    if (a != SQ_OK) return a;
+    if (N > SQ_NOALLOC_MAX_N) return SQ_ERR_SHAPE;
+
+    const hipStream_t st = as_stream(stream);
+    int dev = 0;
+    hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+    float *amax = nullptr;
+    uint32_t *status = nullptr;
+    if (e == hipSuccess) e = sq::noalloc_scratch(dev, &amax, &status);
+    if (e != hipSuccess) return SQ_ERR_HIP;
+    const uint16_t *w = static_cast<const uint16_t *>(w_f16);
+    // the status word keeps the previous call's value: clear it (a fill
+    // kernel; the factor kernel clears the column maxima itself)
+    e = sq::launch_fill_f32(reinterpret_cast<float *>(status), 1, 0.0f, st);
+    if (e == hipSuccess)
+        e = sq::launch_row_smooth(w, K, N, ldw, act_absmax, smooth_in, alpha, smooth_out,
+                                  inv_smooth_out, nullptr, amax, status, st);
+    uint32_t host_status = 0;
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(&host_status, status, sizeof(host_status), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess && N > 0) {
+        e = sq::launch_fold_colabsmax(w, K, N, ldw, smooth_out, amax, st);
+        if (e == hipSuccess)
+            e = sq::launch_fold_quant(w, K, N, ldw, smooth_out, amax, wq, w_scale, st);
+    }
+    // wait for the status copy (and the rest of the fold) even after a failed
+    // launch, so host_status is never written after this frame is gone
+    const hipError_t ew = hipStreamSynchronize(st);
+    if (e != hipSuccess || ew != hipSuccess) return SQ_ERR_HIP;
+    if (host_status & 1u) return SQ_ERR_NONFINITE;
+    if (host_status & 2u) return SQ_ERR_RANGE;
+    return SQ_OK;
 }
 
 SQ_API sq_status sq_smoothing_factors(const void *w_f16, int64_t K, int64_t N, int64_t ldw,
@@ -217,7 +275,7 @@ SQ_API sq_status sq_smoothing_factors(const void *w_f16, int64_t K, int64_t N, i
     if (staging_for(st, K, 0, &g) != hipSuccess) return SQ_ERR_HIP;
     hipError_t e = sq::launch_row_smooth(static_cast<const uint16_t *>(w_f16), K, N, ldw,
                                          act_absmax, nullptr, alpha, smooth_out, inv_smooth_out,
-                                         g->host_dev, nullptr, st);
+                                         g->host_dev, nullptr, nullptr, st);
     if (e == hipSuccess) e = hipEventRecord(g->ready, st);
     g->last = st;
     g->used = true;

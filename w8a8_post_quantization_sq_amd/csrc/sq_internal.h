@@ -16,10 +16,16 @@ hipError_t launch_calib_absmax(const uint16_t *x, int64_t T, int64_t K, int64_t 
 
 // aw_j = max_n |W[j][n]| -> s_out[j] = s_j (also into s_host when not NULL,
 // a device-visible host buffer), inv_out[j] = 1/s_j; zeroes amax[0, N) when
-// amax is not NULL
+// amax is not NULL; when status is not NULL, ORs into it 1 for a NaN factor
+// and 2 for a factor or reciprocal that is not a positive normal float
 hipError_t launch_row_smooth(const uint16_t *w, int64_t K, int64_t N, int64_t ldw,
                              const float *ax, const float *smooth_in, float alpha, float *s_out,
-                             float *inv_out, float *s_host, float *amax, hipStream_t st);
+                             float *inv_out, float *s_host, float *amax, uint32_t *status,
+                             hipStream_t st);
+
+// device addresses, on device `dev`, of the allocation-free fold's scratch:
+// SQ_NOALLOC_MAX_N floats of column maxima and one status word
+hipError_t noalloc_scratch(int dev, float **amax, uint32_t **status);
 
 // amax[n] = max(amax[n], max_j |float(W[j][n]) * s_j|)
 hipError_t launch_fold_colabsmax(const uint16_t *w, int64_t K, int64_t N, int64_t ldw,
