@@ -16,7 +16,8 @@ calibration on a separate 512-token draw.
 Printed: one JSON line with the layer throughput (2MNK per step / wall time),
 the product kernel against the int8 matrix-core roofline (its launch duration
 from batches of back-to-back launches between HIP events on the library's
-stream), the GPU's graphics clock sampled during those launches, and, outside
+stream), the shader clock measured on the GPU during a run of those launches,
+and, outside
 the step: the product at the other large-token configurations (down_proj
 2048 x 11008 -> 4096, prefill 8192 x 8192 -> 3 x 8192), the decode-size layer
 (M = 1, 4 and 16 tokens against an 8192 x 28672 layer, the metric's M <= 16
@@ -156,80 +157,42 @@ def cpu_baseline(samples, threads):
     return out
 
 
-class ClockSampler:
-    """The GPU's graphics clock, sampled from the driver's metrics table
-    (amdsmi) on a host thread while GPU work runs; reports the median and
-    range of the samples in MHz, or why it could not."""
+class ClockWatch:
+    """The shader clock while GPU work runs, measured on the GPU itself: a
+    one-wave probe kernel (libsq_probe.so, sqp_clock_watch) queued on a second
+    stream just before the work reads the shader cycle counter and the
+    constant-rate real-time counter across a span of real time shorter than
+    the work, on one CU that the work's kernels share."""
 
-    def __init__(self, torch, dev, period_s=0.0005):
-        self.samples, self.err, self.h, self.smi = [], None, None, None
-        self.period = period_s
-        self._stop = None
-        self._thr = None
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            handles = amdsmi.amdsmi_get_processor_handles()
-            h = handles[0] if len(handles) == 1 else None
-            if h is None:
-                props = torch.cuda.get_device_properties(dev)
-                bus = getattr(props, "pci_bus_id", None)
-                for c in handles:
-                    bdf = str(amdsmi.amdsmi_get_gpu_device_bdf(c)).lower()
-                    if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
-                        h = c
-                if h is None:
-                    raise RuntimeError(f"{len(handles)} GPUs and none matched cuda:0's bus")
-            self.smi, self.h = amdsmi, h
-            self._read()
-        except Exception as e:      # no amdsmi, no metrics table: report why
-            self.err = f"{type(e).__name__}: {e}"
+    def __init__(self, torch, sq, dev):
+        import ctypes
+        self.torch = torch
+        self.P = sq.probe_lib()
+        khz = ctypes.c_int(0)
+        if self.P.sqp_wall_clock_khz(ctypes.byref(khz)) != 0 or khz.value <= 0:
+            raise RuntimeError("sqp_wall_clock_khz failed")
+        self.khz = khz.value
+        self.out = torch.zeros(5, dtype=torch.int64, device=dev)
+        self.side = torch.cuda.Stream(device=dev)      # default priority
+        self.span_us = 0.0
 
-    def _read(self):
-        m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
-        vals = []
-        for key in ("current_gfxclks", "current_gfxclk"):
-            v = m.get(key)
-            for x in (v if isinstance(v, (list, tuple)) else [v]):
-                if isinstance(x, (int, float)) and 0 < x < 10000:
-                    vals.append(float(x))
-            if vals:
-                break
-        if not vals:
-            raise RuntimeError("no graphics clock in the metrics table")
-        return sum(vals) / len(vals)
-
-    def start(self):
-        import threading
-        if self.err:
-            return self
-        self.samples = []
-        self._stop = threading.Event()
-
-        def loop():
-            while not self._stop.is_set():
-                try:
-                    self.samples.append(self._read())
-                except Exception as e:
-                    self.err = f"{type(e).__name__}: {e}"
-                    return
-                time.sleep(self.period)
-        self._thr = threading.Thread(target=loop, daemon=True)
-        self._thr.start()
-        return self
+    def start(self, span_us):
+        """Queue the probe for `span_us` microseconds of real time (call just
+        before queueing the work, which should last longer)."""
+        self.span_us = float(span_us)
+        ticks = max(1, int(span_us * 1e-6 * self.khz * 1e3))
+        if self.P.sqp_clock_watch(ticks, ticks + 1000, self.out.data_ptr(), self.side.cuda_stream):
+            raise RuntimeError("sqp_clock_watch failed")
 
     def stop(self):
-        if self._thr is not None:
-            self._stop.set()
-            self._thr.join()
-            self._thr = None
-        if self.err or not self.samples:
-            return {"mhz": None, "why": self.err or "no samples"}
-        v = sorted(self.samples)
-        return {"mhz": round(v[len(v) // 2], 1), "min": round(v[0], 1), "max": round(v[-1], 1),
-                "samples": len(v),
-                "how": "amdsmi gpu_metrics current graphics clock (mean over XCDs), sampled "
-                       "on a host thread during the launches"}
+        """Wait for the probe; its reading as a dict (MHz)."""
+        self.torch.cuda.synchronize()
+        r0, r1, c0, c1, it = (int(v) for v in self.out.cpu().tolist())
+        secs = (r1 - r0) / (self.khz * 1e3)
+        mhz = (c1 - c0) / secs / 1e6 if secs > 0 else None
+        return {"mhz": round(mhz, 1) if mhz else None, "span_us": round(secs * 1e6, 1),
+                "how": "shader cycle counter over real-time counter, read by a one-wave probe "
+                       "kernel on a second stream while the launches ran (sqp_clock_watch)"}
 
 
 def prefill_leg(torch, workloads, sq, L, dev, stream, hs, launches, clock, hosts):
@@ -240,8 +203,9 @@ def prefill_leg(torch, workloads, sq, L, dev, stream, hs, launches, clock, hosts
     matrix cores' power, and so their clock, depends on the codes), each as
     `launches` launches between one event pair; and the per-token quantizer of
     the same batches, `launches` launches likewise (HBM-bound: 2MK bytes of X,
-    MK of codes, 4M of scales).  The graphics clock is sampled during the
-    product launches; the host inputs are kept in `hosts` for the CPU baseline."""
+    MK of codes, 4M of scales).  The shader clock is measured during the
+    product launches (ClockWatch); the host inputs are kept in `hosts` for the
+    CPU baseline."""
     out = {"peak": PEAK_INT8_TOPS, "unit": "TOP/s"}
     for name in ("down11008", "prefill8192x3"):
         wl = workloads.WORKLOADS[name]
@@ -288,11 +252,16 @@ def prefill_leg(torch, workloads, sq, L, dev, stream, hs, launches, clock, hosts
         def run():
             return L.sq_w8a8_gemm(xq.data_ptr(), xsc.data_ptr(), wq.data_ptr(), wsc.data_ptr(), M,
                                   N, K, y.data_ptr(), N, sq.SQ_OUT_F16, hs)
+        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0.record(stream)
         for _ in range(3):
             if run():
                 raise RuntimeError(f"{name}: product failed")
+        w1.record(stream)
+        torch.cuda.synchronize()
+        warm_us = w0.elapsed_time(w1) * 1e3 / 3
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        clock.start()
+        clock.start(0.8 * launches * warm_us)
         e0.record(stream)
         for _ in range(launches):
             run()
@@ -350,41 +319,42 @@ def decode_leg(torch, workloads, sq, L, dev, stream, hs, launches):
         xs = torch.empty(m, dtype=torch.float32, device=dev)
         y = torch.empty((m, N), dtype=torch.float16, device=dev)
 
-        def run(i, with_quant):
+        def run(i, mode):
+            # mode: "layer" = quantization + product, "gemm" = the product alone
             r = 0
-            if with_quant:
+            if mode == "layer":
                 r |= L.sq_quant_act_per_token(x.data_ptr(), m, K, K, inv.data_ptr(), xq.data_ptr(),
                                               xs.data_ptr(), hs)
             r |= L.sq_w8a8_gemm(xq.data_ptr(), xs.data_ptr(), copies[i % 4].data_ptr(),
                                 wsc.data_ptr(), m, N, K, y.data_ptr(), N, sq.SQ_OUT_F16, hs)
             return r
         res = {}
-        for with_quant in (True, False, True, False):
+        for mode in ("layer", "gemm", "layer", "gemm"):     # second round is the one kept
             for i in range(8):
-                if run(i, with_quant):
+                if run(i, mode):
                     raise RuntimeError("decode layer call failed")
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for i in range(launches):
-                run(i, with_quant)
+                run(i, mode)
             e1.record(stream)
             torch.cuda.synchronize()
-            res[with_quant] = e0.elapsed_time(e1) * 1e3 / launches
-        gb_layer = N * K / (res[True] * 1e-6) / 1e9
-        gb_gemm = N * K / (res[False] * 1e-6) / 1e9
+            res[mode] = e0.elapsed_time(e1) * 1e3 / launches
+        gb_layer = N * K / (res["layer"] * 1e-6) / 1e9
+        gb_gemm = N * K / (res["gemm"] * 1e-6) / 1e9
         # algorithmic bytes of the layer: int8 weights, weight scales, fp16 X
         # in, 1/s, fp16 Y out (the codes' round trip between the two kernels
         # is the implementation's cost, charged against the time)
         alg = K * N + 4 * N + 2 * m * K + 4 * K + 2 * m * N
-        gb_alg = alg / (res[True] * 1e-6) / 1e9
-        out[f"M{m}"] = {"layer_us": round(res[True], 2), "gemm_us": round(res[False], 2),
+        gb_alg = alg / (res["layer"] * 1e-6) / 1e9
+        out[f"M{m}"] = {"layer_us": round(res["layer"], 2), "gemm_us": round(res["gemm"], 2),
                         "algorithmic_bytes": alg,
                         "layer_alg_gbs": round(gb_alg, 1),
                         "layer_alg_frac": round(gb_alg / PEAK_HBM_GBS, 4),
                         "layer_gbs": round(gb_layer, 1), "gemm_gbs": round(gb_gemm, 1),
                         "layer_frac": round(gb_layer / PEAK_HBM_GBS, 4),
                         "gemm_frac": round(gb_gemm / PEAK_HBM_GBS, 4)}
-        log(f"decode M={m}: layer {res[True]:.2f} us, product {res[False]:.2f} us")
+        log(f"decode M={m}: layer {res['layer']:.2f} us, product {res['gemm']:.2f} us")
 
     # The same layer as Smooth Rotation at 4 bits: factors, Hadamard-rotated
     # 4-bit weights packed two per byte (half the bytes), rotated 4-bit tokens.
@@ -500,8 +470,8 @@ def main():
     ap.add_argument("--product-launches", type=int, default=10,
                     help="product launches per batch")
     ap.add_argument("--clock-launches", type=int, default=1000,
-                    help="back-to-back product launches during which the graphics clock is "
-                         "sampled (0: skip)")
+                    help="back-to-back product launches during which the shader clock is "
+                         "measured on the GPU (0: skip)")
     ap.add_argument("--norm-launches", type=int, default=100,
                     help="launches of the fused RMS-norm + quantization (and of the plain "
                          "quantizer) timed between one pair of events (0: skip)")
@@ -675,11 +645,11 @@ def main():
     def pct(q):
         return batch_us[min(len(batch_us) - 1, int(q * len(batch_us)))]
 
-    # The graphics clock while the product runs back to back.
-    clock = ClockSampler(torch, dev)
+    # The shader clock while the product runs back to back.
+    clock = ClockWatch(torch, sq, dev)
     clk = {"mhz": None, "why": "skipped"}
     if args.clock_launches > 0:
-        clock.start()
+        clock.start(0.8 * args.clock_launches * gemm_us)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(args.clock_launches):
@@ -689,8 +659,8 @@ def main():
         clk = clock.stop()
         clk["launches"] = args.clock_launches
         clk["product_us"] = round(e0.elapsed_time(e1) * 1e3 / args.clock_launches, 2)
-        log(f"graphics clock during {args.clock_launches} products: {clk.get('mhz')} MHz "
-            f"({clk.get('why', '')}), {clk['product_us']} us per product")
+        log(f"shader clock during {args.clock_launches} products: {clk.get('mhz')} MHz, "
+            f"{clk['product_us']} us per product")
 
     # The normalization in front of the layer with 1/s folded into its weight:
     # the fused RMS-norm + quantization against the plain quantizer on the

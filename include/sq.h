@@ -19,7 +19,8 @@
  *   - Matrices are row-major; "ld" arguments are row strides in elements.
  *   - fp16 data is IEEE binary16 passed as raw bits (const void*).
  *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
- *     Work is enqueued on that stream; only sq_smooth_fold_weights waits (for s).
+ *     Work is enqueued on that stream; only the calls that compute smoothing
+ *     factors (the two folds and sq_smoothing_factors) wait, for s.
  *   - Every argument is checked before any HIP call or any write: a call that
  *     returns an argument error (SQ_ERR_NULL, _SHAPE, _ALIGN, _ALPHA, _KIND,
  *     _EPS) has no side effects.

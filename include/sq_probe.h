@@ -34,6 +34,20 @@ int sqp_mfma_rate(const int8_t *a, const int8_t *b, int iters, int blocks, int *
  */
 int sqp_stream_read(const void *buf, int64_t bytes, int blocks, int *out, void *stream);
 
+/* The constant rate of the device's real-time counter (s_memrealtime), kHz. */
+int sqp_wall_clock_khz(int *khz);
+
+/*
+ * One wave on one CU reads the shader cycle counter and the real-time counter,
+ * sleeps until `ticks` real-time ticks have passed (at most `max_iter` sleeps
+ * of 8 x 64 cycles), and reads both again:
+ *   out  device uint64 [5], written: real-time start and end, cycles start
+ *        and end, sleeps taken.
+ * Queued on a second stream just before other work, it measures the shader
+ * clock that work runs at: (cycles end - start) / (real-time span).
+ */
+int sqp_clock_watch(uint64_t ticks, uint64_t max_iter, uint64_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -68,6 +68,8 @@ def test_header_constants_match_binding(sq):
         m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
         assert m and int(m.group(1)) == getattr(sq, name), name
     assert int(re.search(r"#define SQ_MAX_K (\d+)", text).group(1)) == sq.SQ_MAX_K
+    for name in ("SQ_NOALLOC_MAX_N",):
+        assert int(re.search(rf"#define {name} (\d+)", text).group(1)) == getattr(sq, name)
 
 
 # ---- calibrate ----------------------------------------------------------------
@@ -561,3 +563,7 @@ def test_probe_rejects_bad_arguments_before_launching(probe):
     assert probe.sqp_stream_read(P, 1000, 64, Q, None) == 1     # not a multiple of 16
     assert probe.sqp_stream_read(None, 1024, 64, Q, None) == 1
     assert probe.sqp_stream_read(P, 1024, 0, Q, None) == 1
+    assert probe.sqp_clock_watch(100, 100, None, None) == 1
+    assert probe.sqp_clock_watch(0, 100, P, None) == 1
+    assert probe.sqp_clock_watch(100, 0, P, None) == 1
+    assert probe.sqp_wall_clock_khz(None) == 1

@@ -43,3 +43,22 @@ def test_stream_read_xor(env):
     torch.cuda.synchronize()
     o = out.cpu()
     assert o[0].item() == 0x5a and torch.all(o[1:] == 0)
+
+
+def test_clock_watch_reads_a_plausible_clock(env):
+    """The one-wave clock probe ends after about the asked span of real time
+    and reads a shader clock between 0.1 and 3 GHz (MI355X peaks at 2.4)."""
+    import ctypes
+    torch, P, dev = env
+    khz = ctypes.c_int(0)
+    assert P.sqp_wall_clock_khz(ctypes.byref(khz)) == 0 and khz.value > 0
+    out = torch.zeros(5, dtype=torch.int64, device=dev)
+    ticks = int(0.002 * khz.value * 1e3)                 # 2 ms
+    hs = torch.cuda.current_stream(dev).cuda_stream
+    assert P.sqp_clock_watch(ticks, ticks + 1000, out.data_ptr(), hs) == 0
+    torch.cuda.synchronize()
+    r0, r1, c0, c1, it = out.cpu().tolist()
+    assert r1 - r0 >= ticks and 0 < it <= ticks + 1000
+    mhz = (c1 - c0) / ((r1 - r0) / (khz.value * 1e3)) / 1e6
+    print(f"[clock] {mhz:.0f} MHz over {(r1 - r0) / khz.value:.2f} ms, {it} sleeps", flush=True)
+    assert 100 < mhz < 3000

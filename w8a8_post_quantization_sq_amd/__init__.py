@@ -114,7 +114,7 @@ def lib() -> ctypes.CDLL:
 
 
 PROBE_PATH = os.path.join(HERE, "libsq_probe.so")
-PROBE_EXPORTS = ("sqp_mfma_rate", "sqp_stream_read")
+PROBE_EXPORTS = ("sqp_mfma_rate", "sqp_stream_read", "sqp_wall_clock_khz", "sqp_clock_watch")
 _PROBE = None
 
 
@@ -132,6 +132,10 @@ def probe_lib() -> ctypes.CDLL:
         P.sqp_mfma_rate.argtypes = [vp, vp, ci, ci, vp, vp]
         P.sqp_stream_read.restype = ci
         P.sqp_stream_read.argtypes = [vp, i64, ci, vp, vp]
+        P.sqp_wall_clock_khz.restype = ci
+        P.sqp_wall_clock_khz.argtypes = [ctypes.POINTER(ci)]
+        P.sqp_clock_watch.restype = ci
+        P.sqp_clock_watch.argtypes = [ctypes.c_uint64, ctypes.c_uint64, vp, vp]
         _PROBE = P
     return _PROBE
 

@@ -59,9 +59,49 @@ k_stream_read(const v4i *__restrict__ p, int64_t n, int *__restrict__ out) {
     out[(size_t)blockIdx.x * 256 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
+// The shader clock over a stretch of real time: one lane reads the shader
+// cycle counter (s_memtime) and the constant-rate real-time counter
+// (s_memrealtime) at its start, sleeps until `ticks` real-time ticks have
+// passed (or `max_iter` sleeps, whichever comes first, so the wave always
+// ends), and reads both again.  Launched on a second stream just before a run
+// of product kernels, it shares a CU with them and sees the clock they run at.
+__global__ void __launch_bounds__(64)
+k_clock_watch(uint64_t ticks, uint64_t max_iter, uint64_t *__restrict__ out) {
+    if (threadIdx.x != 0) return;
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    const uint64_t c0 = __builtin_amdgcn_s_memtime();
+    uint64_t r = r0, it = 0;
+    while (r - r0 < ticks && it < max_iter) {
+        __builtin_amdgcn_s_sleep(8);
+        r = __builtin_amdgcn_s_memrealtime();
+        ++it;
+    }
+    const uint64_t c1 = __builtin_amdgcn_s_memtime();
+    out[0] = r0;
+    out[1] = r;
+    out[2] = c0;
+    out[3] = c1;
+    out[4] = it;
+}
+
 }  // namespace
 
 extern "C" {
+
+__attribute__((visibility("default")))
+int sqp_wall_clock_khz(int *khz) {
+    int dev = 0;
+    if (!khz) return 1;
+    if (hipGetDevice(&dev) != hipSuccess) return 7;
+    return hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess ? 0 : 7;
+}
+
+__attribute__((visibility("default")))
+int sqp_clock_watch(uint64_t ticks, uint64_t max_iter, uint64_t *out, void *stream) {
+    if (!out || ticks < 1 || max_iter < 1) return 1;
+    k_clock_watch<<<dim3(1), dim3(64), 0, (hipStream_t)stream>>>(ticks, max_iter, out);
+    return hipGetLastError() == hipSuccess ? 0 : 7;
+}
 
 __attribute__((visibility("default")))
 int sqp_mfma_rate(const int8_t *a, const int8_t *b, int iters, int blocks, int *out,
