@@ -215,7 +215,8 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
         wsv[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         if (F16OUT) {
             if (n + 3 < N) {
-                wsv[j] = make_float4(ws[n], ws[n + 1], ws[n + 2], ws[n + 3]);
+                // one 16-byte load: ws is 16-byte aligned and n a multiple of 4
+                wsv[j] = *reinterpret_cast<const float4 *>(ws + n);
             } else {
                 if (n < N) wsv[j].x = ws[n];
                 if (n + 1 < N) wsv[j].y = ws[n + 1];
@@ -269,9 +270,12 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
             lds_load16(rw, ring + (t & 7) * T_SLICE + wave * T_FRAG, wbase + winw(t));
         };
         // Prologue: slices 0..3 and activation steps 0..2, interleaved (slice s,
-        // then step s's two fragments), so the first products wait only for
-        // the first two slices and not for the whole burst every CU issues at
-        // once: after slice 1, 6 loads follow (steps 1 and 2, slices 2 and 3).
+        // then step s's two fragments), then every load of it waited for:
+        // all four slices are in LDS before the loop, which is what the loop's
+        // one wait per step assumes for steps 0 and 1.  (A wait for slices 0
+        // and 1 only is what __syncthreads' own release fence turns into a
+        // full wait anyway, and a barrier without that fence lets the
+        // compiler sink the activation loads below it.)
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
             __builtin_amdgcn_sched_barrier(0);
@@ -281,7 +285,7 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
         __builtin_amdgcn_sched_barrier(0);
         dma_w(3);
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(0x0F76);        // vmcnt(6): slices 0 and 1 have landed
+        __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0): slices 0..3 have landed
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < 8; ++j)
@@ -324,16 +328,15 @@ k_gemm_tile(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
                 // 8 loads were issued after it (2 in its step, 3 in each later
                 // one), and memory loads complete in order, so vmcnt(8) means it
                 // has landed in this wave's part of the buffer; the barrier then
-                // publishes every wave's part.  Slices 2 and 3 were issued in
-                // the prologue, and only 6 loads follow each of them by the end of
-                // steps 0 and 1 respectively, so those two steps wait on vmcnt(6).
-                // The buffer a step loads into (slice t+4: buffer (t-4) & 7) was
-                // last read in step t-5.
+                // publishes every wave's part.  Slices 2 and 3 (steps 0 and 1)
+                // landed in the prologue.  The same wait on every step matters:
+                // a different wait for the first steps made the compiler peel
+                // the first 4 steps and sink their activation loads past the
+                // loop's exit test, leaving fewer than 8 loads behind slices 4
+                // and 5.  The buffer a step loads into (slice t+4: buffer
+                // (t-4) & 7) was last read in step t-5.
                 __builtin_amdgcn_sched_barrier(0);
-                if (t < 2)
-                    __builtin_amdgcn_s_waitcnt(0x0F76);    // vmcnt(6)
-                else
-                    __builtin_amdgcn_s_waitcnt(0x0F78);    // vmcnt(8)
+                __builtin_amdgcn_s_waitcnt(0x0F78);    // vmcnt(8)
                 __builtin_amdgcn_s_barrier();
                 // keep each step's products inside the step: hoisting them above
                 // the barrier would put them right behind the LDS reads they use
