@@ -402,6 +402,9 @@ def test_quant_ties_and_degenerate_rows(sq, dev, orc):
 GEMM_SHAPES = [(1, 1, 16), (3, 5, 48), (17, 100, 80), (40, 100, 320), (49, 1000, 1088),
                (9, 64, 4096), (25, 33, 256), (32, 48, 1024),
                (16, 28672, 128), (9, 28672, 64), (24, 8192, 64), (32, 12304, 64), (20, 8200, 64),
+               # 7 blocks per workgroup of 8 waves over more than one batch round, one and
+               # two row blocks, a ragged last window
+               (16, 28672, 2112), (32, 28672, 2112), (25, 28672, 1040),
                (64, 70, 4096), (65, 33, 64), (100, 200, 64), (128, 128, 4096),
                (130, 129, 1040), (256, 384, 2048), (1, 28672, 128), (16, 300, 8192), (513, 77, 112),
                # 256 x 256 tiles (their rounds of 256 CUs beat the 256 x 128 ones'): ragged M,

@@ -559,12 +559,16 @@ k_gemm_skinny(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
 // always with 4-bit weights, whose 512-byte fragments would otherwise be
 // outweighed by the activations); a window batch's loads stay ahead of its
 // products, and 4-bit codes are widened just before the matrix instruction.
-template <int MB, bool F16OUT, bool W4, int CB>
-__global__ void __launch_bounds__(256)
+// NW waves per workgroup take interleaved k windows; with 7 blocks (one
+// workgroup per CU) 8 waves of half the batch each keep two waves on every
+// SIMD, so one wave's products overlap another's loads.
+template <int MB, bool F16OUT, bool W4, int CB, int NW = 4>
+__global__ void __launch_bounds__(64 * NW)
 k_gemm_skinny_cb(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
               const float *__restrict__ xs, const float *__restrict__ ws, int M, int N, int K,
               void *__restrict__ Y, int64_t ldy, int vec_ok) {
-    __shared__ __align__(16) v4i part[3][CB][MB][64];
+    static_assert(NW == 4 || NW == 8, "waves per workgroup");
+    __shared__ __align__(16) v4i part[NW - 1][CB][MB][64];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -589,14 +593,16 @@ k_gemm_skinny_cb(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
     for (int c = 0; c < CB; ++c)
 #pragma unroll
         for (int b = 0; b < MB; ++b) acc[c][b] = v4i{0, 0, 0, 0};
-    // wave w takes windows w, w + 4, w + 8, ...: the 4 waves stream adjacent KiB
-    constexpr int SU = MB >= 3 ? S_UNROLL / 2 : S_UNROLL;
-    for (int t0 = wave; t0 < KW; t0 += 4 * SU) {
+    // wave w takes windows w, w + NW, w + 2 NW, ...: the waves stream adjacent
+    // KiB; a batch is SU windows, so a workgroup keeps the same bytes in flight
+    // for either wave count
+    constexpr int SU = (MB >= 3 ? S_UNROLL / 2 : S_UNROLL) * 4 / NW;
+    for (int t0 = wave; t0 < KW; t0 += NW * SU) {
         v4i xf[SU][MB], wf[SU][CB];
         uint2 wp[SU][CB];   // 4-bit: the packed codes as loaded
 #pragma unroll
         for (int u = 0; u < SU; ++u) {
-            const int t = t0 + 4 * u;
+            const int t = t0 + NW * u;
             // the weights are read exactly once (non-temporal up to 32 tokens)
 #pragma unroll
             for (int c = 0; c < CB; ++c) {
@@ -651,7 +657,7 @@ k_gemm_skinny_cb(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
 #pragma unroll
         for (int b = 0; b < MB; ++b) {
 #pragma unroll
-            for (int w = 0; w < 3; ++w) {
+            for (int w = 0; w < NW - 1; ++w) {
                 const v4i p = part[w][c][b][lane];
                 acc[c][b][0] += p[0];
                 acc[c][b][1] += p[1];
@@ -708,9 +714,9 @@ void launch_skinny(int cb, dim3 grid, hipStream_t st, const int8_t *xq, const in
         else if (cb == 4)
             k_gemm_skinny_cb<MB, F16OUT, W4, 4><<<grid, b, 0, st>>>(xq, wq, x_scale, w_scale, m, n,
                                                                    k, y, ldy, vec_ok);
-        else if constexpr (!W4)
-            k_gemm_skinny_cb<MB, F16OUT, W4, 7><<<grid, b, 0, st>>>(xq, wq, x_scale, w_scale, m, n,
-                                                                   k, y, ldy, vec_ok);
+        else if constexpr (!W4)   // 8 waves (measured: 37.7-38.0 vs 38.3-38.9 us at 16 tokens)
+            k_gemm_skinny_cb<MB, F16OUT, W4, 7, 8><<<grid, dim3(512), 0, st>>>(
+                xq, wq, x_scale, w_scale, m, n, k, y, ldy, vec_ok);
     }
 }
 
