@@ -14,7 +14,9 @@ needed), take each 8-bit tile kernel's prologue and k loop from the
 assembly, and replay the wave's issue order: at every barrier, each slice
 that the next step reads must be covered by a wait issued before it (slice s
 is read from step s - 1 on, and before the loop for s = 0).  Three loop
-iterations are replayed, so the steady state is checked too.
+iterations are replayed, so the steady state is checked too.  The 4-bit
+tile kernel, which stages its slices with LDS stores and an lgkmcnt wait,
+is checked the same way on its LDS operations.
 """
 import os
 import re
@@ -144,6 +146,69 @@ def test_wide_kernel_waits_cover_every_slice(asm):
         assert [k for k, _ in body].count("D") == 8 and [k for k, _ in body].count("B") == 4, name
         assert [k for k, _ in pro].count("B") == 1, name
         assert replay(pro, body, slice_dmas=2) >= 12, name
+
+
+def lds_events(lines):
+    """LDS-side events in issue order: S (LDS store), R (LDS read), M (scalar
+    memory load, which also counts in lgkmcnt and completes out of order),
+    G<n> (s_waitcnt with lgkmcnt), B (s_barrier), plus loop markers."""
+    ev = []
+    for raw in lines:
+        s = raw.split(";")[0].strip()
+        if not s:
+            continue
+        if s.endswith(":") and s.startswith(".LBB"):
+            if "Loop Header" in raw:
+                ev.append(("H", s[:-1]))
+            continue
+        op = s.split()[0]
+        if op.startswith(("ds_write", "ds_store")):
+            ev.append(("S", None))
+        elif op.startswith(("ds_read", "ds_load")):
+            ev.append(("R", None))
+        elif op.startswith(("s_load", "s_buffer_load")):
+            ev.append(("M", None))
+        elif op == "s_waitcnt" and "lgkmcnt(" in s:
+            ev.append(("G", int(s.split("lgkmcnt(")[1].split(")")[0])))
+        elif op == "s_barrier":
+            ev.append(("B", None))
+        elif op.startswith("s_cbranch") or op == "s_branch":
+            ev.append(("J", s.split()[-1]))
+    return ev
+
+
+def test_four_bit_tile_kernel_publishes_each_staged_slice(asm):
+    """The 4-bit tile kernel stages each widened weight slice with an LDS
+    store and ends the step on lgkmcnt(n) and a barrier: LDS operations of a
+    wave complete in order, so the store has landed if at least n LDS
+    operations follow it before the wait (and no scalar load, which counts
+    in the same counter out of order, is pending in the loop)."""
+    kernels = kernel_body(asm, "_ZN2sq11k_gemm_tileIL")
+    four_bit = {k: v for k, v in kernels.items() if re.match(r"_ZN2sq11k_gemm_tileILb[01]ELb1E", k)}
+    assert len(four_bit) == 2, sorted(kernels)
+    for name, lines in four_bit.items():
+        ev = lds_events(lines)
+        hdr = next(i for i, e in enumerate(ev) if e[0] == "H")
+        back = next(i for i in range(hdr + 1, len(ev)) if ev[i] == ("J", ev[hdr][1]))
+        body = [e for e in ev[hdr + 1:back] if e[0] in "SRMGB"]
+        assert not any(k == "M" for k, _ in body), name
+        steps, cur = [], []
+        for e in body:
+            if e[0] == "B":
+                steps.append(cur)
+                cur = []
+            else:
+                cur.append(e)
+        assert len(steps) == 4, name
+        for step in steps:
+            kinds = [k for k, _ in step]
+            assert kinds.count("S") == 1, (name, kinds)
+            s = kinds.index("S")
+            waits = [i for i, (k, _) in enumerate(step) if k == "G" and i > s]
+            assert waits, (name, kinds)
+            w = waits[-1]
+            after = sum(1 for k in kinds[s + 1:w] if k in "SR")
+            assert after >= step[w][1], (name, kinds)
 
 
 def test_replay_catches_a_peeled_first_iteration():
