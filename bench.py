@@ -17,8 +17,8 @@ Printed: one JSON line with the layer throughput (2MNK per step / wall time),
 the product kernel against the int8 matrix-core roofline (its launch duration
 from batches of back-to-back launches between HIP events on the library's
 stream), the shader clock measured on the GPU during a run of those launches,
-and, outside
-the step: the product at the other large-token configurations (down_proj
+the same layer recorded once as a HIP graph and replayed, and, outside the
+step: the product at the other large-token configurations (down_proj
 2048 x 11008 -> 4096, prefill 8192 x 8192 -> 3 x 8192), the decode-size layer
 (M = 1, 4 and 16 tokens against an 8192 x 28672 layer, the metric's M <= 16
 half, as GB/s of its algorithmic bytes and of its weights), the fused RMS-norm
@@ -286,6 +286,24 @@ def prefill_leg(torch, workloads, sq, L, dev, stream, hs, launches, clock, hosts
     return out
 
 
+def record_graph(torch, dev, fn):
+    """fn(stream handle) recorded in a HIP graph: one eager run on a side
+    stream first (as torch asks before capture), then the capture, on the
+    stream torch records on.  The serving calls launch kernels only (no
+    allocation, memset or host wait), so they record as plain kernel nodes."""
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        fn(side.cuda_stream)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn(torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.synchronize()
+    return g
+
+
 def decode_leg(torch, workloads, sq, L, dev, stream, hs, launches):
     """The serving-time layer at decode sizes, the metric's M <= 16 half: the
     decode8192 workload (K 8192, N 28672) folded once, its codes copied 4 times
@@ -340,6 +358,30 @@ def decode_leg(torch, workloads, sq, L, dev, stream, hs, launches):
             e1.record(stream)
             torch.cuda.synchronize()
             res[mode] = e0.elapsed_time(e1) * 1e3 / launches
+
+        # the same layers recorded once as a HIP graph (8 layers over the 4
+        # copies) and replayed between one event pair
+        def layers8(h):
+            r = 0
+            for i in range(8):
+                r |= L.sq_quant_act_per_token(x.data_ptr(), m, K, K, inv.data_ptr(),
+                                              xq.data_ptr(), xs.data_ptr(), h)
+                r |= L.sq_w8a8_gemm(xq.data_ptr(), xs.data_ptr(), copies[i % 4].data_ptr(),
+                                    wsc.data_ptr(), m, N, K, y.data_ptr(), N, sq.SQ_OUT_F16, h)
+            if r:
+                raise RuntimeError("decode layer call failed")
+        g = record_graph(torch, dev, layers8)
+        reps = max(1, launches // 8)
+        for _ in range(2):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res["graph"] = e0.elapsed_time(e1) * 1e3 / (8 * reps)
+        del g
         gb_layer = N * K / (res["layer"] * 1e-6) / 1e9
         gb_gemm = N * K / (res["gemm"] * 1e-6) / 1e9
         # algorithmic bytes of the layer: int8 weights, weight scales, fp16 X
@@ -353,8 +395,12 @@ def decode_leg(torch, workloads, sq, L, dev, stream, hs, launches):
                         "layer_alg_frac": round(gb_alg / PEAK_HBM_GBS, 4),
                         "layer_gbs": round(gb_layer, 1), "gemm_gbs": round(gb_gemm, 1),
                         "layer_frac": round(gb_layer / PEAK_HBM_GBS, 4),
-                        "gemm_frac": round(gb_gemm / PEAK_HBM_GBS, 4)}
-        log(f"decode M={m}: layer {res['layer']:.2f} us, product {res['gemm']:.2f} us")
+                        "gemm_frac": round(gb_gemm / PEAK_HBM_GBS, 4),
+                        "layer_graph_us": round(res["graph"], 2),
+                        "layer_graph_alg_frac": round(alg / (res["graph"] * 1e-6) / 1e9
+                                                      / PEAK_HBM_GBS, 4)}
+        log(f"decode M={m}: layer {res['layer']:.2f} us (graph {res['graph']:.2f}), "
+            f"product {res['gemm']:.2f} us")
 
     # The same layer as Smooth Rotation at 4 bits: factors, Hadamard-rotated
     # 4-bit weights packed two per byte (half the bytes), rotated 4-bit tokens.
@@ -462,6 +508,8 @@ def main():
     ap.add_argument("--full-steps", type=int, default=50,
                     help="steps of the separate pass over every row A1..A6 (calibrate, fold, "
                          "quantize, product) per batch (0: skip)")
+    ap.add_argument("--graph-steps", type=int, default=400,
+                    help="layers timed as replays of a HIP graph of 20 layers (0: skip)")
     ap.add_argument("--stage-steps", type=int, default=20,
                     help="steps of the separate, untimed pass with an event between stages")
     ap.add_argument("--product-batches", type=int, default=20,
@@ -602,6 +650,40 @@ def main():
                 "steps": args.full_steps, "ms_per_step": round(fwall * 1e3 / args.full_steps, 4),
                 "tops": round(ops * args.full_steps / fwall / 1e12, 2)}
         log(f"full step (A1..A6): {fwall * 1e3 / args.full_steps:.4f} ms")
+
+    # The same serving layer recorded as a HIP graph of back-to-back layers and
+    # replayed, as a serving loop that records its layers would run it: wall
+    # clock over the replays, bracketed by device synchronizations like the step.
+    lgraph = None
+    if args.graph_steps > 0:
+        per_graph = 20
+
+        def layers(h):
+            st = 0
+            for _ in range(per_graph):
+                st |= L.sq_quant_act_per_token(p["x"], M, K, K, p["inv"], p["xq"], p["xsc"], h)
+                st |= L.sq_w8a8_gemm(p["xq"], p["xsc"], p["wq"], p["wsc"], M, N, K, p["y"], N,
+                                     sq.SQ_OUT_F16, h)
+            if st:
+                raise RuntimeError(f"layer call failed: status bits {st}")
+
+        g = record_graph(torch, dev, layers)
+        reps = max(1, args.graph_steps // per_graph)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        gus = (time.perf_counter() - t2) * 1e6 / (reps * per_graph)
+        del g
+        lgraph = {"what": "the step's two calls recorded as one HIP graph of "
+                          f"{per_graph} layers, replayed back to back",
+                  "layers": reps * per_graph, "us": round(gus, 2),
+                  "tops": round(ops / (gus * 1e-6) / 1e12, 2),
+                  "frac_int8_peak": round(ops / (gus * 1e-6) / 1e12 / PEAK_INT8_TOPS, 4)}
+        log(f"layer as a graph: {gus:.2f} us per layer ({reps} replays of {per_graph})")
 
     # Per-stage breakdown, from a separate pass with an event between stages
     # (those events lengthen these steps a little).
@@ -775,6 +857,7 @@ def main():
                   "us": round(ms_step * 1e3, 2), "tops": round(value, 2),
                   "frac_int8_peak": round(value / PEAK_INT8_TOPS, 4),
                   "hbm_gbs_algorithmic": round(layer_bytes / (ms_step * 1e-3) / 1e9, 1)},
+        "layer_graph": lgraph,
         "full_step": full,
         "stage_ms": {n: round(v, 4) for n, v in per.items()},
         "roofline": {"kernel": "k_gemm_w8a8 (sq_w8a8_gemm)", "bound": "mfma",
