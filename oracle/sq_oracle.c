@@ -38,6 +38,8 @@
  *   - quantization is symmetric to [-127, 127] with round-half-even, per token
  *     for activations and per output channel for weights; scales are
  *     absmax/127 in float.
+ *   - where the float multiplier 127/absmax overflows (a maximum below
+ *     127/FLT_MAX), a zero value's code is 0 (code_of).
  *   - the int32 accumulator is exact for K < 133144.
  */
 #include <math.h>
@@ -143,6 +145,22 @@ int oracle_smoothing_factors(const float *ax, const float *aw, int64_t K, float 
     return status;
 }
 
+/* ---- one code ------------------------------------------------------------ */
+
+/* The code of a scaled value v with multiplier r = qmax / a (a the row's or
+ * column's maximum |v|): clamp(rint(v * r), -qmax, qmax).  In float, r
+ * overflows to infinity only for a maximum below qmax / FLT_MAX; then v * r
+ * is +-inf for v != 0, which the clamp takes to +-qmax, and NaN for v == 0,
+ * whose code is taken as 0, the code 0 * r has for every finite r. */
+static int8_t code_of(float v, float r, float qmax)
+{
+    if (v == 0.0f) return 0;
+    float q = rintf(v * r);
+    if (q > qmax) q = qmax;
+    if (q < -qmax) q = -qmax;
+    return (int8_t)q;
+}
+
 /* ---- A3: fold S into W and quantize per output channel ------------------ */
 
 /* Wt[j][n] = float(W[j][n]) * s[j]: row j of W takes the factor of input
@@ -169,10 +187,7 @@ void oracle_fold_quant_weights(const uint16_t *w, int64_t K, int64_t N, int64_t 
         w_scale[n] = amax / 127.0f;
         for (int64_t j = 0; j < K; ++j) {
             float wt = half_to_float(w[j * ldw + n]) * s[j];
-            float q = rintf(wt * r);
-            if (q > 127.0f) q = 127.0f;
-            if (q < -127.0f) q = -127.0f;
-            wq[n * K + j] = (int8_t)q;
+            wq[n * K + j] = code_of(wt, r, 127.0f);
         }
     }
 }
@@ -204,10 +219,7 @@ void oracle_quant_act_per_token(const uint16_t *x, int64_t M, int64_t K, int64_t
         x_scale[m] = a / 127.0f;
         for (int64_t j = 0; j < K; ++j) {
             float xt = half_to_float(x[m * ldx + j]) * inv_s[j];
-            float q = rintf(xt * r);
-            if (q > 127.0f) q = 127.0f;
-            if (q < -127.0f) q = -127.0f;
-            xq[m * K + j] = (int8_t)q;
+            xq[m * K + j] = code_of(xt, r, 127.0f);
         }
     }
 }
@@ -335,10 +347,7 @@ void oracle_rmsnorm_quant_per_token(const uint16_t *h, int64_t M, int64_t K, int
         float r = 127.0f / a;
         for (int64_t j = 0; j < K; ++j) {
             float xt = half_to_float(row[j]) * g[j];
-            float q = rintf(xt * r);
-            if (q > 127.0f) q = 127.0f;
-            if (q < -127.0f) q = -127.0f;
-            xq[m * K + j] = (int8_t)q;
+            xq[m * K + j] = code_of(xt, r, 127.0f);
         }
     }
 }
@@ -404,10 +413,7 @@ void oracle_quant4_rows(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
         float r = 7.0f / a;
         scale[m] = (a / 7.0f) * post;
         for (int64_t j = 0; j < K; ++j) {
-            float c = rintf(work[j] * r);
-            if (c > 7.0f) c = 7.0f;
-            if (c < -7.0f) c = -7.0f;
-            q[m * K + j] = (int8_t)c;
+            q[m * K + j] = code_of(work[j], r, 7.0f);
         }
     }
 }

@@ -284,6 +284,53 @@ def test_quantizer_degenerate_rows(orc):
     assert np.isfinite(xs[[0, 2]]).all() and np.abs(xq[[0, 2]]).max() == 127
 
 
+def overflow_rows(K, seed):
+    """Three fp16 rows with every magnitude in [2^-6, 2^-2] or zero (row 0 has
+    zeros, row 1 negative zeros, row 2 none): times 2^-120 every value is a
+    normal float, the row maximum is at most 2^-122, and 127 / max overflows."""
+    rng = np.random.default_rng(seed)
+    mag = 2.0 ** rng.uniform(-6, -2, size=(3, K))
+    x = (mag * rng.choice([-1.0, 1.0], size=(3, K))).astype(np.float16)
+    x[0, ::7] = 0.0
+    x[1, 3::5] = -0.0
+    return x
+
+
+def test_rows_whose_multiplier_overflows(orc):
+    """For a maximum a below QMAX / FLT_MAX the float multiplier QMAX / a is
+    infinite: nonzero values take the clamp's +-QMAX and zeros the code 0, in
+    every quantizer (8-bit activations, the fused norm, weights, 4-bit)."""
+    K = 64
+    x = overflow_rows(K, 5)
+    inv = np.full(K, 2.0 ** -120, np.float32)
+    xt = x.astype(np.float32) * inv
+    a = np.abs(xt).max(axis=1)
+    assert np.all(np.abs(xt[xt != 0]) >= np.float32(2.0 ** -126))      # normal floats
+    with np.errstate(over="ignore"):
+        assert np.all(np.isinf(np.float32(127.0) / a))
+    sign = np.sign(xt).astype(np.int8)
+    assert (sign == 0).sum() > 0
+    xq, xs = orc.quant_act_per_token(x, inv)
+    assert np.array_equal(xq, sign * 127)
+    assert np.array_equal(xs.view(np.uint32), (a / np.float32(127.0)).view(np.uint32))
+    xq2, _ = orc.rmsnorm_quant_per_token(x, inv, 1e-5)
+    assert np.array_equal(xq2, sign * 127)
+    wq, ws = orc.fold_quant_weights(np.ascontiguousarray(x.T), inv)
+    assert np.array_equal(wq, sign * 127) and np.array_equal(ws, xs)
+    # 4 bits: 7 / a overflows only for a <= 2^-126 (the smallest normal float)
+    x4 = (np.sign(x.astype(np.float32)) * 0.25).astype(np.float16)
+    q4, s4 = orc.quant4_act_per_token(x4, np.full(K, 2.0 ** -124, np.float32), False)
+    assert np.array_equal(q4, sign * 7)
+    assert np.all(s4 == np.float32(2.0 ** -126) / np.float32(7.0))
+    # rotated: a single nonzero 2^-126 at channel 1 spreads to +-2^-126 on
+    # every output, with the signs of row 1 of the Sylvester matrix
+    e1 = np.zeros((1, K), np.float16)
+    e1[0, 1] = 0.25
+    q4r, s4r = orc.quant4_act_per_token(e1, np.full(K, 2.0 ** -124, np.float32), True)
+    assert q4r[0].tolist() == [7 if i % 2 == 0 else -7 for i in range(K)]
+    assert s4r[0] == np.float32(2.0 ** -126) / np.float32(7.0)
+
+
 # ---- A5 / A6 ---------------------------------------------------------------------
 
 @pytest.mark.parametrize("shape", [(1, 1, 16), (7, 13, 48), (33, 65, 160), (3, 5, 4096)])
