@@ -142,6 +142,16 @@ def test_rmsnorm_quant_degenerate_rows(sq, dev, orc):
         assert s[8] == 0.0 and np.isnan(s[3]) and np.isnan(s[4])
 
 
+@pytest.mark.parametrize("M,K", [(5, 4096), (600, 4096), (300, 1040), (130, 16400)])
+def test_rmsnorm_rows_whose_multiplier_overflows(sq, dev, orc, M, K):
+    """A folded weight of 2^-120: rows whose maximum is below 127 / FLT_MAX
+    take +-127 and 0, as in the plain quantizer."""
+    from test_gpu_parity import overflow_mix
+    h = overflow_mix(M, K, 960 + M)
+    g = np.full(K, 2.0 ** -120, np.float32)
+    check_norm_quant(sq, dev, orc, h, g, EPS, f"overflowing multipliers M={M} K={K}")
+
+
 def test_rmsnorm_codes_are_the_quantizer_codes(sq, dev, orc):
     """The codes do not depend on the RMS factor: they equal the per-token
     quantizer's codes of h with the folded weight in place of 1/s."""

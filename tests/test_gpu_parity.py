@@ -393,6 +393,54 @@ def test_quant_ties_and_degenerate_rows(sq, dev, orc):
     assert H(xs)[1] == 0 and np.isnan(H(xs)[2]) and np.isnan(H(xs)[3])
 
 
+def overflow_mix(M, K, seed):
+    """fp16 rows for a 1/s of 2^-120: even rows have every magnitude in
+    [2^-6, 2^-2] or zero, so their scaled maximum is at most 2^-122 and the
+    float multiplier 127 / a overflows; odd rows reach 2^4, a finite
+    multiplier.  Every scaled value is a normal float or zero; every seventh
+    channel is zero, some others negative zero."""
+    rng = np.random.default_rng(seed)
+    mag = 2.0 ** rng.uniform(-6.0, -2.0, size=(M, K))
+    mag[1::2] *= 64.0
+    x = (mag * rng.choice([-1.0, 1.0], size=(M, K))).astype(np.float16)
+    x[:, ::7] = 0.0
+    x[1::4, 3::5] = -0.0
+    return x
+
+
+# every quantizer form: one token per workgroup (5, 40), row groups with and
+# without whole-row chunks (600 x 4096, 70 x 1024 / 300 x 1040, 520 x 8208),
+# and the 8-row streaming form past K = 16384 (130 x 16400)
+@pytest.mark.parametrize("M,K", [(5, 64), (40, 8192), (600, 4096), (70, 1024), (300, 1040),
+                                 (520, 8208), (130, 16400)])
+def test_quant_rows_whose_multiplier_overflows(sq, dev, orc, M, K):
+    """A caller's tiny 1/s: rows whose maximum is below 127 / FLT_MAX take
+    +-127 for nonzero values and 0 for zeros, as the oracle defines them."""
+    x = overflow_mix(M, K, 900 + M)
+    inv = np.full(K, 2.0 ** -120, np.float32)
+    xq, xs = sq.quant(T(x, dev), T(inv, dev))
+    rq, rs = orc.quant_act_per_token(x, inv)
+    g = H(xq)
+    assert bits_equal(H(xs), rs) and np.array_equal(unpack(g, M, K), rq)
+    assert padding_is_zero(g, M, K)
+    ev = rq[0::2]
+    assert np.all(np.isin(ev, [-127, 0, 127])) and (ev == 0).any() and (ev == 127).any()
+
+
+def test_fold_columns_whose_multiplier_overflows(sq, dev, orc):
+    """The fold with a caller's factors of 2^-120 (the smallest magnitudes the
+    factor checks accept are normal floats): even output channels' maxima
+    fall below 127 / FLT_MAX."""
+    K, N = 256, 200
+    w = np.ascontiguousarray(overflow_mix(N, K, 950).T)
+    s = np.full(K, 2.0 ** -120, np.float32)
+    f = sq.fold(T(w, dev), T(np.ones(K, np.float32), dev), 0.5, smooth_in=T(s, dev))
+    rq, rs = orc.fold_quant_weights(w, s)
+    assert bits_equal(H(f.w_scale), rs)
+    assert np.array_equal(unpack(H(f.wq), N, K), rq)
+    assert np.all(np.isin(rq[0::2], [-127, 0, 127])) and (rq[0::2] == 0).any()
+
+
 # ---- A5 + A6 the product -----------------------------------------------------------------
 
 # token counts 1..64 run the decode kernels (1, 2, 3 or 4 activation row blocks;

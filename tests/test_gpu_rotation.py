@@ -115,6 +115,32 @@ def test_a4_degenerate_rows(sq, dev, orc):
         assert s[1] == 0.0 and np.isnan(s[2]) and np.isnan(s[3])
 
 
+# every 4-bit form: rotated rows of K <= 2048, the transposed form (4096,
+# 8192), one token per workgroup (5 x 4096, 16 x 8192), and unrotated row groups
+@pytest.mark.parametrize("M,K,rotate", [(100, 1024, True), (100, 4096, True), (70, 8192, True),
+                                        (5, 4096, True), (16, 8192, True), (600, 4096, False),
+                                        (20, 1040, False)])
+def test_a4_rows_whose_multiplier_overflows(sq, dev, orc, M, K, rotate):
+    """Multipliers of 2^-124: even rows have scaled maximum 2^-126, below
+    7 / FLT_MAX, so their codes are +-7 and 0.  Rotated, such a row holds
+    2^-127 (a subnormal float) at two channels, whose transform is 0 or
+    +-2^-126; unrotated, +-2^-126 or 0 per channel.  Odd rows are ordinary."""
+    rng = np.random.default_rng(970 + M + K)
+    x = (rng.standard_normal((M, K)) * 4).astype(np.float16)
+    for r in range(0, M, 2):
+        x[r] = 0.0
+        if rotate:
+            c1, c2 = rng.choice(K, 2, replace=False)
+            x[r, c1] = 0.125
+            x[r, c2] = rng.choice([-0.125, 0.125])
+        else:
+            x[r] = (rng.choice([-1.0, 0.0, 1.0], K) * 0.25).astype(np.float16)
+    mult = np.full(K, 2.0 ** -124, np.float32)
+    _, xs = check_a4(sq, dev, orc, x, mult, rotate, f"overflowing M={M} K={K} rotate={rotate}")
+    rq, _ = orc.quant4_act_per_token(x, mult, rotate)
+    assert np.all(np.isin(rq[0::2], [-7, 0, 7])) and (rq[0::2] == 0).any() and (rq[0::2] == 7).any()
+
+
 @pytest.mark.parametrize("rotate", [True, False])
 @pytest.mark.parametrize("name,K,N,ldw", [("tiny", None, None, None), ("qkv4096", None, None, None),
                                           ("decode8192", None, None, None),

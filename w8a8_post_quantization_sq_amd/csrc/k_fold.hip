@@ -333,7 +333,10 @@ k_fold_quant(const uint16_t *__restrict__ w, int64_t K, int64_t N, int64_t ldw,
                 const float wt = v * sj[it][q];             // W~ = W * s_j (float)
                 float qf = __builtin_rintf(wt * r[c]);      // round half to even
                 qf = fminf(fmaxf(qf, -127.0f), 127.0f);
-                packed[c] |= ((uint32_t)(int)qf & 0xffu) << (8 * q);
+                // a zero value's code is 0, also where 127 / amax overflowed
+                // (a column maximum below 127 / FLT_MAX makes wt * r NaN there)
+                const uint32_t b = wt == 0.0f ? 0u : ((uint32_t)(int)qf & 0xffu);
+                packed[c] |= b << (8 * q);
             }
         }
 #pragma unroll

@@ -32,6 +32,8 @@
 // row-minor), so 16 consecutive codes of a row are one 16-byte piece and the
 // pieces of 16 consecutive rows for one quarter of a 64-code window are
 // contiguous.  X is read from HBM once (the second pass hits L2).
+#include <type_traits>
+
 #include "sq_device.h"
 
 namespace sq {
@@ -79,19 +81,49 @@ __device__ __forceinline__ void scale8(const Chunk &ch, float v[8], uint32_t &am
     }
 }
 
-template <int QMAX>
+// Codes of 8 values, clamp(rint(v * r), -QMAX, QMAX), zero codes for a row
+// with zero set.  CLAMP: as the definition writes it (rint, then the clamp),
+// for any multiplier: where r overflowed (a maximum below QMAX / FLT_MAX)
+// v * r is +-inf, which the clamp takes to +-QMAX, or NaN for v = 0, whose
+// code is 0 (the code 0 * r has for every finite r).
+// Otherwise with fewer instructions, for rows whose multiplier r is finite:
+// for |y| <= 2^22 the float sum y + 1.5 * 2^23 lies in [2^23, 2^24), where
+// the floats are exactly the integers, so its one rounding (to nearest, ties
+// to even) is rint(y), and the low byte of its bits is rint(y) mod 256, the
+// two's-complement code.  The clamp cannot act there: r = QMAX / a is a
+// correctly rounded quotient and every |v| <= a, so |v * r| <= QMAX (1 + 2^-24)
+// and rint gives at most QMAX.  (Callers take the clamped form for a row
+// whose r overflowed.)  v_perm_b32
+// gathers the low bytes: selector bytes 0..3 pick bytes of its second
+// operand, 4..7 of its first, 0x0c a zero byte.
+template <int QMAX, bool CLAMP = true>
 __device__ __forceinline__ uint2 quant8(const float v[8], float r, bool zero) {
-    uint32_t lo = 0, hi = 0;
+#pragma clang fp contract(off)
+    if (CLAMP) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float q = __builtin_rintf(v[i] * r);
+            q = fminf(fmaxf(q, -(float)QMAX), (float)QMAX);
+            const uint32_t b = (zero || v[i] == 0.0f) ? 0u : ((uint32_t)(int)q & 0xffu);
+            if (i < 4) lo |= b << (8 * i);
+            else hi |= b << (8 * (i - 4));
+        }
+        return make_uint2(lo, hi);
+    }
+    uint32_t b[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        float q = __builtin_rintf(v[i] * r);
-        q = fminf(fmaxf(q, -(float)QMAX), (float)QMAX);
-        const uint32_t b = zero ? 0u : ((uint32_t)(int)q & 0xffu);
-        if (i < 4) lo |= b << (8 * i);
-        else hi |= b << (8 * (i - 4));
+        const float y = v[i] * r;
+        b[i] = __float_as_uint(y + 12582912.0f);
     }
-    return make_uint2(lo, hi);
+    const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u) |
+                        __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);
+    const uint32_t hi = __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u) |
+                        __builtin_amdgcn_perm(b[7], b[6], 0x04000c0cu);
+    return zero ? make_uint2(0u, 0u) : make_uint2(lo, hi);
 }
+
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
@@ -241,7 +273,7 @@ k_quant_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
 // rows (runs of RG * 16 bytes).  Workgroups of 512 threads let two share a CU
 // at up to 128 registers a lane, so one group's loads overlap another's
 // reduction and stores.
-template <int CPL, bool NORM, int QMAX, int RG, int WPR>
+template <int CPL, bool NORM, int QMAX, int RG, int WPR, bool FULL>
 __global__ void __launch_bounds__(RG * WPR * 64)
 k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
                  const float *__restrict__ inv_s, double eps, int8_t *__restrict__ xq,
@@ -273,12 +305,12 @@ k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t l
 #pragma unroll
         for (int c = 0; c < ROUND; ++c) {
             const int64_t k = ((int64_t)((c0 + c) * WPR + h) * 64 + lane) * 8;
-            if (real && k < K) ch[c] = load8(row, inv_s, k);
+            if (FULL || (real && k < K)) ch[c] = load8(row, inv_s, k);
         }
 #pragma unroll
         for (int c = 0; c < ROUND; ++c) {
             const int64_t k = ((int64_t)((c0 + c) * WPR + h) * 64 + lane) * 8;
-            if (real && k < K) scale8<NORM>(ch[c], v[c0 + c], amax, &ss);
+            if (FULL || (real && k < K)) scale8<NORM>(ch[c], v[c0 + c], amax, &ss);
         }
     }
     amax = wave_max_u32(amax);
@@ -299,13 +331,18 @@ k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t l
     row_params<QMAX>(arow, scale, rr, zero);
     if (!NORM && real && h == 0 && lane == 0) x_scale[m] = scale;
     zero = zero || !real;
+    auto put = [&](auto clamp) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        const int64_t k = ((int64_t)(c * WPR + h) * 64 + lane) * 8;
-        if (k < pitch)   // codes past K (padding) are zero
-            *reinterpret_cast<uint2 *>(codes + r * pitch + k) =
-                (k < K) ? quant8<QMAX>(v[c], rr, zero) : make_uint2(0u, 0u);
-    }
+        for (int c = 0; c < CPL; ++c) {
+            const int64_t k = ((int64_t)(c * WPR + h) * 64 + lane) * 8;
+            if (FULL || k < pitch)   // codes past K (padding) are zero
+                *reinterpret_cast<uint2 *>(codes + r * pitch + k) =
+                    (FULL || k < K) ? quant8<QMAX, decltype(clamp)::value>(v[c], rr, zero)
+                                    : make_uint2(0u, 0u);
+        }
+    };
+    if (finite_r(rr)) put(std::false_type{});
+    else put(std::true_type{});
     // the normalized scale once the row's values are no longer held (the
     // row's partial sums added in wave order)
     if (NORM && real && h == 0 && lane == 0) {
@@ -386,14 +423,20 @@ k_quant_row1(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
     zero = zero || !real;
     const int64_t KW = (K + 63) >> 6;
     int8_t *base = xq + (((m >> 4) * KW) << 10) + (m & 15) * 16;
+    auto put = [&](auto clamp) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        const int64_t k = ((int64_t)c * 1024 + threadIdx.x) * 8;
-        if (k < KW * 64) {   // codes past K (padding) are zero
-            const uint2 q = (k < K) ? quant8<QMAX>(v[c], r, zero) : make_uint2(0u, 0u);
-            *reinterpret_cast<uint2 *>(base + ((k >> 6) << 10) + (((k >> 4) & 3) << 8) + (k & 15)) = q;
+        for (int c = 0; c < CPL; ++c) {
+            const int64_t k = ((int64_t)c * 1024 + threadIdx.x) * 8;
+            if (k < KW * 64) {   // codes past K (padding) are zero
+                const uint2 q = (k < K) ? quant8<QMAX, decltype(clamp)::value>(v[c], r, zero)
+                                        : make_uint2(0u, 0u);
+                *reinterpret_cast<uint2 *>(base + ((k >> 6) << 10) + (((k >> 4) & 3) << 8) +
+                                           (k & 15)) = q;
+            }
         }
-    }
+    };
+    if (finite_r(r)) put(std::false_type{});
+    else put(std::true_type{});
 }
 
 template <bool NORM, int QMAX>
@@ -413,10 +456,18 @@ hipError_t launch_rows(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, con
     // channels, 4 up to 16384
     const int64_t blocks = (M + 15) / 16;
     const int64_t KW = (K + 63) / 64;
+    // FULL: the lanes' chunks cover K exactly (no chunk past the row's end)
 #define SQ_QR(C, RG, WPR)                                                                        \
-    k_quant_rows_reg<C, NORM, QMAX, RG, WPR>                                                     \
-        <<<dim3((unsigned)(blocks * (16 / RG))), dim3(RG * WPR * 64), (size_t)RG * KW * 64, st>>>( \
-            x, M, K, ldx, inv_s, eps, xq, x_scale)
+    do {                                                                                         \
+        const dim3 g_((unsigned)(blocks * (16 / RG))), b_(RG * WPR * 64);                         \
+        const size_t lds_ = (size_t)RG * KW * 64;                                                \
+        if (K == (int64_t)(C) * (WPR) * 512)                                                     \
+            k_quant_rows_reg<C, NORM, QMAX, RG, WPR, true><<<g_, b_, lds_, st>>>(                 \
+                x, M, K, ldx, inv_s, eps, xq, x_scale);                                          \
+        else                                                                                     \
+            k_quant_rows_reg<C, NORM, QMAX, RG, WPR, false><<<g_, b_, lds_, st>>>(                \
+                x, M, K, ldx, inv_s, eps, xq, x_scale);                                          \
+    } while (0)
     if (K <= 8192) {
         const int64_t cpl = (K + 1023) / 1024;    // chunks of 8 per lane
         if (M > 512) {

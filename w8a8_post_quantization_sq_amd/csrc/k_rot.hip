@@ -155,9 +155,10 @@ k_quant4_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
             if (!zero && k < K) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
+                    // (a zero value's code is 0 also where r overflowed)
                     float c = __builtin_rintf(v[u][e] * r);
                     c = fminf(fmaxf(c, -7.0f), 7.0f);
-                    const uint32_t b = (uint32_t)(int)c & 0xffu;
+                    const uint32_t b = v[u][e] == 0.0f ? 0u : (uint32_t)(int)c & 0xffu;
                     if (e < 4) lo |= b << (8 * e);
                     else hi |= b << (8 * (e - 4));
                 }
@@ -301,14 +302,27 @@ k_quant4_rot_t(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx
     zero = zero || !real;
     // codes into the wave's (now free) transpose area, row-major (17 KiB >= K)
     int8_t *codes = reinterpret_cast<int8_t *>(tr);
+    if (finite_r(r)) {
 #pragma unroll
-    for (int j = 0; j < V / 64; ++j)
+        for (int j = 0; j < V / 64; ++j)
 #pragma unroll
-        for (int h = 0; h < 64; ++h) {
-            // |v r| <= 7 (1 + 2^-23)^2 < 7.5: no clamp needed
-            const float c = __builtin_rintf(v[64 * j + h] * r);
-            codes[h * V + 64 * j + lane] = zero ? (int8_t)0 : (int8_t)(int)c;
-        }
+            for (int h = 0; h < 64; ++h) {
+                // |v r| <= 7 (1 + 2^-23)^2 < 7.5: no clamp needed
+                const float c = __builtin_rintf(v[64 * j + h] * r);
+                codes[h * V + 64 * j + lane] = zero ? (int8_t)0 : (int8_t)(int)c;
+            }
+    } else {
+        // r overflowed (a maximum below 7 / FLT_MAX): v r is +-inf, clamped to
+        // +-7, and a zero value's code is 0
+#pragma unroll
+        for (int j = 0; j < V / 64; ++j)
+#pragma unroll
+            for (int h = 0; h < 64; ++h) {
+                const float x = v[64 * j + h];
+                codes[h * V + 64 * j + lane] =
+                    zero ? (int8_t)0 : (int8_t)(x > 0.0f ? 7 : (x < 0.0f ? -7 : 0));
+            }
+    }
     __syncthreads();
     const int64_t KW = K >> 6;
     const int64_t rb = m0 >> 4;
@@ -432,7 +446,8 @@ k_quant4_rot_row1(const uint16_t *__restrict__ x, int64_t M, int64_t ldx,
         for (int w = 0; w < WAVES; ++w) {
             float c = __builtin_rintf(u[w] * r);
             c = fminf(fmaxf(c, -7.0f), 7.0f);
-            codes[tid + 512 * w] = zero ? (int8_t)0 : (int8_t)(int)c;
+            // (a zero value's code is 0 also where r overflowed)
+            codes[tid + 512 * w] = (zero || u[w] == 0.0f) ? (int8_t)0 : (int8_t)(int)c;
         }
     }
     __syncthreads();

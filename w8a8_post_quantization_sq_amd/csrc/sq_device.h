@@ -21,6 +21,10 @@ __device__ __forceinline__ uint16_t f2h_bits(float f) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// A row's quantization multiplier r = QMAX / a is finite (false only where
+// the quotient overflowed: a maximum a below QMAX / FLT_MAX).
+__device__ __forceinline__ bool finite_r(float r) { return r <= 3.40282347e38f; }
+
 // Maximum over a 64-lane wavefront.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
