@@ -39,7 +39,8 @@
 namespace sq {
 
 // One 8-channel chunk: the raw fp16 values and their 1/s factors, loaded
-// together; scale8 then forms x * inv_s and folds the magnitudes into amax.
+// together; scale8 then forms x * inv_s and folds the magnitudes into a
+// running maximum.
 // Callers issue the loads of all their chunks before scaling any, so the
 // loads are in flight together (a load followed at once by its use makes
 // the compiler wait for each one in turn).
@@ -57,9 +58,33 @@ __device__ __forceinline__ Chunk load8(const uint16_t *__restrict__ x,
     return ch;
 }
 
+// Running maximum of |v| as float bits (magnitude bits order like
+// magnitudes, NaN above +inf), kept as two maxima of the raw bits so each
+// value costs one integer max and no sign masking: the unsigned maximum
+// holds the largest negative magnitude (sign bit set) whenever a negative
+// value was seen, else the largest positive one; the signed maximum holds
+// the largest positive magnitude (negative values are negative integers).
+struct AbsMax {
+    uint32_t u = 0;
+    int32_t i = 0;
+    __device__ __forceinline__ void add(float v) {
+        const uint32_t b = __float_as_uint(v);
+        u = u > b ? u : b;
+        i = i > (int32_t)b ? i : (int32_t)b;
+    }
+    __device__ __forceinline__ uint32_t bits() const {
+        const uint32_t n = u & 0x7fffffffu;
+        return n > (uint32_t)i ? n : (uint32_t)i;      // i >= 0
+    }
+};
+
+// x * inv_s for the 8 values of a chunk, each as fma(float(x), inv_s, +0):
+// the compiler makes it one v_fma_mix_f32, which widens the fp16 operand
+// inside the instruction.  The +0 addend changes no product except the sign
+// of a zero (-0 becomes +0), which neither the codes nor |x * inv_s| see.
 // With NORM, also adds the chunk's squares (exact in float) to ss in double.
 template <bool NORM = false>
-__device__ __forceinline__ void scale8(const Chunk &ch, float v[8], uint32_t &amax,
+__device__ __forceinline__ void scale8(const Chunk &ch, float v[8], AbsMax &am,
                                        double *ss = nullptr) {
     const float sv[8] = {ch.s0.x, ch.s0.y, ch.s0.z, ch.s0.w, ch.s1.x, ch.s1.y, ch.s1.z, ch.s1.w};
     const uint32_t h[4] = {ch.raw.x, ch.raw.y, ch.raw.z, ch.raw.w};
@@ -67,55 +92,41 @@ __device__ __forceinline__ void scale8(const Chunk &ch, float v[8], uint32_t &am
     for (int i = 0; i < 4; ++i) {
         const float lo = h2f(h[i] & 0xffffu), hi = h2f(h[i] >> 16);
         if (NORM) {
-            *ss += (double)(lo * lo);
-            *ss += (double)(hi * hi);
+            *ss += (double)__builtin_fmaf(lo, lo, 0.0f);
+            *ss += (double)__builtin_fmaf(hi, hi, 0.0f);
         }
-        v[2 * i] = lo * sv[2 * i];
-        v[2 * i + 1] = hi * sv[2 * i + 1];
+        v[2 * i] = __builtin_fmaf(lo, sv[2 * i], 0.0f);
+        v[2 * i + 1] = __builtin_fmaf(hi, sv[2 * i + 1], 0.0f);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        // magnitude bits order like magnitudes; NaN sits above +inf
-        const uint32_t b = __float_as_uint(v[i]) & 0x7fffffffu;
-        amax = amax > b ? amax : b;
-    }
+    for (int i = 0; i < 8; ++i) am.add(v[i]);
 }
 
 // Codes of 8 values, clamp(rint(v * r), -QMAX, QMAX), zero codes for a row
-// with zero set.  CLAMP: as the definition writes it (rint, then the clamp),
-// for any multiplier: where r overflowed (a maximum below QMAX / FLT_MAX)
-// v * r is +-inf, which the clamp takes to +-QMAX, or NaN for v = 0, whose
-// code is 0 (the code 0 * r has for every finite r).
-// Otherwise with fewer instructions, for rows whose multiplier r is finite:
-// for |y| <= 2^22 the float sum y + 1.5 * 2^23 lies in [2^23, 2^24), where
-// the floats are exactly the integers, so its one rounding (to nearest, ties
-// to even) is rint(y), and the low byte of its bits is rint(y) mod 256, the
-// two's-complement code.  The clamp cannot act there: r = QMAX / a is a
-// correctly rounded quotient and every |v| <= a, so |v * r| <= QMAX (1 + 2^-24)
-// and rint gives at most QMAX.  (Callers take the clamped form for a row
-// whose r overflowed.)  v_perm_b32
-// gathers the low bytes: selector bytes 0..3 pick bytes of its second
-// operand, 4..7 of its first, 0x0c a zero byte.
-template <int QMAX, bool CLAMP = true>
+// with zero set.  For a finite multiplier r: for |y| <= 2^22 the float sum
+// y + 1.5 * 2^23 lies in [2^23, 2^24), where the floats are exactly the
+// integers, so its one rounding (to nearest, ties to even) is rint(y), and
+// the low byte of its bits is rint(y) mod 256, the two's-complement code.
+// The clamp cannot act: r = QMAX / a is a correctly rounded quotient and
+// every |v| <= a, so |v * r| <= QMAX (1 + 2^-24) and rint gives at most QMAX.
+// v_perm_b32 gathers the low bytes: selector bytes 0..3 pick bytes of its
+// second operand, 4..7 of its first, 0x0c a zero byte.
+// OVERFLOW: the form for a row whose r overflowed (a maximum below
+// QMAX / FLT_MAX): v * r is +-inf, which the clamp takes to +-QMAX, for
+// v != 0, and a zero value's code is 0 (the code 0 * r has for every
+// finite r).
+template <int QMAX, bool OVERFLOW = false>
 __device__ __forceinline__ uint2 quant8(const float v[8], float r, bool zero) {
 #pragma clang fp contract(off)
-    if (CLAMP) {
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float q = __builtin_rintf(v[i] * r);
-            q = fminf(fmaxf(q, -(float)QMAX), (float)QMAX);
-            const uint32_t b = (zero || v[i] == 0.0f) ? 0u : ((uint32_t)(int)q & 0xffu);
-            if (i < 4) lo |= b << (8 * i);
-            else hi |= b << (8 * (i - 4));
-        }
-        return make_uint2(lo, hi);
-    }
     uint32_t b[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float y = v[i] * r;
-        b[i] = __float_as_uint(y + 12582912.0f);
+        if (OVERFLOW) {
+            b[i] = v[i] > 0.0f ? (uint32_t)QMAX : (v[i] < 0.0f ? (uint32_t)(256 - QMAX) : 0u);
+        } else {
+            const float y = v[i] * r;
+            b[i] = __float_as_uint(y + 12582912.0f);
+        }
     }
     const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u) |
                         __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);
@@ -123,7 +134,6 @@ __device__ __forceinline__ uint2 quant8(const float v[8], float r, bool zero) {
                         __builtin_amdgcn_perm(b[7], b[6], 0x04000c0cu);
     return zero ? make_uint2(0u, 0u) : make_uint2(lo, hi);
 }
-
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
@@ -184,7 +194,7 @@ k_quant_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
     const int64_t KW = (K + 63) >> 6;
     {
         const int64_t m = m0 + wave;
-        uint32_t amax = 0;
+        AbsMax am;
         double ss = 0.0;
         if (m < M) {
             const uint16_t *row = x + m * ldx;
@@ -197,11 +207,11 @@ k_quant_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     float v[8];
-                    if (c0 + u * 512 < K) scale8<NORM>(ch[u], v, amax, &ss);
+                    if (c0 + u * 512 < K) scale8<NORM>(ch[u], v, am, &ss);
                 }
             }
         }
-        amax = wave_max_u32(amax);
+        const uint32_t amax = wave_max_u32(am.bits());
         if (NORM) ss = wave_sum_f64(ss);
         float scale, r;
         bool zero;
@@ -225,7 +235,7 @@ k_quant_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
     const uint16_t *row = x + (m0 + r) * ldx;
     for (int64_t p0 = threadIdx.x; p0 < pieces; p0 += 4 * 512) {
         float v[4][16];
-        uint32_t dummy = 0;
+        AbsMax dummy;
         Chunk ch[4][2];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {   // all loads of 4 pieces first
@@ -254,8 +264,14 @@ k_quant_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
             const int64_t k = kw * 64 + q * 16;
             uint4 out = make_uint4(0u, 0u, 0u, 0u);
             if (!skip && k < K) {
-                const uint2 a = quant8<QMAX>(&v[u][0], rr, false);
-                const uint2 b = quant8<QMAX>(&v[u][8], rr, false);
+                uint2 a, b;
+                if (finite_r(rr)) {
+                    a = quant8<QMAX>(&v[u][0], rr, false);
+                    b = quant8<QMAX>(&v[u][8], rr, false);
+                } else {
+                    a = quant8<QMAX, true>(&v[u][0], rr, false);
+                    b = quant8<QMAX, true>(&v[u][8], rr, false);
+                }
                 out = make_uint4(a.x, a.y, b.x, b.y);
             }
             // piece (window kw, quarter q, row half + r) of the packed row block
@@ -293,7 +309,7 @@ k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t l
     const bool real = m < M;
     const uint16_t *row = x + (real ? m : 0) * ldx;
     float v[CPL][8];
-    uint32_t amax = 0;
+    AbsMax am;
     double ss = 0.0;
     // Every load of the row first; with the sum of squares at 8 chunks per
     // lane that needs more than the 128 registers a lane has here, so there
@@ -310,10 +326,10 @@ k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t l
 #pragma unroll
         for (int c = 0; c < ROUND; ++c) {
             const int64_t k = ((int64_t)((c0 + c) * WPR + h) * 64 + lane) * 8;
-            if (FULL || (real && k < K)) scale8<NORM>(ch[c], v[c0 + c], amax, &ss);
+            if (FULL || (real && k < K)) scale8<NORM>(ch[c], v[c0 + c], am, &ss);
         }
     }
-    amax = wave_max_u32(amax);
+    const uint32_t amax = wave_max_u32(am.bits());
     if (NORM) ss = wave_sum_f64(ss);
     if (lane == 0) {
         s_max[wave] = amax;
@@ -331,13 +347,13 @@ k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t l
     row_params<QMAX>(arow, scale, rr, zero);
     if (!NORM && real && h == 0 && lane == 0) x_scale[m] = scale;
     zero = zero || !real;
-    auto put = [&](auto clamp) {
+    auto put = [&](auto overflow) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             const int64_t k = ((int64_t)(c * WPR + h) * 64 + lane) * 8;
             if (FULL || k < pitch)   // codes past K (padding) are zero
                 *reinterpret_cast<uint2 *>(codes + r * pitch + k) =
-                    (FULL || k < K) ? quant8<QMAX, decltype(clamp)::value>(v[c], rr, zero)
+                    (FULL || k < K) ? quant8<QMAX, decltype(overflow)::value>(v[c], rr, zero)
                                     : make_uint2(0u, 0u);
         }
     };
@@ -388,7 +404,7 @@ k_quant_row1(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
     const bool real = m < M;
     const uint16_t *row = x + (real ? m : 0) * ldx;
     float v[CPL][8];
-    uint32_t amax = 0;
+    AbsMax am;
     double ss = 0.0;
     Chunk ch[CPL];
 #pragma unroll
@@ -399,9 +415,9 @@ k_quant_row1(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
         const int64_t k = ((int64_t)c * 1024 + threadIdx.x) * 8;
-        if (real && k < K) scale8<NORM>(ch[c], v[c], amax, &ss);
+        if (real && k < K) scale8<NORM>(ch[c], v[c], am, &ss);
     }
-    amax = wave_max_u32(amax);
+    const uint32_t amax = wave_max_u32(am.bits());
     if (NORM) ss = wave_sum_f64(ss);
     if (lane == 0) {
         s_max[wave] = amax;
@@ -423,12 +439,12 @@ k_quant_row1(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
     zero = zero || !real;
     const int64_t KW = (K + 63) >> 6;
     int8_t *base = xq + (((m >> 4) * KW) << 10) + (m & 15) * 16;
-    auto put = [&](auto clamp) {
+    auto put = [&](auto overflow) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             const int64_t k = ((int64_t)c * 1024 + threadIdx.x) * 8;
             if (k < KW * 64) {   // codes past K (padding) are zero
-                const uint2 q = (k < K) ? quant8<QMAX, decltype(clamp)::value>(v[c], r, zero)
+                const uint2 q = (k < K) ? quant8<QMAX, decltype(overflow)::value>(v[c], r, zero)
                                         : make_uint2(0u, 0u);
                 *reinterpret_cast<uint2 *>(base + ((k >> 6) << 10) + (((k >> 4) & 3) << 8) +
                                            (k & 15)) = q;
