@@ -58,26 +58,6 @@ __device__ __forceinline__ Chunk load8(const uint16_t *__restrict__ x,
     return ch;
 }
 
-// Running maximum of |v| as float bits (magnitude bits order like
-// magnitudes, NaN above +inf), kept as two maxima of the raw bits so each
-// value costs one integer max and no sign masking: the unsigned maximum
-// holds the largest negative magnitude (sign bit set) whenever a negative
-// value was seen, else the largest positive one; the signed maximum holds
-// the largest positive magnitude (negative values are negative integers).
-struct AbsMax {
-    uint32_t u = 0;
-    int32_t i = 0;
-    __device__ __forceinline__ void add(float v) {
-        const uint32_t b = __float_as_uint(v);
-        u = u > b ? u : b;
-        i = i > (int32_t)b ? i : (int32_t)b;
-    }
-    __device__ __forceinline__ uint32_t bits() const {
-        const uint32_t n = u & 0x7fffffffu;
-        return n > (uint32_t)i ? n : (uint32_t)i;      // i >= 0
-    }
-};
-
 // x * inv_s for the 8 values of a chunk, each as fma(float(x), inv_s, +0):
 // the compiler makes it one v_fma_mix_f32, which widens the fp16 operand
 // inside the instruction.  The +0 addend changes no product except the sign

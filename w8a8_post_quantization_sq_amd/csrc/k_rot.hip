@@ -234,8 +234,11 @@ k_quant4_rot_t(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx
                                 f1[i].x, f1[i].y, f1[i].z, f1[i].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                v[(c0 + i) * 8 + 2 * e] = h2f(h[e] & 0xffffu) * f[2 * e];
-                v[(c0 + i) * 8 + 2 * e + 1] = h2f(h[e] >> 16) * f[2 * e + 1];
+                // fma(float(x), mult, +0): one v_fma_mix_f32, equal to the
+                // product but for the sign of a zero, which no code or
+                // magnitude below sees
+                v[(c0 + i) * 8 + 2 * e] = __builtin_fmaf(h2f(h[e] & 0xffffu), f[2 * e], 0.0f);
+                v[(c0 + i) * 8 + 2 * e + 1] = __builtin_fmaf(h2f(h[e] >> 16), f[2 * e + 1], 0.0f);
             }
         }
     }
@@ -280,13 +283,10 @@ k_quant4_rot_t(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx
                     v[64 * j + h + hb] = a - b;
                 }
 
-    uint32_t amax = 0;
+    AbsMax am;
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-        const uint32_t b = __float_as_uint(v[i]) & 0x7fffffffu;
-        amax = amax > b ? amax : b;
-    }
-    amax = wave_max_u32(amax);
+    for (int i = 0; i < V; ++i) am.add(v[i]);
+    const uint32_t amax = wave_max_u32(am.bits());
     float r = 0.0f;
     bool zero = true;
     if (amax >= 0x7f800000u) {
@@ -302,14 +302,23 @@ k_quant4_rot_t(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx
     zero = zero || !real;
     // codes into the wave's (now free) transpose area, row-major (17 KiB >= K)
     int8_t *codes = reinterpret_cast<int8_t *>(tr);
-    if (finite_r(r)) {
+    if (zero) {
+#pragma unroll
+        for (int j = 0; j < V / 64; ++j)
+#pragma unroll
+            for (int h = 0; h < 64; ++h) codes[h * V + 64 * j + lane] = 0;
+    } else if (finite_r(r)) {
+        // |v r| <= 7 (1 + 2^-23)^2 < 7.5: no clamp needed.  rint by one
+        // float add: y + 1.5 * 2^23 lies in [2^23, 2^24), where the floats are
+        // the integers, so its rounding (ties to even) is rint(y) and the low
+        // byte of its bits, which the byte store takes, is the code
+#pragma clang fp contract(off)
 #pragma unroll
         for (int j = 0; j < V / 64; ++j)
 #pragma unroll
             for (int h = 0; h < 64; ++h) {
-                // |v r| <= 7 (1 + 2^-23)^2 < 7.5: no clamp needed
-                const float c = __builtin_rintf(v[64 * j + h] * r);
-                codes[h * V + 64 * j + lane] = zero ? (int8_t)0 : (int8_t)(int)c;
+                const float y = v[64 * j + h] * r;
+                codes[h * V + 64 * j + lane] = (int8_t)__float_as_uint(y + 12582912.0f);
             }
     } else {
         // r overflowed (a maximum below 7 / FLT_MAX): v r is +-inf, clamped to
@@ -319,8 +328,7 @@ k_quant4_rot_t(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx
 #pragma unroll
             for (int h = 0; h < 64; ++h) {
                 const float x = v[64 * j + h];
-                codes[h * V + 64 * j + lane] =
-                    zero ? (int8_t)0 : (int8_t)(x > 0.0f ? 7 : (x < 0.0f ? -7 : 0));
+                codes[h * V + 64 * j + lane] = (int8_t)(x > 0.0f ? 7 : (x < 0.0f ? -7 : 0));
             }
     }
     __syncthreads();

@@ -25,6 +25,26 @@ __device__ __forceinline__ uint16_t f2h_bits(float f) {
 // the quotient overflowed: a maximum a below QMAX / FLT_MAX).
 __device__ __forceinline__ bool finite_r(float r) { return r <= 3.40282347e38f; }
 
+// Running maximum of |v| as float bits (magnitude bits order like
+// magnitudes, NaN above +inf), kept as two maxima of the raw bits so each
+// value costs one integer max and no sign masking: the unsigned maximum
+// holds the largest negative magnitude (sign bit set) whenever a negative
+// value was seen, else the largest positive one; the signed maximum holds
+// the largest positive magnitude (negative values are negative integers).
+struct AbsMax {
+    uint32_t u = 0;
+    int32_t i = 0;
+    __device__ __forceinline__ void add(float v) {
+        const uint32_t b = __float_as_uint(v);
+        u = u > b ? u : b;
+        i = i > (int32_t)b ? i : (int32_t)b;
+    }
+    __device__ __forceinline__ uint32_t bits() const {
+        const uint32_t n = u & 0x7fffffffu;
+        return n > (uint32_t)i ? n : (uint32_t)i;      // i >= 0
+    }
+};
+
 // Maximum over a 64-lane wavefront.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
