@@ -44,10 +44,12 @@ _f16p1 = np.ctypeslib.ndpointer(dtype=np.uint16, ndim=1, flags="C_CONTIGUOUS")
 
 
 def lib():
-    """Loads the compiled oracle, building it first only if it is missing."""
+    """Loads the compiled oracle, building it first only if it is missing
+    (SQ_ORACLE_LIB names another build of the same source, e.g. the
+    sanitized one the tests run the pins against)."""
     global _LIB
     if _LIB is None:
-        path = _build.LIB_PATH
+        path = os.environ.get("SQ_ORACLE_LIB") or _build.LIB_PATH
         if not os.path.exists(path):
             _build.build()
         L = ctypes.CDLL(path)
