@@ -129,7 +129,9 @@ sq_status sq_calibrate_absmax(const void *x_cal_f16, int64_t T, int64_t K, int64
  *   Wt[j][n]   = float(W[j][n]) * s_j
  *   w_scale[n] = max_j |Wt[j][n]| / 127
  *   wq[n][j]   = clamp(rint(Wt[j][n] * (127 / max_j|Wt[j][n]|)), -127, 127)
- * (an all-zero column gets scale 0 and codes 0).
+ * (an all-zero column gets scale 0 and codes 0; where 127 / max overflows, a
+ * column maximum below 127 / FLT_MAX from a caller's tiny smooth_in, nonzero
+ * values get +-127 and zeros 0).
  *
  *   w           fp16 [K][ldw], N output channels used per row
  *   act_absmax  float [K] from sq_calibrate_absmax; ignored when smooth_in != NULL
@@ -209,7 +211,10 @@ sq_status sq_smoothing_factors(const void *w_f16, int64_t K, int64_t N, int64_t 
  *   x_scale[m] = max_j |xt[j]| / 127
  *   xq[m][j]   = clamp(rint(xt[j] * (127 / max_j|xt[j]|)), -127, 127)
  * An all-zero row gets scale 0 and codes 0; a row with a non-finite xt gets
- * scale NaN and codes 0 (so its outputs are NaN).
+ * scale NaN and codes 0 (so its outputs are NaN).  A row whose maximum is
+ * below 127 / FLT_MAX (possible only with a caller's 1/s far below the fold's
+ * range) makes the float 127 / max infinite: its nonzero values get +-127 and
+ * its zeros 0.
  *
  *   x           fp16 [M][ldx]
  *   inv_smooth  float [K] (inv_smooth_out of the fold)
@@ -254,8 +259,9 @@ sq_status sq_fold_norm_weight(const void *gamma_f16, int64_t K, const float *inv
  * square of an fp16 value is exact), so x_scale is within one float rounding
  * of its value for the exact sum.  The codes do not depend on rstd_m (a
  * positive per-token factor), so they are exactly sq_quant_act_per_token's
- * codes of h with inv_smooth = gamma_folded.  An all-zero row gets scale 0
- * and codes 0; a row with a non-finite xt gets scale NaN and codes 0.
+ * codes of h with inv_smooth = gamma_folded (the same rule for a row whose
+ * float 127 / max overflows).  An all-zero row gets scale 0 and codes 0; a row
+ * with a non-finite xt gets scale NaN and codes 0.
  *
  *   h             fp16 [M][ldh], the normalization's input (hidden state)
  *   gamma_folded  float [K] from sq_fold_norm_weight
@@ -299,7 +305,8 @@ int64_t sq_w4_workspace_bytes(int64_t K, int64_t N);
  *   w_scale[n] = (max_j |v_j| / 7) * (rotate ? 1/K : 1)
  *   wq[n][j]   = clamp(rint(v_j * (7 / max_j |v_j|)), -7, 7)
  * (products float(W) * s in float; a zero channel gets scale 0 and codes 0, a
- * non-finite value scale NaN and codes 0).
+ * non-finite value scale NaN and codes 0; where 7 / max overflows, nonzero
+ * values get +-7 and zeros 0).
  *   w          fp16 [K][ldw]
  *   smooth     float [K] (s from sq_smoothing_factors, or ones for S = I)
  *   wq4        packed 4-bit, sq_packed4_bytes(N, K) bytes, written, padding zero
@@ -318,7 +325,9 @@ sq_status sq_w4_fold_weights(const void *w_f16, int64_t K, int64_t N, int64_t ld
  * without H), then
  *   x_scale[m] = max_j |v_j| / 7
  *   xq[m][j]   = clamp(rint(v_j * (7 / max_j |v_j|)), -7, 7)
- * (all-zero token: scale 0, codes 0; a non-finite value: scale NaN, codes 0).
+ * (all-zero token: scale 0, codes 0; a non-finite value: scale NaN, codes 0;
+ * where 7 / max overflows, a maximum of at most 2^-126, nonzero values get +-7
+ * and zeros 0).
  *   x        fp16 [M][ldx]
  *   xq       packed int8, sq_packed_bytes(M, K) bytes, written, padding zero
  *   x_scale  float [M], written
