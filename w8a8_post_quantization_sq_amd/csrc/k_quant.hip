@@ -115,10 +115,32 @@ __device__ __forceinline__ uint2 quant8(const float v[8], float r, bool zero) {
     return zero ? make_uint2(0u, 0u) : make_uint2(lo, hi);
 }
 
+// A double moved between lanes by one DPP control (both halves; a lane whose
+// source is outside its row of 16 reads +0).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xf, 0xf, false);
+    const uint32_t hi =
+        (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xf, 0xf, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over a 64-lane wavefront (every lane active), returned to every lane,
+// in one fixed order: row shifts by 1, 2, 4 and 8 leave each row's sum in the
+// row's last lane, and the four row sums are added in row order.
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_f64<0x111>(v);    // row_shr:1
+    v += dpp_f64<0x112>(v);    // row_shr:2
+    v += dpp_f64<0x114>(v);    // row_shr:4
+    v += dpp_f64<0x118>(v);    // row_shr:8
+    auto lane_val = [](double x, int l) {
+        const uint64_t b = __builtin_bit_cast(uint64_t, x);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+        return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+    };
+    return ((lane_val(v, 15) + lane_val(v, 31)) + lane_val(v, 47)) + lane_val(v, 63);
 }
 
 // Turns the row maximum into (scale, multiplier, all-zero-codes flag).

@@ -45,14 +45,23 @@ struct AbsMax {
     }
 };
 
-// Maximum over a 64-lane wavefront.
+// Maximum over a 64-lane wavefront (every lane active), returned to every
+// lane.  DPP row shifts by 1, 2, 4 and 8 (a lane shifted in from outside its
+// row of 16 reads 0, the identity) leave each row's maximum in the row's last
+// lane; the four row maxima are read as scalars.  No LDS round trips, unlike
+// lane shuffles through ds_bpermute.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        uint32_t t = (uint32_t)__shfl_xor((int)v, o, 64);
-        v = v > t ? v : t;
-    }
-    return v;
+    auto umax = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+    // dpp_ctrl row_shr:n = 0x110 + n; all rows and banks; out-of-row lanes take old (0)
+    v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
+    v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));
+    v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
+    v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+    return umax(umax(r0, r1), umax(r2, r3));
 }
 
 // Lanes of one wave exchanging data through LDS: orders this lane's earlier
