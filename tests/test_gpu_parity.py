@@ -363,6 +363,10 @@ def test_quant_matches_oracle(sq, dev, orc, name):
                                     (70, 16, 16), (100, 4096, 4104), (513, 1040, 1040),
                                     (300, 11008, 11024), (520, 8208, 8208), (600, 16384, 16392),
                                     (130, 16400, 16400),
+                                    # above 512 tokens and K <= 8192: the 4-row column form, whole and
+                                    # ragged chunk columns, M not a multiple of 4 or 16, strided rows
+                                    (530, 2048, 2056), (1001, 4096, 4104), (777, 3088, 3088),
+                                    (2050, 8176, 8192), (600, 8192, 8192), (515, 16, 16),
                                     (5, 32784, 32784), (2, 40000, 40000), (1, 131056, 131056)])
 def test_quant_ragged_long_and_strided(sq, dev, orc, M, K, ld):
     x = W.random_f16(600 + K, M, ld, 2.0)

@@ -91,7 +91,8 @@ def test_a4_rotated_ragged_and_strided(sq, dev, orc, M, K, ld):
     check_a4(sq, dev, orc, xk, inv, True, f"M={M} K={K} ld={ld}", xv=T(x, dev)[:, :K])
 
 
-@pytest.mark.parametrize("M,K", [(17, 4112), (3, 48), (2, 8192), (300, 8192), (700, 4096)])
+@pytest.mark.parametrize("M,K", [(17, 4112), (3, 48), (2, 8192), (300, 8192), (700, 4096),
+                                 (900, 2064), (1030, 8192)])
 def test_a4_unrotated_any_width(sq, dev, orc, M, K):
     x = W.random_f16(950 + K, M, K, 3.0)
     inv = W.random_scales(951 + K, K, 0.05, 4.0)
