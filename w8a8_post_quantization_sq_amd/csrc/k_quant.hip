@@ -8,8 +8,10 @@
 //   xt = float(x) * inv_s[j];  a = max_j |xt|;  scale = a / 127;
 //   q  = clamp(rint(xt * (127 / a)), -127, 127)
 // The two divisions are IEEE-correct float divisions (the compiler's default,
-// no fast-math), the products single float multiplies, so the codes are the
-// ones the plain definition gives.
+// no fast-math) and each product one correctly rounded float operation (x *
+// inv_s as a mixed-precision fma with a +0 addend, x * r a multiply), and
+// rint is taken by a float addition whose rounding is exactly it (quant8),
+// so the codes are the ones the plain definition gives.
 //
 // The same kernels also serve the normalization in front of the layer with
 // 1/s folded into its weight (the fold into the preceding operation that the
@@ -174,7 +176,7 @@ __device__ __forceinline__ float norm_scale(uint32_t abits, double ss, int64_t K
 // Row-group kernel: a workgroup of 8 waves owns 8 consecutive token rows
 // (half a packed row block).
 //   pass 1: wave w streams row m0 + w once from HBM (16-byte loads) and
-//           reduces max |x * inv_s| with wave shuffles; lane 0 stores the
+//           reduces max |x * inv_s| across the wave (DPP); lane 0 stores the
 //           scale and keeps (multiplier, zero-row flag) in LDS;
 //   pass 2: the rows are now in L2; lane p of the group makes one 16-code piece
 //           (row p % 8, quarter (p / 8) % 4, window p / 32), so consecutive
@@ -285,7 +287,7 @@ k_quant_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
 // Register-resident variant for K <= 16384: RG rows per workgroup, WPR waves
 // per row (RG * WPR <= 16).  Every lane loads all its chunks of its row at
 // once (the only HBM read of X), keeps x * inv_s in registers through the row
-// reduction (wave shuffles, then the WPR waves of a row through LDS),
+// reduction (a DPP wave reduction, then the WPR waves of a row through LDS),
 // quantizes, and writes its codes into an LDS copy of the RG rows; the group
 // then leaves LDS as packed 16-byte pieces, consecutive lanes on consecutive
 // rows (runs of RG * 16 bytes).  Workgroups of 512 threads let two share a CU
@@ -388,7 +390,7 @@ k_quant_rows_reg(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t l
 
 // Decode-size batches (M <= 64): one token per workgroup of 1024 threads, one
 // (K <= 8192) or two chunks of 8 channels per lane, so a token's loads all go
-// out at once over 16 waves and each reduction is one wave shuffle plus one
+// out at once over 16 waves and each reduction is one DPP wave reduction plus one
 // LDS round (every thread folds the 16 wave results in the same order, so the
 // double sum of squares is the same everywhere).  Each lane writes its 8 codes
 // straight into the packed layout (half of a 16-byte piece); rows of the last
