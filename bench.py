@@ -508,6 +508,9 @@ def main():
     ap.add_argument("--full-steps", type=int, default=50,
                     help="steps of the separate pass over every row A1..A6 (calibrate, fold, "
                          "quantize, product) per batch (0: skip)")
+    ap.add_argument("--sweep-m", default="",
+                    help="comma-separated token counts: the layer on the step's weights at each "
+                         "(outside the step; empty: skip)")
     ap.add_argument("--graph-steps", type=int, default=400,
                     help="layers timed as replays of a HIP graph of 20 layers (0: skip)")
     ap.add_argument("--stage-steps", type=int, default=20,
@@ -787,6 +790,52 @@ def main():
                 "saved_bytes_per_batch": 4 * M * K}
         log(f"fused norm + quant {us[True]:.2f} us, plain quant {us[False]:.2f} us")
 
+    # The layer across token counts on the step's folded weights (outside the
+    # step; --sweep-m): quantization + product and the product alone, each
+    # as a run of launches between one event pair, X drawn like the step's.
+    sweep = None
+    if args.sweep_m:
+        sweep = {"what": f"serving layer on the {wl.name} weights (K {K}, N {N}) at other token "
+                         "counts, weights cache-resident", "points": []}
+        for ms in [int(v) for v in args.sweep_m.split(",") if v.strip()]:
+            xs_m = torch.from_numpy(workloads.generate(wl, m=ms, with_w=False).x).to(dev)
+            assert xs_m.shape == (ms, K)
+            xq_m = torch.empty(sq.packed_bytes(ms, K), dtype=torch.int8, device=dev)
+            xsc_m = torch.empty(ms, dtype=torch.float32, device=dev)
+            y_m = torch.empty((ms, N), dtype=torch.float16, device=dev)
+            n_launch = 10 if 2.0 * ms * N * K > 2e11 else 50
+
+            def run_m(quantize):
+                r = 0
+                if quantize:
+                    r |= L.sq_quant_act_per_token(xs_m.data_ptr(), ms, K, K, p["inv"],
+                                                  xq_m.data_ptr(), xsc_m.data_ptr(), hs)
+                r |= L.sq_w8a8_gemm(xq_m.data_ptr(), xsc_m.data_ptr(), p["wq"], p["wsc"], ms, N, K,
+                                    y_m.data_ptr(), N, sq.SQ_OUT_F16, hs)
+                if r:
+                    raise RuntimeError("sweep call failed")
+
+            t = {}
+            for quantize in (True, False, True, False):     # second round is the one kept
+                for _ in range(5):
+                    run_m(quantize)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(n_launch):
+                    run_m(quantize)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t[quantize] = e0.elapsed_time(e1) * 1e3 / n_launch
+            ops_m = 2.0 * ms * N * K
+            sweep["points"].append({"M": ms, "layer_us": round(t[True], 2),
+                                    "layer_tops": round(ops_m / (t[True] * 1e-6) / 1e12, 1),
+                                    "gemm_us": round(t[False], 2),
+                                    "gemm_tops": round(ops_m / (t[False] * 1e-6) / 1e12, 1)})
+            log(f"sweep M={ms}: layer {t[True]:.2f} us, product {t[False]:.2f} us")
+            del xs_m, xq_m, xsc_m, y_m
+        # the step's own codes again for what follows
+        L.sq_quant_act_per_token(p["x"], M, K, K, p["inv"], p["xq"], p["xsc"], hs)
+
     # Smooth Rotation at 4 bits (outside the step): the per-token quantizer
     # with the Hadamard transform against the same quantizer without it, on
     # the same batch and factors; the product takes their codes unchanged.
@@ -876,6 +925,7 @@ def main():
         "decode": decode,
         "norm_fold": norm,
         "rotation_w4": rot,
+        "sweep": sweep,
         "cpu_baseline": None,
     }
     if args.attainable:

@@ -458,6 +458,10 @@ GEMM_SHAPES = [(1, 1, 16), (3, 5, 48), (17, 100, 80), (40, 100, 320), (49, 1000,
                # two row blocks, a ragged last window
                (16, 28672, 2112), (32, 28672, 2112), (25, 28672, 1040),
                (64, 70, 4096), (65, 33, 64), (100, 200, 64), (128, 128, 4096),
+               # mid-size batches (at most 64 tiles of 256 x 128): 64-token groups of the
+               # multi-block kernel, 2 and 4 channel blocks, ragged tokens and channels
+               (512, 4096, 1024), (200, 1000, 4160), (1000, 128, 256), (320, 2048, 512),
+               (65, 4096, 2048),
                (130, 129, 1040), (256, 384, 2048), (1, 28672, 128), (16, 300, 8192), (513, 77, 112),
                # 256 x 256 tiles (their rounds of 256 CUs beat the 256 x 128 ones'): ragged M,
                # N (a partial row block) and K, and a full-width one

@@ -561,7 +561,9 @@ k_gemm_skinny(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
 // products, and 4-bit codes are widened just before the matrix instruction.
 // NW waves per workgroup take interleaved k windows; with 7 blocks (one
 // workgroup per CU) 8 waves of half the batch each keep two waves on every
-// SIMD, so one wave's products overlap another's loads.
+// SIMD, so one wave's products overlap another's loads.  blockIdx.y picks the
+// workgroup's MB row blocks of tokens (one group at decode sizes; 64-token
+// groups for the mid-size batches below).
 template <int MB, bool F16OUT, bool W4, int CB, int NW = 4>
 __global__ void __launch_bounds__(64 * NW)
 k_gemm_skinny_cb(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
@@ -573,11 +575,13 @@ k_gemm_skinny_cb(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int nb0 = blockIdx.x * CB;             // first 16-channel block
+    const int m0 = blockIdx.y * MB * 16;         // first token of this workgroup's rows
     const int KW = (K + 63) >> 6;
-    const int rbx = (M + 15) >> 4;
+    const int rbx = min(MB, ((M + 15) >> 4) - (m0 >> 4));   // row blocks present
     const int rbw = (N + 15) >> 4;
     const int ncb = rbw - nb0 < CB ? rbw - nb0 : CB;   // blocks present
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (int64_t)rbx * KW * T_FRAG);
+    const __amdgpu_buffer_rsrc_t rx =
+        make_rsrc(X + (int64_t)(m0 >> 4) * KW * T_FRAG, (int64_t)rbx * KW * T_FRAG);
     constexpr int WF = W4 ? T_FRAG / 2 : T_FRAG;           // weight bytes per fragment
     const __amdgpu_buffer_rsrc_t rw =
         make_rsrc(W + (int64_t)nb0 * KW * WF, (int64_t)ncb * KW * WF);
@@ -586,7 +590,7 @@ k_gemm_skinny_cb(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
     // 15 of 16 lanes), which keeps the activations' L2 traffic to the real rows.
     bool xrow[MB];
 #pragma unroll
-    for (int b = 0; b < MB; ++b) xrow[b] = b * 16 + (lane & 15) < M;
+    for (int b = 0; b < MB; ++b) xrow[b] = m0 + b * 16 + (lane & 15) < M;
 
     v4i acc[CB][MB];
 #pragma unroll
@@ -665,7 +669,7 @@ k_gemm_skinny_cb(const int8_t *__restrict__ X, const int8_t *__restrict__ W,
                 acc[c][b][3] += p[3];
             }
             if (c >= ncb) continue;
-            const int m = b * 16 + (lane & 15);
+            const int m = m0 + b * 16 + (lane & 15);
             const float xsm = (F16OUT && m < M) ? xs[m] : 0.0f;
             store4<F16OUT>(Y, ldy, (vec_ok & 1) != 0, m, (nb0 + c) * 16 + (lane >> 4) * 4, M, N,
                            acc[c][b], xsm, ws);
@@ -936,6 +940,36 @@ hipError_t launch_gemm_any(const int8_t *xq, const float *x_scale, const int8_t 
                          (!f16 || ((uintptr_t)w_scale % 16) == 0)) ? 1 : 0) |
                        ((f16 && (ldy % 8) == 0 && ((uintptr_t)y % 16) == 0) ? 2 : 0);
     const int m = (int)M, n = (int)N, k = (int)K;
+    // Mid-size batches whose 256 x 128 tiles would occupy at most a quarter of
+    // the 256 CUs (e.g. 65..512 tokens against 4096 channels): the multi-block
+    // decode kernel over 64-token groups, each workgroup's 4 waves splitting K,
+    // which spreads the same work over many more CUs (measured 21.6 -> 9.0 us
+    // at 128 x 4096 x 4096, 49.8 -> 16.3 at 128 tokens, K 11008, N 4096; the
+    // tiles win from about 96 of them on).  2 channel blocks per workgroup
+    // while that keeps the workgroup count near one per CU, else 4.
+    if (!W4 && M > 64 &&
+        (int64_t)((m + T_BM - 1) / T_BM) * ((n + T_BN - 1) / T_BN) <= 64) {
+        const int64_t nblk = (n + 15) / 16;
+        const int64_t mt = (m + 63) / 64;
+        const bool two = ((nblk + 1) / 2) * mt <= 256;
+        const dim3 grid((unsigned)((nblk + (two ? 1 : 3)) / (two ? 2 : 4)), (unsigned)mt);
+        if (f16) {
+            if (two)
+                k_gemm_skinny_cb<4, true, false, 2><<<grid, dim3(256), 0, st>>>(
+                    xq, wq, x_scale, w_scale, m, n, k, y, ldy, vec_ok);
+            else
+                k_gemm_skinny_cb<4, true, false, 4><<<grid, dim3(256), 0, st>>>(
+                    xq, wq, x_scale, w_scale, m, n, k, y, ldy, vec_ok);
+        } else {
+            if (two)
+                k_gemm_skinny_cb<4, false, false, 2><<<grid, dim3(256), 0, st>>>(
+                    xq, wq, x_scale, w_scale, m, n, k, y, ldy, vec_ok);
+            else
+                k_gemm_skinny_cb<4, false, false, 4><<<grid, dim3(256), 0, st>>>(
+                    xq, wq, x_scale, w_scale, m, n, k, y, ldy, vec_ok);
+        }
+        return hipGetLastError();
+    }
     if (M > 64) {
         const int tiles_m = (m + T_BM - 1) / T_BM;
         // 256 x 256 tiles (8-bit weights) where their rounds of 256 CUs cost
