@@ -113,6 +113,7 @@ def test_rmsnorm_quant_matches_oracle(sq, dev, orc, name, m):
                                     (2, 8208, 8208), (64, 16384, 16384), (65, 8192, 8192),
                                     (100, 4096, 4104), (600, 11008, 11008), (520, 16384, 16392),
                                     (1001, 4096, 4104), (777, 6160, 6160), (2050, 8192, 8192),
+                                    (300, 12288, 12288), (100, 9008, 9016), (900, 12288, 12296),
                                     (5, 32784, 32784), (1, 131056, 131056)])
 def test_rmsnorm_quant_ragged_long_and_strided(sq, dev, orc, M, K, ld):
     h = W.random_f16(800 + K, M, ld, 3.0)

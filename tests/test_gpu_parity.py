@@ -355,8 +355,9 @@ def test_quant_matches_oracle(sq, dev, orc, name):
 
 # up to 64 tokens and K <= 16384 the one-token-per-workgroup form runs (one or
 # two chunks per lane); beyond 64 tokens the row-group form (2 rows per
-# workgroup up to 512 tokens, 4 beyond; 2 waves per row up to K = 8192, 4 up
-# to 16384), and past K = 16384 the 8-row streaming form
+# workgroup up to 512 tokens, 4 beyond; 2 waves per row up to K = 8192; up to
+# 12288, 3 waves (8 waves of 3 chunks at most 512 tokens); 4 up to 16384), and
+# past K = 16384 the 8-row streaming form
 @pytest.mark.parametrize("M,K,ld", [(1, 16, 16), (3, 48, 56), (17, 2064, 2064), (2, 4112, 4128),
                                     (4, 11008, 11024), (64, 16384, 16384), (33, 8192, 8192),
                                     (65, 4096, 4096), (64, 16400, 16400),
@@ -367,6 +368,9 @@ def test_quant_matches_oracle(sq, dev, orc, name):
                                     # ragged chunk columns, M not a multiple of 4 or 16, strided rows
                                     (530, 2048, 2056), (1001, 4096, 4104), (777, 3088, 3088),
                                     (2050, 8176, 8192), (600, 8192, 8192), (515, 16, 16),
+                                    # 8193..12288 channels: ragged and exact cover, both group shapes
+                                    (700, 11008, 11024), (513, 9008, 9008), (600, 12288, 12288),
+                                    (200, 12288, 12296), (90, 8208, 8208),
                                     (5, 32784, 32784), (2, 40000, 40000), (1, 131056, 131056)])
 def test_quant_ragged_long_and_strided(sq, dev, orc, M, K, ld):
     x = W.random_f16(600 + K, M, ld, 2.0)

@@ -473,7 +473,9 @@ hipError_t launch_rows(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, con
     }
     // every row of the padded row blocks: 4 rows per workgroup, or 2 where
     // that leaves too few workgroups for the CUs; 2 waves per row up to 8192
-    // channels, 4 up to 16384
+    // channels; up to 12288, 3 waves of 8 chunks (a quarter fewer idle lanes
+    // than 4 waves at K = 11008), or on small batches 8 waves of 3 chunks;
+    // 4 waves up to 16384
     const int64_t blocks = (M + 15) / 16;
     const int64_t KW = (K + 63) / 64;
     // FULL: the lanes' chunks cover K exactly (no chunk past the row's end)
@@ -501,6 +503,9 @@ hipError_t launch_rows(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, con
             else if (cpl <= 4) SQ_QR(4, 2, 2);
             else SQ_QR(8, 2, 2);
         }
+    } else if (K <= 12288) {
+        if (M > 512) SQ_QR(8, 4, 3);
+        else SQ_QR(3, 2, 8);
     } else if (K <= 16384) {
         if (M > 512) SQ_QR(8, 4, 4);
         else SQ_QR(8, 2, 4);
