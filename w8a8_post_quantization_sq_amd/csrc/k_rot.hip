@@ -195,11 +195,24 @@ k_quant4_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
 constexpr int RT = 4;     // rows per workgroup
 constexpr int TP = 68;    // padded floats per transpose row
 
-template <int V>
-__global__ void __launch_bounds__(256)
+// STAGED (K = 4096): the inputs fetched in line order.  A load whose 64
+// lanes each read 16 bytes of another 128-byte line costs the vector memory
+// path a tag lookup per lane; the direct form issues 24 such loads per wave
+// (its row and its factors), and they, not HBM, held each wave up for about
+// half its time.  Staged, 8 consecutive lanes read one line, and the wave
+// passes the data through its own transpose area into lane order: first its
+// copy of the factors (16 KiB), then the row (8 KiB).  Both copies place
+// 16-byte chunk c at slot c ^ ((c >> S) & 15) (S = 4 for the factors, 3 for
+// the row), so the line-order writes and the lane-order reads alike touch 16
+// different 16-byte bank groups per 16 lanes (8 per 8).
+__device__ __forceinline__ int swz(int c, int s) { return c ^ ((c >> s) & 15); }
+
+template <int V, bool STAGED = false>
+__global__ void __launch_bounds__(64 * RT)
 k_quant4_rot_t(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
                const float *__restrict__ mult, float post, int8_t *__restrict__ q,
                float *__restrict__ scale) {
+    static_assert(!STAGED || V == 64, "the staged form is for K = 4096");
     extern __shared__ __align__(16) float tr_all[];     // [RT][64][TP]
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -210,35 +223,80 @@ k_quant4_rot_t(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx
     float *tr = tr_all + wave * 64 * TP;
 
     float v[V];
-    const int64_t k0 = (int64_t)lane * V;
+    if constexpr (STAGED) {
+        // 16-byte chunks in line order: c = 64 t + lane (the row: elements
+        // 8c .. 8c + 7; the factors: 4c .. 4c + 3)
+        uint4 raw[V / 8];
+        float4 fl[V / 4];
 #pragma unroll
-    for (int c0 = 0; c0 < V / 8; c0 += 4) {     // loads in rounds of 4 chunks of 8
-        uint4 raw[4];
-        float4 f0[4], f1[4];
+        for (int t = 0; t < V / 8; ++t)
+            raw[t] = real ? *reinterpret_cast<const uint4 *>(row + (t * 64 + lane) * 8)
+                          : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t k = k0 + (c0 + i) * 8;
-            if (real) {
-                raw[i] = *reinterpret_cast<const uint4 *>(row + k);
-                f0[i] = *reinterpret_cast<const float4 *>(mult + k);
-                f1[i] = *reinterpret_cast<const float4 *>(mult + k + 4);
-            } else {
-                raw[i] = make_uint4(0u, 0u, 0u, 0u);
-                f0[i] = f1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+        for (int t = 0; t < V / 4; ++t)
+            fl[t] = *reinterpret_cast<const float4 *>(mult + (t * 64 + lane) * 4);
+        float4 *fs = reinterpret_cast<float4 *>(tr);
+#pragma unroll
+        for (int t = 0; t < V / 4; ++t) fs[swz(t * 64 + lane, 4)] = fl[t];
+        wave_lds_exchange();
+        float f[V];                                       // the lane's factors, k = V lane + i
+#pragma unroll
+        for (int i = 0; i < V / 4; ++i) {
+            const float4 g = fs[swz(lane * (V / 4) + i, 4)];
+            f[4 * i] = g.x;
+            f[4 * i + 1] = g.y;
+            f[4 * i + 2] = g.z;
+            f[4 * i + 3] = g.w;
         }
+        wave_lds_exchange();                              // the row now goes over the factors
+        uint4 *xs = reinterpret_cast<uint4 *>(tr);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t h[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-            const float f[8] = {f0[i].x, f0[i].y, f0[i].z, f0[i].w,
-                                f1[i].x, f1[i].y, f1[i].z, f1[i].w};
+        for (int t = 0; t < V / 8; ++t) xs[swz(t * 64 + lane, 3)] = raw[t];
+        wave_lds_exchange();
+#pragma unroll
+        for (int j = 0; j < V / 8; ++j) {
+            const uint4 r4 = xs[swz(lane * (V / 8) + j, 3)];      // elements V lane + 8j ..
+            const uint32_t h[4] = {r4.x, r4.y, r4.z, r4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                // fma(float(x), mult, +0): one v_fma_mix_f32, equal to the
-                // product but for the sign of a zero, which no code or
-                // magnitude below sees
-                v[(c0 + i) * 8 + 2 * e] = __builtin_fmaf(h2f(h[e] & 0xffffu), f[2 * e], 0.0f);
-                v[(c0 + i) * 8 + 2 * e + 1] = __builtin_fmaf(h2f(h[e] >> 16), f[2 * e + 1], 0.0f);
+                v[8 * j + 2 * e] = __builtin_fmaf(h2f(h[e] & 0xffffu), f[8 * j + 2 * e], 0.0f);
+                v[8 * j + 2 * e + 1] =
+                    __builtin_fmaf(h2f(h[e] >> 16), f[8 * j + 2 * e + 1], 0.0f);
+            }
+        }
+        // the transpose below writes over the staged row
+        wave_lds_exchange();
+    } else {
+        const int64_t k0 = (int64_t)lane * V;
+#pragma unroll
+        for (int c0 = 0; c0 < V / 8; c0 += 4) {     // loads in rounds of 4 chunks of 8
+            uint4 raw[4];
+            float4 f0[4], f1[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t k = k0 + (c0 + i) * 8;
+                if (real) {
+                    raw[i] = *reinterpret_cast<const uint4 *>(row + k);
+                    f0[i] = *reinterpret_cast<const float4 *>(mult + k);
+                    f1[i] = *reinterpret_cast<const float4 *>(mult + k + 4);
+                } else {
+                    raw[i] = make_uint4(0u, 0u, 0u, 0u);
+                    f0[i] = f1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t h[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+                const float f[8] = {f0[i].x, f0[i].y, f0[i].z, f0[i].w,
+                                    f1[i].x, f1[i].y, f1[i].z, f1[i].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // fma(float(x), mult, +0): one v_fma_mix_f32, equal to the
+                    // product but for the sign of a zero, which no code or
+                    // magnitude below sees
+                    v[(c0 + i) * 8 + 2 * e] = __builtin_fmaf(h2f(h[e] & 0xffffu), f[2 * e], 0.0f);
+                    v[(c0 + i) * 8 + 2 * e + 1] = __builtin_fmaf(h2f(h[e] >> 16), f[2 * e + 1], 0.0f);
+                }
             }
         }
     }
@@ -482,7 +540,7 @@ hipError_t launch_quant4_rows(const uint16_t *x, int64_t M, int64_t K, int64_t l
     if (K == 4096 || K == 8192) {
         const dim3 g((unsigned)((M + 15) / 16 * 4)), b(256);   // every row of the padded blocks
         const size_t lds = (size_t)RT * 64 * TP * sizeof(float);
-        if (K == 4096) k_quant4_rot_t<64><<<g, b, lds, st>>>(x, M, K, ldx, mult, post, q, scale);
+        if (K == 4096) k_quant4_rot_t<64, true><<<g, b, lds, st>>>(x, M, K, ldx, mult, post, q, scale);
         else k_quant4_rot_t<128><<<g, b, lds, st>>>(x, M, K, ldx, mult, post, q, scale);
         return hipGetLastError();
     }
