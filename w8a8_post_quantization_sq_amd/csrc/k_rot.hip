@@ -199,12 +199,13 @@ constexpr int TP = 68;    // padded floats per transpose row
 // lanes each read 16 bytes of another 128-byte line costs the vector memory
 // path a tag lookup per lane; the direct form issues 24 such loads per wave
 // (its row and its factors), and they, not HBM, held each wave up for about
-// half its time.  Staged, 8 consecutive lanes read one line, and the wave
-// passes the data through its own transpose area into lane order: first its
-// copy of the factors (16 KiB), then the row (8 KiB).  Both copies place
-// 16-byte chunk c at slot c ^ ((c >> S) & 15) (S = 4 for the factors, 3 for
-// the row), so the line-order writes and the lane-order reads alike touch 16
-// different 16-byte bank groups per 16 lanes (8 per 8).
+// half its time.  Staged, 8 consecutive lanes read one line, and the data
+// passes through the transpose areas (before the transposes need them) into
+// lane order: the group's one copy of the factors (16 KiB) and each wave's
+// row (8 KiB).  Both copies place 16-byte chunk c at slot c ^ ((c >> S) & 15)
+// (S = 4 for the factors, 3 for the row), so the line-order writes and the
+// lane-order reads alike touch 16 different 16-byte bank groups per 16 lanes
+// (8 per 8).
 __device__ __forceinline__ int swz(int c, int s) { return c ^ ((c >> s) & 15); }
 
 template <int V, bool STAGED = false>
@@ -224,48 +225,48 @@ k_quant4_rot_t(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx
 
     float v[V];
     if constexpr (STAGED) {
-        // 16-byte chunks in line order: c = 64 t + lane (the row: elements
-        // 8c .. 8c + 7; the factors: 4c .. 4c + 3)
+        // 16-byte chunks in line order.  The factors (the same for the 4 rows)
+        // are loaded by the whole group, chunk c = 256 i + thread (elements
+        // 4c .. 4c + 3), into the first halves of waves 0 and 1's areas (chunk
+        // slot s at area s >> 9, offset 16 (s & 511)); each wave's row, chunk
+        // c = 64 t + lane (elements 8c .. 8c + 7), into the second half of its
+        // own area (offset 9216).
+        constexpr int XOFF = 9216 / 4;                    // floats; 64 * TP * 4 - 8192 bytes free
+        static_assert(64 * TP * 4 - 9216 >= V * 64 * 2 && 9216 >= V * 64 * 4 / 2, "staging fits");
         uint4 raw[V / 8];
-        float4 fl[V / 4];
+        float4 fl[V / 16];
 #pragma unroll
         for (int t = 0; t < V / 8; ++t)
             raw[t] = real ? *reinterpret_cast<const uint4 *>(row + (t * 64 + lane) * 8)
                           : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-        for (int t = 0; t < V / 4; ++t)
-            fl[t] = *reinterpret_cast<const float4 *>(mult + (t * 64 + lane) * 4);
-        float4 *fs = reinterpret_cast<float4 *>(tr);
+        for (int i = 0; i < V / 16; ++i)
+            fl[i] = *reinterpret_cast<const float4 *>(mult + (i * 256 + (int)threadIdx.x) * 4);
+        auto fslot = [&](int c) {
+            const int sl = swz(c, 4);
+            return reinterpret_cast<float4 *>(tr_all + (sl >> 9) * 64 * TP) + (sl & 511);
+        };
 #pragma unroll
-        for (int t = 0; t < V / 4; ++t) fs[swz(t * 64 + lane, 4)] = fl[t];
-        wave_lds_exchange();
-        float f[V];                                       // the lane's factors, k = V lane + i
-#pragma unroll
-        for (int i = 0; i < V / 4; ++i) {
-            const float4 g = fs[swz(lane * (V / 4) + i, 4)];
-            f[4 * i] = g.x;
-            f[4 * i + 1] = g.y;
-            f[4 * i + 2] = g.z;
-            f[4 * i + 3] = g.w;
-        }
-        wave_lds_exchange();                              // the row now goes over the factors
-        uint4 *xs = reinterpret_cast<uint4 *>(tr);
+        for (int i = 0; i < V / 16; ++i) *fslot(i * 256 + (int)threadIdx.x) = fl[i];
+        uint4 *xs = reinterpret_cast<uint4 *>(tr + XOFF);
 #pragma unroll
         for (int t = 0; t < V / 8; ++t) xs[swz(t * 64 + lane, 3)] = raw[t];
-        wave_lds_exchange();
+        __syncthreads();                                  // the group's factors
 #pragma unroll
         for (int j = 0; j < V / 8; ++j) {
             const uint4 r4 = xs[swz(lane * (V / 8) + j, 3)];      // elements V lane + 8j ..
+            const float4 f0 = *fslot(lane * (V / 4) + 2 * j);     // and their factors
+            const float4 f1 = *fslot(lane * (V / 4) + 2 * j + 1);
             const uint32_t h[4] = {r4.x, r4.y, r4.z, r4.w};
+            const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                v[8 * j + 2 * e] = __builtin_fmaf(h2f(h[e] & 0xffffu), f[8 * j + 2 * e], 0.0f);
-                v[8 * j + 2 * e + 1] =
-                    __builtin_fmaf(h2f(h[e] >> 16), f[8 * j + 2 * e + 1], 0.0f);
+                v[8 * j + 2 * e] = __builtin_fmaf(h2f(h[e] & 0xffffu), f[2 * e], 0.0f);
+                v[8 * j + 2 * e + 1] = __builtin_fmaf(h2f(h[e] >> 16), f[2 * e + 1], 0.0f);
             }
         }
-        // the transpose below writes over the staged row
-        wave_lds_exchange();
+        // the transposes below write over the factors (waves 0, 1) and rows
+        __syncthreads();
     } else {
         const int64_t k0 = (int64_t)lane * V;
 #pragma unroll
