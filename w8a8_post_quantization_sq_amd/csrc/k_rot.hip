@@ -195,17 +195,17 @@ k_quant4_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
 constexpr int RT = 4;     // rows per workgroup
 constexpr int TP = 68;    // padded floats per transpose row
 
-// STAGED (K = 4096): the inputs fetched in line order.  A load whose 64
-// lanes each read 16 bytes of another 128-byte line costs the vector memory
-// path a tag lookup per lane; the direct form issues 24 such loads per wave
-// (its row and its factors), and they, not HBM, held each wave up for about
-// half its time.  Staged, 8 consecutive lanes read one line, and the data
-// passes through the transpose areas (before the transposes need them) into
-// lane order: the group's one copy of the factors (16 KiB) and each wave's
-// row (8 KiB).  Both copies place 16-byte chunk c at slot c ^ ((c >> S) & 15)
-// (S = 4 for the factors, 3 for the row), so the line-order writes and the
-// lane-order reads alike touch 16 different 16-byte bank groups per 16 lanes
-// (8 per 8).
+// STAGED: the inputs fetched in line order.  A load whose 64 lanes each read
+// 16 bytes of another 128-byte line costs the vector memory path a tag lookup
+// per lane; the direct form issues 24 such loads per wave at K = 4096 (its
+// row and its factors), and they, not HBM, held each wave up for about half
+// its time.  Staged, 8 consecutive lanes read one line, and the data passes
+// through the transpose areas (before the transposes need them) into lane
+// order: the group's one copy of the factors (16 or 32 KiB) and each wave's
+// row, 8 KiB at a time.  Both copies place 16-byte chunk c at slot
+// c ^ ((c >> S) & 15) (S = log2 of the lane's chunks: 3 for the row, 4 or 5
+// for the factors), so the line-order writes and the lane-order reads alike
+// touch 16 different 16-byte bank groups per 16 lanes (8 per 8).
 __device__ __forceinline__ int swz(int c, int s) { return c ^ ((c >> s) & 15); }
 
 template <int V, bool STAGED = false>
@@ -213,7 +213,7 @@ __global__ void __launch_bounds__(64 * RT)
 k_quant4_rot_t(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
                const float *__restrict__ mult, float post, int8_t *__restrict__ q,
                float *__restrict__ scale) {
-    static_assert(!STAGED || V == 64, "the staged form is for K = 4096");
+    static_assert(!STAGED || V == 64 || V == 128, "the staged form is for K = 4096 and 8192");
     extern __shared__ __align__(16) float tr_all[];     // [RT][64][TP]
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -227,45 +227,58 @@ k_quant4_rot_t(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx
     if constexpr (STAGED) {
         // 16-byte chunks in line order.  The factors (the same for the 4 rows)
         // are loaded by the whole group, chunk c = 256 i + thread (elements
-        // 4c .. 4c + 3), into the first halves of waves 0 and 1's areas (chunk
-        // slot s at area s >> 9, offset 16 (s & 511)); each wave's row, chunk
-        // c = 64 t + lane (elements 8c .. 8c + 7), into the second half of its
-        // own area (offset 9216).
-        constexpr int XOFF = 9216 / 4;                    // floats; 64 * TP * 4 - 8192 bytes free
-        static_assert(64 * TP * 4 - 9216 >= V * 64 * 2 && 9216 >= V * 64 * 4 / 2, "staging fits");
-        uint4 raw[V / 8];
-        float4 fl[V / 16];
+        // 4c .. 4c + 3), into the first halves of the areas (chunk slot s at
+        // area s >> 9, offset 16 (s & 511)); each wave's row, 64 elements of
+        // every lane at a time, into the second half of its own area (offset
+        // 9216): lane l of load t takes chunk 8 (V/8) (t * 8 + l / 8) + 8 h +
+        // l % 8 (8 elements; h the half), 8 consecutive lanes one line.
+        constexpr int XOFF = 9216 / 4;                    // floats
+        constexpr int SF = V == 64 ? 4 : 5;               // log2 of the lane's factor chunks
+        static_assert(64 * TP * 4 - 9216 >= 8192 && 9216 * RT >= V * 64 * 4, "staging fits");
+        uint4 raw[V / 64][8];                             // the row first: it comes from HBM
 #pragma unroll
-        for (int t = 0; t < V / 8; ++t)
-            raw[t] = real ? *reinterpret_cast<const uint4 *>(row + (t * 64 + lane) * 8)
-                          : make_uint4(0u, 0u, 0u, 0u);
+        for (int h = 0; h < V / 64; ++h)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int c = V == 64 ? t * 64 + lane       // (the same chunk, written plainly)
+                                      : (t * 8 + (lane >> 3)) * (V / 8) + 8 * h + (lane & 7);
+                raw[h][t] = real ? *reinterpret_cast<const uint4 *>(row + c * 8)
+                                 : make_uint4(0u, 0u, 0u, 0u);
+            }
+        float4 fl[V / 16];
 #pragma unroll
         for (int i = 0; i < V / 16; ++i)
             fl[i] = *reinterpret_cast<const float4 *>(mult + (i * 256 + (int)threadIdx.x) * 4);
         auto fslot = [&](int c) {
-            const int sl = swz(c, 4);
+            const int sl = swz(c, SF);
             return reinterpret_cast<float4 *>(tr_all + (sl >> 9) * 64 * TP) + (sl & 511);
         };
 #pragma unroll
         for (int i = 0; i < V / 16; ++i) *fslot(i * 256 + (int)threadIdx.x) = fl[i];
         uint4 *xs = reinterpret_cast<uint4 *>(tr + XOFF);
 #pragma unroll
-        for (int t = 0; t < V / 8; ++t) xs[swz(t * 64 + lane, 3)] = raw[t];
-        __syncthreads();                                  // the group's factors
+        for (int h = 0; h < V / 64; ++h) {
+            if (h > 0) wave_lds_exchange();               // the last half's reads are done
 #pragma unroll
-        for (int j = 0; j < V / 8; ++j) {
-            const uint4 r4 = xs[swz(lane * (V / 8) + j, 3)];      // elements V lane + 8j ..
-            const float4 f0 = *fslot(lane * (V / 4) + 2 * j);     // and their factors
-            const float4 f1 = *fslot(lane * (V / 4) + 2 * j + 1);
-            const uint32_t h[4] = {r4.x, r4.y, r4.z, r4.w};
-            const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+            for (int t = 0; t < 8; ++t) xs[swz(t * 64 + lane, 3)] = raw[h][t];
+            if (h == 0) __syncthreads();                  // the group's factors (and the row)
+            else wave_lds_exchange();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[8 * j + 2 * e] = __builtin_fmaf(h2f(h[e] & 0xffffu), f[2 * e], 0.0f);
-                v[8 * j + 2 * e + 1] = __builtin_fmaf(h2f(h[e] >> 16), f[2 * e + 1], 0.0f);
+            for (int j = 0; j < 8; ++j) {
+                const uint4 r4 = xs[swz(lane * 8 + j, 3)];   // elements V lane + 64 h + 8 j ..
+                const int c = lane * (V / 4) + 16 * h + 2 * j;   // and their factors
+                const float4 f0 = *fslot(c), f1 = *fslot(c + 1);
+                const uint32_t hw[4] = {r4.x, r4.y, r4.z, r4.w};
+                const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+                float *vv = v + 64 * h + 8 * j;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    vv[2 * e] = __builtin_fmaf(h2f(hw[e] & 0xffffu), f[2 * e], 0.0f);
+                    vv[2 * e + 1] = __builtin_fmaf(h2f(hw[e] >> 16), f[2 * e + 1], 0.0f);
+                }
             }
         }
-        // the transposes below write over the factors (waves 0, 1) and rows
+        // the transposes below write over the factors and rows
         __syncthreads();
     } else {
         const int64_t k0 = (int64_t)lane * V;
@@ -542,7 +555,7 @@ hipError_t launch_quant4_rows(const uint16_t *x, int64_t M, int64_t K, int64_t l
         const dim3 g((unsigned)((M + 15) / 16 * 4)), b(256);   // every row of the padded blocks
         const size_t lds = (size_t)RT * 64 * TP * sizeof(float);
         if (K == 4096) k_quant4_rot_t<64, true><<<g, b, lds, st>>>(x, M, K, ldx, mult, post, q, scale);
-        else k_quant4_rot_t<128><<<g, b, lds, st>>>(x, M, K, ldx, mult, post, q, scale);
+        else k_quant4_rot_t<128, true><<<g, b, lds, st>>>(x, M, K, ldx, mult, post, q, scale);
         return hipGetLastError();
     }
     const int64_t groups = (M + 15) / 16 * 2;       // every row of the padded row blocks
