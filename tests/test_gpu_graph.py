@@ -83,8 +83,9 @@ def inputs(seed, M, K, N):
                                    (16, 8192, 3584), (5, 4096, 1000)])
 def test_layer_graph_replays_equal_eager(sq, dev, orc, M, K, N):
     """Quantization + W8A8 product (fp16 out) recorded once, replayed on new
-    tokens; large token counts take the tile kernel, 1 token the one-token
-    decode kernel, 5-16 tokens the multi-block decode kernel."""
+    tokens; 2048 tokens take the tile kernel, 300 the multi-block kernel over
+    64-token groups, 1 token the one-token decode kernel, 5-16 tokens the
+    multi-block decode kernel."""
     import torch
     from test_gpu_parity import assert_f16_close, tile_rows
     print(f"[graph] layer M={M} K={K} N={N}", flush=True)

@@ -454,7 +454,8 @@ def test_fold_columns_whose_multiplier_overflows(sq, dev, orc):
 # token counts 1..64 run the decode kernels (1, 2, 3 or 4 activation row blocks;
 # non-temporal weight loads up to 2 of them; at 9..32 tokens with 512 or more
 # channel blocks, 2, 4 or 7 blocks per workgroup, also with a partial last
-# workgroup), 65 and up the tile kernel
+# workgroup); 65 and up the multi-block kernel over 64-token groups while the
+# 256 x 128 tiles would number at most 64, beyond that the tile kernels
 GEMM_SHAPES = [(1, 1, 16), (3, 5, 48), (17, 100, 80), (40, 100, 320), (49, 1000, 1088),
                (9, 64, 4096), (25, 33, 256), (32, 48, 1024),
                (16, 28672, 128), (9, 28672, 64), (24, 8192, 64), (32, 12304, 64), (20, 8200, 64),
@@ -467,6 +468,8 @@ GEMM_SHAPES = [(1, 1, 16), (3, 5, 48), (17, 100, 80), (40, 100, 320), (49, 1000,
                (512, 4096, 1024), (200, 1000, 4160), (1000, 128, 256), (320, 2048, 512),
                (65, 4096, 2048),
                (130, 129, 1040), (256, 384, 2048), (1, 28672, 128), (16, 300, 8192), (513, 77, 112),
+               # 256 x 128 tiles (65..256 of them): ragged tokens, channels and k windows
+               (300, 8200, 1040), (1100, 1950, 208), (600, 4000, 80), (2100, 1030, 64),
                # 256 x 256 tiles (their rounds of 256 CUs beat the 256 x 128 ones'): ragged M,
                # N (a partial row block) and K, and a full-width one
                (4000, 4040, 80), (4096, 8192, 64)]
@@ -512,9 +515,10 @@ def test_gemm_extreme_sums_and_strided_output(sq, dev, orc):
     assert_f16_close(out[:, :24], orc.dequant(orc.gemm_i32(xq, wq), xs, ws))
 
 
-def test_gemm_tile_path_at_max_k(sq, dev, orc):
-    """65 tokens (the tile kernel) at the largest K the library takes: window
-    offsets up to 2047 KiB per row block, int32 sums near their bound."""
+def test_gemm_mid_path_at_max_k(sq, dev, orc):
+    """65 tokens (the multi-block kernel over 64-token groups, two groups) at
+    the largest K the library takes: window offsets up to 2047 KiB per row
+    block, int32 sums near their bound."""
     M, N, K = 65, 40, 131056
     xq = W.random_i8(920, M, K, -128, 127)
     wq = W.random_i8(921, N, K, -128, 127)
@@ -648,10 +652,13 @@ def test_gemm_wide_tile_path_deep_k_full_output(sq, dev, orc, M, N, K):
     assert_f16_close(H(y), orc.dequant(ref, xs, ws))
 
 
-@pytest.mark.parametrize("M,N,ldy,off", [(100, 72, 80, 0), (300, 130, 136, 8), (257, 64, 72, 4)])
-def test_gemm_tile_path_strided_and_offset_output(sq, dev, orc, M, N, ldy, off):
-    """Token counts on the tile kernel with output rows of stride ldy >= N,
-    starting `off` elements into the buffer (8- or 16-byte aligned or not)."""
+@pytest.mark.parametrize("M,N,ldy,off", [(100, 72, 80, 0), (300, 130, 136, 8), (257, 64, 72, 4),
+                                         (300, 8200, 8208, 8), (2100, 1030, 1040, 4)])
+def test_gemm_large_m_strided_and_offset_output(sq, dev, orc, M, N, ldy, off):
+    """Token counts above 64, on the multi-block kernel over 64-token groups
+    (the first three) and on the 256 x 128 tile kernel (65 and 81 tiles), with
+    output rows of stride ldy >= N, starting `off` elements into the buffer
+    (8- or 16-byte aligned or not)."""
     import torch
     K = 192
     xq = W.random_i8(1100 + M, M, K)

@@ -176,8 +176,9 @@ def test_w4_fold_matches_oracle(sq, dev, orc, name, K, N, ldw, rotate):
     del torch
 
 
-# token counts 1..64 run the decode kernel, 65 and up the tile kernel (as for
-# the 8-bit product)
+# token counts 1..64 run the decode kernel, 65 and up the tile kernel (the
+# 8-bit product also runs mid-size batches on its multi-block decode kernel;
+# the 4-bit one does not)
 GEMM4_SHAPES = [(1, 1, 16), (3, 5, 48), (17, 100, 80), (40, 100, 320), (64, 70, 4096),
                 (16, 28672, 64), (33, 8200, 64),
                 (65, 33, 64), (128, 128, 4096), (130, 129, 1040), (256, 384, 2048),
