@@ -470,6 +470,8 @@ GEMM_SHAPES = [(1, 1, 16), (3, 5, 48), (17, 100, 80), (40, 100, 320), (49, 1000,
                (130, 129, 1040), (256, 384, 2048), (1, 28672, 128), (16, 300, 8192), (513, 77, 112),
                # 256 x 128 tiles (65..256 of them): ragged tokens, channels and k windows
                (300, 8200, 1040), (1100, 1950, 208), (600, 4000, 80), (2100, 1030, 64),
+               # the switch: 64 tiles (multi-block kernel) and 65 (tile kernel)
+               (256, 8192, 64), (256, 8320, 64),
                # 256 x 256 tiles (their rounds of 256 CUs beat the 256 x 128 ones'): ragged M,
                # N (a partial row block) and K, and a full-width one
                (4000, 4040, 80), (4096, 8192, 64)]
