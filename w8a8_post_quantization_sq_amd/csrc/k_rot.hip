@@ -182,38 +182,39 @@ k_quant4_rows(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
 }
 
 // Wide rows, K = 64 * V (4096 or 8192), one wave per row, 4 rows per group.
-// Lane l first holds the contiguous elements l*V .. l*V + V - 1, so the
-// stages h = 1 .. V/2 (the low log2(V) index bits) run in its registers; one
+// Lane l holds the contiguous elements l*V .. l*V + V - 1, so the stages
+// h = 1 .. V/2 (the low log2(V) index bits) run in its registers; one
 // transpose through LDS then gives lane l' the elements h*V + l' + 64 j
 // (h = 0..63, j < V/64), the six high index bits in registers for the stages
 // h = V .. K/2.  No butterfly crosses lanes.  The transpose area, 64 rows of
 // 64 floats padded to 68 per wave (writes and reads free of bank conflicts),
 // is the wave's own, so the transpose needs no workgroup barrier (a wave-level
 // ordering of its lanes' accesses suffices); it is reused for the wave's
-// codes, and one barrier before the packed stores (which take all 4 rows) is
-// the only one.
+// codes, and one barrier before the packed stores takes all 4 rows.
+//
+// The inputs arrive in line order.  Loaded straight into that lane layout, a
+// load whose 64 lanes each read 16 bytes of another 128-byte line costs the
+// vector memory path a tag lookup per lane: at K = 4096 a wave issued 24 such
+// loads (its row and its factors), and they, not HBM, held each wave up for
+// about half its time.  Here 8 consecutive lanes read one line, and the data
+// passes through the transpose areas (before the transposes need them) into
+// lane order: the group's one copy of the factors (16 or 32 KiB) and each
+// wave's row, 8 KiB at a time.  Both copies place 16-byte chunk c at slot
+// c ^ ((c >> S) & 15) (S = log2 of the lane's chunks: 3 for the row, 4 or 5
+// for the factors), so the line-order writes and the lane-order reads alike
+// touch 16 different 16-byte bank groups per 16 lanes (8 per 8); a barrier
+// publishes the factors and another frees the areas for the transposes.
 constexpr int RT = 4;     // rows per workgroup
 constexpr int TP = 68;    // padded floats per transpose row
 
-// STAGED: the inputs fetched in line order.  A load whose 64 lanes each read
-// 16 bytes of another 128-byte line costs the vector memory path a tag lookup
-// per lane; the direct form issues 24 such loads per wave at K = 4096 (its
-// row and its factors), and they, not HBM, held each wave up for about half
-// its time.  Staged, 8 consecutive lanes read one line, and the data passes
-// through the transpose areas (before the transposes need them) into lane
-// order: the group's one copy of the factors (16 or 32 KiB) and each wave's
-// row, 8 KiB at a time.  Both copies place 16-byte chunk c at slot
-// c ^ ((c >> S) & 15) (S = log2 of the lane's chunks: 3 for the row, 4 or 5
-// for the factors), so the line-order writes and the lane-order reads alike
-// touch 16 different 16-byte bank groups per 16 lanes (8 per 8).
 __device__ __forceinline__ int swz(int c, int s) { return c ^ ((c >> s) & 15); }
 
-template <int V, bool STAGED = false>
+template <int V>
 __global__ void __launch_bounds__(64 * RT)
 k_quant4_rot_t(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx,
                const float *__restrict__ mult, float post, int8_t *__restrict__ q,
                float *__restrict__ scale) {
-    static_assert(!STAGED || V == 64 || V == 128, "the staged form is for K = 4096 and 8192");
+    static_assert(V == 64 || V == 128, "K = 4096 or 8192");
     extern __shared__ __align__(16) float tr_all[];     // [RT][64][TP]
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -224,96 +225,61 @@ k_quant4_rot_t(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ldx
     float *tr = tr_all + wave * 64 * TP;
 
     float v[V];
-    if constexpr (STAGED) {
-        // 16-byte chunks in line order.  The factors (the same for the 4 rows)
-        // are loaded by the whole group, chunk c = 256 i + thread (elements
-        // 4c .. 4c + 3), into the first halves of the areas (chunk slot s at
-        // area s >> 9, offset 16 (s & 511)); each wave's row, 64 elements of
-        // every lane at a time, into the second half of its own area (offset
-        // 9216): lane l of load t takes chunk 8 (V/8) (t * 8 + l / 8) + 8 h +
-        // l % 8 (8 elements; h the half), 8 consecutive lanes one line.
-        constexpr int XOFF = 9216 / 4;                    // floats
-        constexpr int SF = V == 64 ? 4 : 5;               // log2 of the lane's factor chunks
-        static_assert(64 * TP * 4 - 9216 >= 8192 && 9216 * RT >= V * 64 * 4, "staging fits");
-        uint4 raw[V / 64][8];                             // the row first: it comes from HBM
+    // 16-byte chunks in line order.  The factors (the same for the 4 rows)
+    // are loaded by the whole group, chunk c = 256 i + thread (elements
+    // 4c .. 4c + 3), into the first halves of the areas (chunk slot s at
+    // area s >> 9, offset 16 (s & 511)); each wave's row, 64 elements of
+    // every lane at a time, into the second half of its own area (offset
+    // 9216): lane l of load t takes chunk (V/8) (8 t + l / 8) + 8 h + l % 8
+    // (8 elements; h the half), 8 consecutive lanes one line.
+    constexpr int XOFF = 9216 / 4;                    // floats
+    constexpr int SF = V == 64 ? 4 : 5;               // log2 of the lane's factor chunks
+    static_assert(64 * TP * 4 - 9216 >= 8192 && 9216 * RT >= V * 64 * 4, "staging fits");
+    uint4 raw[V / 64][8];                             // the row first: it comes from HBM
 #pragma unroll
-        for (int h = 0; h < V / 64; ++h)
+    for (int h = 0; h < V / 64; ++h)
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int c = V == 64 ? t * 64 + lane       // (the same chunk, written plainly)
-                                      : (t * 8 + (lane >> 3)) * (V / 8) + 8 * h + (lane & 7);
-                raw[h][t] = real ? *reinterpret_cast<const uint4 *>(row + c * 8)
-                                 : make_uint4(0u, 0u, 0u, 0u);
-            }
-        float4 fl[V / 16];
-#pragma unroll
-        for (int i = 0; i < V / 16; ++i)
-            fl[i] = *reinterpret_cast<const float4 *>(mult + (i * 256 + (int)threadIdx.x) * 4);
-        auto fslot = [&](int c) {
-            const int sl = swz(c, SF);
-            return reinterpret_cast<float4 *>(tr_all + (sl >> 9) * 64 * TP) + (sl & 511);
-        };
-#pragma unroll
-        for (int i = 0; i < V / 16; ++i) *fslot(i * 256 + (int)threadIdx.x) = fl[i];
-        uint4 *xs = reinterpret_cast<uint4 *>(tr + XOFF);
-#pragma unroll
-        for (int h = 0; h < V / 64; ++h) {
-            if (h > 0) wave_lds_exchange();               // the last half's reads are done
-#pragma unroll
-            for (int t = 0; t < 8; ++t) xs[swz(t * 64 + lane, 3)] = raw[h][t];
-            if (h == 0) __syncthreads();                  // the group's factors (and the row)
-            else wave_lds_exchange();
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint4 r4 = xs[swz(lane * 8 + j, 3)];   // elements V lane + 64 h + 8 j ..
-                const int c = lane * (V / 4) + 16 * h + 2 * j;   // and their factors
-                const float4 f0 = *fslot(c), f1 = *fslot(c + 1);
-                const uint32_t hw[4] = {r4.x, r4.y, r4.z, r4.w};
-                const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-                float *vv = v + 64 * h + 8 * j;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vv[2 * e] = __builtin_fmaf(h2f(hw[e] & 0xffffu), f[2 * e], 0.0f);
-                    vv[2 * e + 1] = __builtin_fmaf(h2f(hw[e] >> 16), f[2 * e + 1], 0.0f);
-                }
-            }
+        for (int t = 0; t < 8; ++t) {
+            const int c = V == 64 ? t * 64 + lane       // (the same chunk, written plainly)
+                                  : (t * 8 + (lane >> 3)) * (V / 8) + 8 * h + (lane & 7);
+            raw[h][t] = real ? *reinterpret_cast<const uint4 *>(row + c * 8)
+                             : make_uint4(0u, 0u, 0u, 0u);
         }
-        // the transposes below write over the factors and rows
-        __syncthreads();
-    } else {
-        const int64_t k0 = (int64_t)lane * V;
+    float4 fl[V / 16];
 #pragma unroll
-        for (int c0 = 0; c0 < V / 8; c0 += 4) {     // loads in rounds of 4 chunks of 8
-            uint4 raw[4];
-            float4 f0[4], f1[4];
+    for (int i = 0; i < V / 16; ++i)
+        fl[i] = *reinterpret_cast<const float4 *>(mult + (i * 256 + (int)threadIdx.x) * 4);
+    auto fslot = [&](int c) {
+        const int sl = swz(c, SF);
+        return reinterpret_cast<float4 *>(tr_all + (sl >> 9) * 64 * TP) + (sl & 511);
+    };
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t k = k0 + (c0 + i) * 8;
-                if (real) {
-                    raw[i] = *reinterpret_cast<const uint4 *>(row + k);
-                    f0[i] = *reinterpret_cast<const float4 *>(mult + k);
-                    f1[i] = *reinterpret_cast<const float4 *>(mult + k + 4);
-                } else {
-                    raw[i] = make_uint4(0u, 0u, 0u, 0u);
-                    f0[i] = f1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-                }
-            }
+    for (int i = 0; i < V / 16; ++i) *fslot(i * 256 + (int)threadIdx.x) = fl[i];
+    uint4 *xs = reinterpret_cast<uint4 *>(tr + XOFF);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t h[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-                const float f[8] = {f0[i].x, f0[i].y, f0[i].z, f0[i].w,
-                                    f1[i].x, f1[i].y, f1[i].z, f1[i].w};
+    for (int h = 0; h < V / 64; ++h) {
+        if (h > 0) wave_lds_exchange();               // the last half's reads are done
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    // fma(float(x), mult, +0): one v_fma_mix_f32, equal to the
-                    // product but for the sign of a zero, which no code or
-                    // magnitude below sees
-                    v[(c0 + i) * 8 + 2 * e] = __builtin_fmaf(h2f(h[e] & 0xffffu), f[2 * e], 0.0f);
-                    v[(c0 + i) * 8 + 2 * e + 1] = __builtin_fmaf(h2f(h[e] >> 16), f[2 * e + 1], 0.0f);
-                }
+        for (int t = 0; t < 8; ++t) xs[swz(t * 64 + lane, 3)] = raw[h][t];
+        if (h == 0) __syncthreads();                  // the group's factors (and the row)
+        else wave_lds_exchange();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint4 r4 = xs[swz(lane * 8 + j, 3)];   // elements V lane + 64 h + 8 j ..
+            const int c = lane * (V / 4) + 16 * h + 2 * j;   // and their factors
+            const float4 f0 = *fslot(c), f1 = *fslot(c + 1);
+            const uint32_t hw[4] = {r4.x, r4.y, r4.z, r4.w};
+            const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+            float *vv = v + 64 * h + 8 * j;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vv[2 * e] = __builtin_fmaf(h2f(hw[e] & 0xffffu), f[2 * e], 0.0f);
+                vv[2 * e + 1] = __builtin_fmaf(h2f(hw[e] >> 16), f[2 * e + 1], 0.0f);
             }
         }
     }
+    // the transposes below write over the factors and rows
+    __syncthreads();
     // stages h = 1 .. V/2: inside the lane's segment
 #pragma unroll
     for (int hb = 1; hb < V; hb <<= 1)
@@ -554,8 +520,8 @@ hipError_t launch_quant4_rows(const uint16_t *x, int64_t M, int64_t K, int64_t l
     if (K == 4096 || K == 8192) {
         const dim3 g((unsigned)((M + 15) / 16 * 4)), b(256);   // every row of the padded blocks
         const size_t lds = (size_t)RT * 64 * TP * sizeof(float);
-        if (K == 4096) k_quant4_rot_t<64, true><<<g, b, lds, st>>>(x, M, K, ldx, mult, post, q, scale);
-        else k_quant4_rot_t<128, true><<<g, b, lds, st>>>(x, M, K, ldx, mult, post, q, scale);
+        if (K == 4096) k_quant4_rot_t<64><<<g, b, lds, st>>>(x, M, K, ldx, mult, post, q, scale);
+        else k_quant4_rot_t<128><<<g, b, lds, st>>>(x, M, K, ldx, mult, post, q, scale);
         return hipGetLastError();
     }
     const int64_t groups = (M + 15) / 16 * 2;       // every row of the padded row blocks
