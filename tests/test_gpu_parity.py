@@ -130,7 +130,9 @@ def test_calibrate_matches_oracle(sq, dev, orc, name):
     assert bits_equal(H(ax2), orc.calibrate_absmax(inp.x_cal))
 
 
-@pytest.mark.parametrize("T_,K,ld", [(1, 16, 16), (37, 48, 48), (5, 80, 96), (300, 528, 536)])
+@pytest.mark.parametrize("T_,K,ld", [(1, 16, 16), (37, 48, 48), (5, 80, 96), (300, 528, 536),
+                                    # wide rows (257 and 313 channel groups) and a ragged one
+                                    (200, 16400, 16408), (30, 20000, 20000), (513, 4112, 4120)])
 def test_calibrate_ragged_and_strided(sq, dev, orc, T_, K, ld):
     x = W.random_f16(100 + K, T_, ld, scale=4.0)
     xv = T(x, dev)[:, :K]
